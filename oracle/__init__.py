@@ -1,0 +1,165 @@
+"""fp64 CPU oracle for attention forward and row softmax (ctypes wrapper of oracle.c).
+
+TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the benchmark's CPU
+baseline may import this package; the product path never does.  It shares no
+code with the HIP library.
+
+Inputs arrive in their storage type (float32, float16, or bfloat16 bit
+patterns held in ``np.uint16``) and are widened exactly to float64 here, by
+this package's own decoder.  Every result is float64.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(_HERE, "oracle.c")
+LIB = os.path.join(_HERE, "liboracle.so")
+
+_lib = None
+
+
+def build(src: str = SRC, out: str = LIB) -> str:
+    """Compile the oracle with gcc (-O2, no fast-math, IEEE double throughout)."""
+    cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fno-fast-math",
+           "-ffp-contract=off", src, "-o", out + ".tmp", "-lm", "-lpthread"]
+    subprocess.run(cmd, check=True)
+    os.replace(out + ".tmp", out)
+    return out
+
+
+def default_threads() -> int:
+    n = os.cpu_count() or 1
+    return max(1, min(n, 16))
+
+
+class Oracle:
+    """Bound view of one compiled oracle library (the real one, or a test build)."""
+
+    def __init__(self, path: str):
+        lib = ctypes.CDLL(path)
+        dp = ctypes.POINTER(ctypes.c_double)
+        lp = ctypes.POINTER(ctypes.c_long)
+        L, I, D = ctypes.c_long, ctypes.c_int, ctypes.c_double
+        lib.oracle_softmax_rows.argtypes = [dp, dp, L, L, I]
+        lib.oracle_softmax_rows.restype = None
+        lib.oracle_attention_rows.argtypes = [dp, dp, dp, L, L, D, I, lp, L, dp, dp, I]
+        lib.oracle_attention_rows.restype = None
+        lib.oracle_attention_probs.argtypes = [dp, dp, L, L, D, I, L, dp]
+        lib.oracle_attention_probs.restype = None
+        lib.oracle_online_normaliser.argtypes = [dp, L, dp, dp]
+        lib.oracle_online_normaliser.restype = None
+        lib.oracle_attention_tiled_row.argtypes = [dp, dp, dp, L, L, D, I, L, L, dp, dp, dp]
+        lib.oracle_attention_tiled_row.restype = L
+        self.lib = lib
+        self.path = path
+
+    # -- decoding of the storage types -------------------------------------
+    @staticmethod
+    def to_f64(x: np.ndarray, dtype: str | None = None) -> np.ndarray:
+        """Exact widening to float64.  ``dtype='bf16'`` marks uint16 bit patterns."""
+        x = np.asarray(x)
+        if dtype == "bf16" or (dtype is None and x.dtype == np.uint16):
+            if x.dtype != np.uint16:
+                raise TypeError("bf16 data must be np.uint16 bit patterns")
+            widened = (x.astype(np.uint32) << np.uint32(16)).view(np.float32)
+            return np.ascontiguousarray(widened, dtype=np.float64)
+        return np.ascontiguousarray(x, dtype=np.float64)
+
+    @staticmethod
+    def _p(a: np.ndarray):
+        return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+    # -- row softmax ---------------------------------------------------------
+    def softmax_rows(self, x, threads: int | None = None) -> np.ndarray:
+        x = self.to_f64(x)
+        if x.ndim != 2:
+            raise ValueError("softmax_rows expects [rows, cols]")
+        y = np.empty_like(x)
+        self.lib.oracle_softmax_rows(self._p(x), self._p(y), x.shape[0], x.shape[1],
+                                     threads or default_threads())
+        return y
+
+    # -- attention, one head ---------------------------------------------------
+    def attention_head(self, q, k, v, scale: float, causal: bool, rows=None,
+                       dtype: str | None = None, threads: int | None = None):
+        """O [len(rows), d] and LSE [len(rows)] of one head; q, k, v are [N, d]."""
+        q, k, v = (self.to_f64(t, dtype) for t in (q, k, v))
+        n, d = q.shape
+        if k.shape != (n, d) or v.shape != (n, d):
+            raise ValueError("q, k, v must share the shape [N, d]")
+        rows = np.arange(n, dtype=np.int64) if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
+        if rows.size and (rows.min() < 0 or rows.max() >= n):
+            raise ValueError("row index out of range")
+        o = np.empty((rows.size, d), np.float64)
+        lse = np.empty(rows.size, np.float64)
+        self.lib.oracle_attention_rows(self._p(q), self._p(k), self._p(v), n, d, float(scale),
+                                       int(bool(causal)),
+                                       rows.ctypes.data_as(ctypes.POINTER(ctypes.c_long)),
+                                       rows.size, self._p(o), self._p(lse),
+                                       threads or default_threads())
+        return o, lse
+
+    def attention(self, q, k, v, scale: float, causal: bool, rows_of=None,
+                  dtype: str | None = None, threads: int | None = None):
+        """[B, H, N, d] inputs; ``rows_of(b, h)`` picks the checked rows (default all).
+
+        Returns a list over heads of (b, h, rows, O [rows, d], LSE [rows]).
+        """
+        B, H, N, _ = q.shape
+        out = []
+        for b in range(B):
+            for h in range(H):
+                rows = None if rows_of is None else rows_of(b, h)
+                o, lse = self.attention_head(q[b, h], k[b, h], v[b, h], scale, causal, rows,
+                                             dtype, threads)
+                rr = np.arange(N, dtype=np.int64) if rows is None else np.asarray(rows, np.int64)
+                out.append((b, h, rr, o, lse))
+        return out
+
+    def attention_probs(self, q, k, scale: float, causal: bool, i: int, dtype=None) -> np.ndarray:
+        q, k = self.to_f64(q, dtype), self.to_f64(k, dtype)
+        n, d = q.shape
+        p = np.empty(n, np.float64)
+        self.lib.oracle_attention_probs(self._p(q), self._p(k), n, d, float(scale),
+                                        int(bool(causal)), int(i), self._p(p))
+        return p
+
+    # -- online forms ----------------------------------------------------------
+    def online_normaliser(self, x) -> tuple[float, float]:
+        x = self.to_f64(np.ravel(x))
+        m = ctypes.c_double()
+        s = ctypes.c_double()
+        self.lib.oracle_online_normaliser(self._p(x), x.size, ctypes.byref(m), ctypes.byref(s))
+        return m.value, s.value
+
+    def attention_tiled_row(self, q, k, v, scale: float, causal: bool, i: int, tile: int,
+                            dtype=None):
+        """(o [d], lse, alphas [tiles]) of the tile-wise recurrence for query row i."""
+        q, k, v = (self.to_f64(t, dtype) for t in (q, k, v))
+        n, d = q.shape
+        o = np.empty(d, np.float64)
+        lse = ctypes.c_double()
+        alphas = np.empty(max(1, (n + tile - 1) // tile), np.float64)
+        t = self.lib.oracle_attention_tiled_row(self._p(q), self._p(k), self._p(v), n, d,
+                                                float(scale), int(bool(causal)), int(i),
+                                                int(tile), self._p(o), ctypes.byref(lse),
+                                                self._p(alphas))
+        return o, lse.value, alphas[:t].copy()
+
+
+def load(path: str = LIB) -> Oracle:
+    """The oracle library, compiled on first use if absent or older than its source."""
+    global _lib
+    if path == LIB:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(SRC):
+            build()
+        _lib = Oracle(LIB)
+        return _lib
+    return Oracle(path)

@@ -1,0 +1,294 @@
+"""Pins of the fp64 oracle to facts fixed outside itself.
+
+Each ``pin_*`` function takes a bound oracle library and raises AssertionError
+when the oracle disagrees with a fact that the pages or plain mathematics fix:
+hand-derived closed forms (tests/golden/closed_forms.json), special cases,
+invariants the pages state (online == three-pass, rows of P sum to one, the
+rescale factor never exceeds one, the loud key in the last tile), and a
+50-digit brute force on tiny inputs.  The same pins run against deliberately
+broken copies of the oracle (test_oracle_mutants.py) to show they would catch
+a dropped term, a wrong sign or index, or a transposed operand.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+
+import workloads
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "closed_forms.json")
+
+
+def _close(a, b, tol, what):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    assert a.shape == b.shape, f"{what}: shape {a.shape} != {b.shape}"
+    assert np.all(np.isfinite(a)), f"{what}: non-finite values"
+    err = float(np.max(np.abs(a - b))) if a.size else 0.0
+    assert err <= tol, f"{what}: max abs err {err:.3e} > {tol:.1e}"
+
+
+def _rng(tag):
+    return np.random.default_rng([4242, tag])
+
+
+# ---------------------------------------------------------------------------
+# softmax pins
+# ---------------------------------------------------------------------------
+def pin_softmax_golden(orc):
+    """Hand-derived rows: exp ratios 1:2:3:4, the same shifted by 1000, three spikes."""
+    cases = json.load(open(GOLDEN))["softmax"]
+    for c in cases:
+        y = orc.softmax_rows(np.array([c["x"]], np.float64))[0]
+        _close(y, c["y"], c.get("tol", 1e-15), f"softmax golden {c['name']}")
+
+
+def pin_softmax_constant_row(orc):
+    """A row of equal values gives 1/cols everywhere."""
+    for cols in (1, 2, 7, 64, 1000):
+        x = np.full((3, cols), -3.25)
+        _close(orc.softmax_rows(x), np.full((3, cols), 1.0 / cols), 1e-15, f"constant row {cols}")
+
+
+def pin_softmax_two_element_logistic(orc):
+    """softmax([a, b])_0 = 1 / (1 + e^(b - a)), the logistic function."""
+    r = _rng(1)
+    x = r.normal(0, 5, size=(50, 2))
+    y = orc.softmax_rows(x)
+    ref = 1.0 / (1.0 + np.exp(x[:, 1] - x[:, 0]))
+    _close(y[:, 0], ref, 1e-14, "logistic")
+    _close(y[:, 1], 1.0 - ref, 1e-14, "logistic complement")
+
+
+def pin_softmax_spike_rows(orc):
+    """k entries at +50 and the rest <= -1e3: exactly 1/k at the spikes, 0 elsewhere."""
+    r = _rng(2)
+    x = -1e3 - r.random((6, 300)) * 10
+    ks = []
+    for i in range(6):
+        idx = r.choice(300, size=i + 1, replace=False)
+        x[i, idx] = 50.0
+        ks.append(idx)
+    y = orc.softmax_rows(x)
+    for i, idx in enumerate(ks):
+        ref = np.zeros(300)
+        ref[idx] = 1.0 / len(idx)
+        _close(y[i], ref, 1e-15, f"spike row {i}")
+
+
+def pin_softmax_shift_invariance(orc):
+    """softmax(x + t) = softmax(x) for t = 700 (exp(700+) is beyond double range)."""
+    x = _rng(3).normal(0, 3, size=(4, 257))
+    _close(orc.softmax_rows(x + 700.0), orc.softmax_rows(x), 1e-13, "shift invariance")
+
+
+def pin_softmax_brute_force(orc):
+    """50-digit brute force exp(x_i)/sum exp(x_j) on tiny rows."""
+    import mpmath
+    mpmath.mp.dps = 50
+    x = _rng(4).normal(0, 4, size=(5, 9))
+    y = orc.softmax_rows(x)
+    for i in range(x.shape[0]):
+        e = [mpmath.exp(mpmath.mpf(float(t))) for t in x[i]]
+        s = mpmath.fsum(e)
+        ref = [float(t / s) for t in e]
+        _close(y[i], ref, 1e-15, f"softmax brute force row {i}")
+
+
+def pin_online_normaliser_equals_three_pass(orc):
+    """The scalar recurrence (max, rescaled sum) reproduces the three-pass softmax."""
+    r = _rng(5)
+    for n in (1, 2, 17, 1000):
+        x = r.normal(0, 6, size=n)
+        if n > 3:
+            x[-1] = x.max() + 20.0       # the maximum arrives last
+        m, dsum = orc.online_normaliser(x)
+        assert m == float(np.max(x)), "online max differs from the row max"
+        y = orc.softmax_rows(x[None, :])[0]
+        _close(np.exp(x - m) / dsum, y, 1e-14, f"online normaliser n={n}")
+
+
+def pin_softmax_rows_sum_to_one(orc):
+    """Rows of the spiked workload recipe are non-negative and sum to one."""
+    x = workloads.random_rows(8, 4096, seed=6, spike_prob=0.01)
+    y = orc.softmax_rows(x)
+    assert np.all(y >= 0), "negative probability"
+    _close(y.sum(axis=1), np.ones(8), 1e-13, "softmax row sums")
+
+
+# ---------------------------------------------------------------------------
+# attention pins
+# ---------------------------------------------------------------------------
+def pin_attention_golden(orc):
+    """Hand-derived two-key cases (non-causal, causal, scaled)."""
+    for c in json.load(open(GOLDEN))["attention"]:
+        q, k, v = (np.array(c[t], np.float64) for t in "qkv")
+        o, lse = orc.attention_head(q, k, v, c["scale"], c["causal"])
+        _close(o, c["o"], 1e-14, f"attention golden {c['name']} O")
+        _close(lse, c["lse"], 1e-14, f"attention golden {c['name']} LSE")
+
+
+def pin_attention_brute_force(orc):
+    """50-digit softmax(scale Q K^T) V on tiny non-square inputs, causal and not."""
+    import mpmath
+    mpmath.mp.dps = 50
+    r = _rng(10)
+    for n, d, causal in ((1, 3, False), (5, 3, False), (7, 2, True), (8, 4, True), (3, 5, False)):
+        q, k, v = (r.normal(0, 1.5, size=(n, d)) for _ in range(3))
+        scale = 0.7
+        o, lse = orc.attention_head(q, k, v, scale, causal)
+        for i in range(n):
+            js = range(i + 1) if causal else range(n)
+            s = [mpmath.mpf(scale) * mpmath.fsum(mpmath.mpf(float(q[i, e])) * mpmath.mpf(float(k[j, e]))
+                                                 for e in range(d)) for j in js]
+            w = [mpmath.exp(t) for t in s]
+            z = mpmath.fsum(w)
+            ref = [float(mpmath.fsum(w[t] * mpmath.mpf(float(v[j, e])) for t, j in enumerate(js)) / z)
+                   for e in range(d)]
+            _close(o[i], ref, 1e-14, f"attention brute force n={n} d={d} causal={causal} row {i}")
+            _close([lse[i]], [float(mpmath.log(z))], 1e-14, f"lse brute force row {i}")
+
+
+def pin_attention_zero_query(orc):
+    """Q = 0: every visible key gets the same weight, so o_i is the mean of the
+    visible v_j and lse_i = ln(number of visible keys)."""
+    r = _rng(11)
+    n, d = 37, 8
+    k, v = r.normal(size=(n, d)), r.normal(size=(n, d))
+    q = np.zeros((n, d))
+    for causal in (False, True):
+        o, lse = orc.attention_head(q, k, v, 0.3, causal)
+        for i in range(n):
+            cnt = i + 1 if causal else n
+            _close(o[i], v[:cnt].mean(axis=0), 1e-14, f"zero-q mean causal={causal} row {i}")
+            _close([lse[i]], [math.log(cnt)], 1e-14, f"zero-q lse row {i}")
+
+
+def pin_attention_constant_values(orc):
+    """V rows all equal to c: o_i = c whatever the weights."""
+    r = _rng(12)
+    n, d = 29, 6
+    q, k = r.normal(0, 2, size=(n, d)), r.normal(0, 2, size=(n, d))
+    c = r.normal(size=d)
+    v = np.tile(c, (n, 1))
+    for causal in (False, True):
+        o, _ = orc.attention_head(q, k, v, 0.5, causal)
+        _close(o, np.tile(c, (n, 1)), 1e-13, f"constant V causal={causal}")
+
+
+def pin_attention_causal_first_row(orc):
+    """Causal row 0 sees key 0 only: o_0 = v_0 and lse_0 = scale <q_0, k_0>."""
+    r = _rng(13)
+    n, d = 16, 5
+    q, k, v = (r.normal(size=(n, d)) for _ in range(3))
+    o, lse = orc.attention_head(q, k, v, 0.9, True, rows=[0])
+    _close(o[0], v[0], 1e-15, "causal row 0 O")
+    _close([lse[0]], [0.9 * float(np.dot(q[0], k[0]))], 1e-14, "causal row 0 LSE")
+
+
+def pin_attention_key_permutation(orc):
+    """Non-causal: permuting K and V rows together leaves O and LSE unchanged."""
+    r = _rng(14)
+    n, d = 40, 7
+    q, k, v = (r.normal(size=(n, d)) for _ in range(3))
+    perm = r.permutation(n)
+    o1, l1 = orc.attention_head(q, k, v, 0.4, False)
+    o2, l2 = orc.attention_head(q, k[perm], v[perm], 0.4, False)
+    _close(o1, o2, 1e-14, "key permutation O")
+    _close(l1, l2, 1e-14, "key permutation LSE")
+
+
+def pin_attention_scale_moves_between_operands(orc):
+    """softmax(s Q K^T) = softmax((s/2)(2Q) K^T), and LSE matches too."""
+    r = _rng(15)
+    n, d = 24, 4
+    q, k, v = (r.normal(size=(n, d)) for _ in range(3))
+    o1, l1 = orc.attention_head(q, k, v, 0.8, True)
+    o2, l2 = orc.attention_head(2 * q, k, v, 0.4, True)
+    o3, l3 = orc.attention_head(q, k, v, 0.4, True)
+    _close(o1, o2, 1e-14, "scale O")
+    _close(l1, l2, 1e-14, "scale LSE")
+    assert np.max(np.abs(o1 - o3)) > 1e-3, "output does not depend on the scale"
+
+
+def pin_attention_probs(orc):
+    """Rows of P are non-negative, sum to one, vanish on hidden keys, and their
+    ratios are p_j / p_k = exp(s_j - s_k) (I2 and the definition of softmax)."""
+    r = _rng(16)
+    n, d = 33, 8
+    q, k = r.normal(size=(n, d)), r.normal(size=(n, d))
+    for causal in (False, True):
+        for i in (0, 5, n - 1):
+            p = orc.attention_probs(q, k, 0.35, causal, i)
+            vis = i + 1 if causal else n
+            assert np.all(p >= 0), "negative probability"
+            assert np.all(p[vis:] == 0), "hidden key has weight"
+            _close([p.sum()], [1.0], 1e-14, "P row sum")
+            s = 0.35 * (k[:vis] @ q[i])
+            _close(np.log(p[:vis] / p[0]), s - s[0], 1e-12, "P log-ratios")
+
+
+def pin_attention_matches_probs_times_v(orc):
+    """O = P V with P from the probability routine (a second path through the definition)."""
+    r = _rng(17)
+    n, d = 21, 6
+    q, k, v = (r.normal(size=(n, d)) for _ in range(3))
+    for causal in (False, True):
+        o, _ = orc.attention_head(q, k, v, 0.6, causal)
+        P = np.stack([orc.attention_probs(q, k, 0.6, causal, i) for i in range(n)])
+        _close(o, P @ v, 1e-14, f"O = P V causal={causal}")
+
+
+def pin_tiled_recurrence_equals_definition(orc):
+    """The per-tile (m, l, O) recurrence equals the three-pass result for any tile
+    size (exact in exact arithmetic; reassociation only in double)."""
+    r = _rng(18)
+    n, d = 150, 16
+    q, k, v = (r.normal(0, 1.5, size=(n, d)) for _ in range(3))
+    for causal in (False, True):
+        o_ref, lse_ref = orc.attention_head(q, k, v, 0.25, causal)
+        for tile in (1, 7, 64, n):
+            for i in (0, 1, 63, 64, 100, n - 1):
+                o, lse, alphas = orc.attention_tiled_row(q, k, v, 0.25, causal, i, tile)
+                _close(o, o_ref[i], 1e-12, f"tiled O tile={tile} row={i} causal={causal}")
+                _close([lse], [lse_ref[i]], 1e-12, f"tiled LSE tile={tile} row={i}")
+                vis = i + 1 if causal else n
+                assert len(alphas) == -(-vis // tile), "wrong number of tiles visited"
+
+
+def pin_rescale_factors(orc):
+    """Every rescale factor lies in [0, 1]; the first one is exactly 0 (m starts at
+    -inf); a factor equals 1 exactly when the running max did not move."""
+    r = _rng(19)
+    n, d = 200, 8
+    q, k, v = (r.normal(0, 2, size=(n, d)) for _ in range(3))
+    tile = 16
+    for i in (3, 77, 199):
+        _, _, alphas = orc.attention_tiled_row(q, k, v, 0.5, False, i, tile)
+        assert alphas[0] == 0.0, "first rescale factor is not 0"
+        assert np.all((alphas >= 0) & (alphas <= 1)), "rescale factor outside [0, 1]"
+        s = 0.5 * (k @ q[i])
+        run = np.maximum.accumulate([s[j:j + tile].max() for j in range(0, n, tile)])
+        moved = np.r_[True, run[1:] > run[:-1]]
+        assert np.array_equal(alphas == 1.0, ~moved), "alpha == 1 does not track a still max"
+
+
+def pin_last_tile_case(orc):
+    """The loud-key workload: every row's largest score lies in the last 64-key
+    tile, and the tile-wise run still rescales (alpha < 1) on that last tile."""
+    w = workloads.ATTN["attn_f32_n256_last"]
+    q, k, v = workloads.attn_head(w)
+    o_ref, _ = orc.attention_head(q, k, v, w.sm_scale, w.causal)
+    n = w.N
+    for i in range(0, n, 5):
+        p = orc.attention_probs(q, k, w.sm_scale, w.causal, i)
+        assert int(np.argmax(p)) >= n - 64, f"row {i}: argmax not in the last tile"
+        o, _, alphas = orc.attention_tiled_row(q, k, v, w.sm_scale, w.causal, i, 64)
+        assert alphas[-1] < 1.0, f"row {i}: no rescale on the last tile"
+        _close(o, o_ref[i], 1e-12, f"last-tile tiled row {i}")
+
+
+ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -1,0 +1,54 @@
+"""Plant mistakes in copies of the oracle and check that the pins catch each one.
+
+Every mutation is a plausible slip (a dropped term, a wrong sign or index, a
+transposed operand, a forgotten rescale) and keeps all memory accesses in
+bounds.  A mutant that passes every pin would mean the pins cannot tell that
+mistake from the definition.
+"""
+import os
+
+import pytest
+
+import oracle
+from oracle_pins import ALL_PINS
+
+MUTATIONS = [
+    ("drop_scale", "s[j] = c->scale * acc;", "s[j] = acc;"),
+    ("causal_off_by_one", "return causal ? i + 1 : n;", "return causal ? i : n;"),
+    ("causal_ignored", "return causal ? i + 1 : n;", "return causal ? n : n;"),
+    ("transposed_scores", "const double* qi = c->q + i * c->d;", "const double* qi = c->k + i * c->d;"),
+    ("reversed_values", "const double* vj = c->v + j * c->d;", "const double* vj = c->v + (nvis - 1 - j) * c->d;"),
+    ("sum_without_max", "    l += exp(s[j] - m);", "    l += exp(s[j]);"),
+    ("lse_without_max", "c->lse[r] = m + log(l);", "c->lse[r] = log(l);"),
+    ("p_wrong_sign", "double pij = exp(s[j] - m) / l;", "double pij = exp(m - s[j]) / l;"),
+    ("p_not_normalised", "double pij = exp(s[j] - m) / l;", "double pij = exp(s[j] - m);"),
+    ("softmax_not_normalised", "y[j] = exp(x[j] - m) / l;", "y[j] = exp(x[j] - m);"),
+    ("softmax_min_not_max", "if (x[j] > m) m = x[j];", "if (x[j] < m) m = x[j];"),
+    ("softmax_sum_unshifted", "    l += exp(x[j] - m);", "    l += exp(x[j]);"),
+    ("online_no_rescale", "dsum = dsum * exp(m - m_next) + exp(x[j] - m_next);", "dsum = dsum + exp(x[j] - m_next);"),
+    ("online_rescale_sign", "dsum = dsum * exp(m - m_next)", "dsum = dsum * exp(m_next - m)"),
+    ("tiled_no_o_rescale", "o[e] = o[e] * alpha;", "o[e] = o[e];"),
+    ("tiled_no_l_rescale", "l = l * alpha + psum;", "l = l + psum;"),
+    ("tiled_tile_max_weights", "psum += exp(s[j] - m_new);", "psum += exp(s[j] - rowmax);"),
+    ("tiled_no_final_divide", "o[e] = o[e] / l;", "o[e] = o[e];"),
+    ("probs_not_normalised", "p[j] = exp(p[j] - m) / l;", "p[j] = exp(p[j] - m);"),
+    ("partition_drops_rows", "jobs[t].end = (t + 1) * per < nrows ? (t + 1) * per : nrows;",
+     "jobs[t].end = (t + 1) * per < nrows ? (t + 1) * per - 1 : nrows;"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_mutant_is_caught(tmp_path, name, old, new):
+    src = open(oracle.SRC).read()
+    assert src.count(old) == 1, f"mutation anchor for {name} not unique in oracle.c"
+    mpath = tmp_path / f"mutant_{name}.c"
+    mpath.write_text(src.replace(old, new))
+    lib = oracle.build(str(mpath), str(tmp_path / f"libmutant_{name}.so"))
+    orc = oracle.load(lib)
+    caught = []
+    for pin in ALL_PINS:
+        try:
+            pin(orc)
+        except (AssertionError, FloatingPointError, ValueError) as e:
+            caught.append(pin.__name__)
+    assert caught, f"mutation {name} passes every pin"

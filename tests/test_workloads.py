@@ -1,0 +1,58 @@
+"""The seeded input generators: determinism, rounding and the recipes' structure."""
+import numpy as np
+import torch
+
+import workloads
+
+
+def test_bf16_rounding_matches_torch():
+    rng = np.random.default_rng(1)
+    x = np.concatenate([rng.standard_normal(100000).astype(np.float32) * 10,
+                        np.array([0.0, -0.0, 1.0, 1.00390625, 1.01171875, 3.4e38, -3.4e38, 1e-40], np.float32)])
+    mine = workloads.f32_to_bf16_bits(x)
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(mine, ref)
+    back = workloads.bf16_bits_to_f32(mine)
+    assert np.array_equal(back, torch.from_numpy(x).to(torch.bfloat16).float().numpy())
+
+
+def test_heads_are_deterministic_and_distinct():
+    w = workloads.ATTN["attn_bf16_b8h32n8192_causal"]
+    a = workloads.attn_head(w, 3, 7)
+    b = workloads.attn_head(w, 3, 7)
+    c = workloads.attn_head(w, 3, 8)
+    for x, y, z in zip(a, b, c):
+        assert x.dtype == np.uint16 and x.shape == (8192, 128)
+        assert np.array_equal(x, y)
+        assert not np.array_equal(x, z)
+
+
+def test_k_row_scaling_range():
+    w = workloads.ATTN["attn_bf16_b8h32n8192_causal"]
+    _, k, _ = workloads.attn_head(w, 0, 0)
+    kf = workloads.bf16_bits_to_f32(k)
+    rms = np.sqrt((kf.astype(np.float64) ** 2).mean(axis=1))
+    # rows are N(0,1) times u ~ U(0.5, 2): the row RMS spans that range up to the
+    # sampling spread of a 128-element RMS (about 6% per row, 25% at the extremes)
+    assert 0.35 < rms.min() < 0.6 and 1.8 < rms.max() < 2.7
+
+
+def test_sample_rows():
+    w = workloads.ATTN["attn_bf16_n131072_causal"]
+    rows = workloads.attn_sample_rows(w, 0, 0)
+    assert rows.size == 256 and np.unique(rows).size == 256
+    for r in (0, 1, 63, 64, 127, 128, w.N - 1):
+        assert r in rows
+    assert np.array_equal(rows, workloads.attn_sample_rows(w, 0, 0))
+    small = workloads.ATTN["attn_bf16_n4096"]
+    assert workloads.attn_sample_rows(small, 0, 0).size == 4096
+
+
+def test_softmax_input_recipe():
+    w = workloads.SOFTMAX["softmax_4096x32768"]
+    x = workloads.softmax_input(w, rows=slice(10, 14))
+    assert x.dtype == np.float32 and x.shape == (4, 32768)
+    spikes = (x == 50.0).sum(axis=1)
+    assert np.all(spikes >= 1) and np.all(np.abs(spikes - 327.68) < 80)
+    assert np.array_equal(x, workloads.softmax_input(w, rows=slice(10, 14)))
+    assert np.array_equal(x[1], workloads.softmax_input(w, rows=slice(11, 12))[0])

@@ -1,0 +1,256 @@
+"""Seeded synthetic inputs for the attention-forward and row-softmax workloads.
+
+This module only draws random numbers and lays them out. It holds none of the
+method's arithmetic (no scores, no exponentials, no normalisation), so both the
+fp64 oracle and the HIP path can consume what it produces without sharing any
+of the computation being checked.
+
+Storage conventions
+-------------------
+* ``"f32"`` tensors are ``np.float32``.
+* ``"f16"`` tensors are ``np.float16`` (numpy's cast rounds to nearest even).
+* ``"bf16"`` tensors are ``np.uint16`` arrays holding bfloat16 bit patterns,
+  produced from float32 draws by round-to-nearest-even.
+* Attention tensors are row-major ``[B, H, N, d]``.
+
+Workloads (sizes and value recipes of the pages' examples):
+* ``attn_f32_n256``      -- one head, N=256, d=64, fp32, non-causal, scale 1/8.
+* ``attn_f32_n256_last`` -- the same shape with the largest score of every
+  query row placed in the final 64-key tile and Q multiplied by 10, so the
+  running maximum still moves on the last tile ("Day 97", the loud key N-3).
+* ``softmax_4096x32768`` -- row softmax input, fp32, N(0,1) with about 1% of
+  entries set to +50.
+* ``attn_bf16_n4096``    -- one head, N=4096, d=64, bf16, non-causal.
+* ``attn_bf16_b8h32n8192_causal`` -- B=8, H=32, N=8192, d=128, bf16, causal,
+  every K row scaled by a U(0.5, 2) factor.
+* ``attn_bf16_n131072_causal`` -- one head, N=131072, d=64, bf16, causal.
+"""
+from __future__ import annotations
+
+import math
+from concurrent.futures import ThreadPoolExecutor
+from dataclasses import dataclass, field
+
+import numpy as np
+
+BASE_SEED = 97000
+
+__all__ = [
+    "AttnWorkload", "SoftmaxWorkload", "ATTN", "SOFTMAX",
+    "f32_to_bf16_bits", "bf16_bits_to_f32", "cast", "attn_head", "attn_full",
+    "attn_sample_rows", "softmax_input", "random_attn", "random_rows",
+]
+
+
+# --------------------------------------------------------------------------
+# bit-level storage helpers (no arithmetic of the method)
+# --------------------------------------------------------------------------
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to bfloat16 (nearest, ties to even); return bits."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    if not np.all(np.isfinite(x)):
+        raise ValueError("bf16 rounding helper expects finite inputs")
+    u = x.view(np.uint32)
+    lsb = (u >> np.uint32(16)) & np.uint32(1)
+    return ((u + np.uint32(0x7FFF) + lsb) >> np.uint32(16)).astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """Exact widening of bfloat16 bit patterns to float32."""
+    b = np.ascontiguousarray(b, dtype=np.uint16)
+    return (b.astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def cast(x32: np.ndarray, dtype: str) -> np.ndarray:
+    """Store float32 draws in the workload's element type."""
+    if dtype == "f32":
+        return np.ascontiguousarray(x32, dtype=np.float32)
+    if dtype == "f16":
+        return np.ascontiguousarray(x32.astype(np.float16))
+    if dtype == "bf16":
+        return f32_to_bf16_bits(x32)
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+# --------------------------------------------------------------------------
+# workload descriptions
+# --------------------------------------------------------------------------
+@dataclass(frozen=True)
+class AttnWorkload:
+    name: str
+    B: int
+    H: int
+    N: int
+    d: int
+    dtype: str
+    causal: bool
+    seed: int
+    k_row_scale: tuple | None = None      # (lo, hi) of a per-key-row U(lo, hi) factor
+    last_tile_max: bool = False           # loud key N-3 + Q x 10
+    sampled_rows: int | None = None       # rows checked per head (None = all)
+    scale: float = field(default=0.0)
+
+    @property
+    def sm_scale(self) -> float:
+        return self.scale if self.scale else 1.0 / math.sqrt(self.d)
+
+    @property
+    def flops(self) -> float:
+        """4*N^2*d per head (QK^T and PV, 2 flops per MAC), halved when causal."""
+        f = 4.0 * self.N * self.N * self.d * self.B * self.H
+        return f / 2.0 if self.causal else f
+
+
+@dataclass(frozen=True)
+class SoftmaxWorkload:
+    name: str
+    rows: int
+    cols: int
+    seed: int
+    spike_prob: float = 0.01
+    spike_value: float = 50.0
+
+    @property
+    def algorithmic_bytes(self) -> int:
+        """One read of X and one write of Y, fp32."""
+        return 8 * self.rows * self.cols
+
+
+ATTN = {
+    w.name: w for w in [
+        AttnWorkload("attn_f32_n256", 1, 1, 256, 64, "f32", False, BASE_SEED + 1),
+        AttnWorkload("attn_f32_n256_last", 1, 1, 256, 64, "f32", False, BASE_SEED + 11,
+                     last_tile_max=True),
+        AttnWorkload("attn_bf16_n4096", 1, 1, 4096, 64, "bf16", False, BASE_SEED + 3),
+        AttnWorkload("attn_bf16_b8h32n8192_causal", 8, 32, 8192, 128, "bf16", True,
+                     BASE_SEED + 4, k_row_scale=(0.5, 2.0), sampled_rows=256),
+        AttnWorkload("attn_bf16_n131072_causal", 1, 1, 131072, 64, "bf16", True,
+                     BASE_SEED + 5, sampled_rows=256),
+    ]
+}
+
+SOFTMAX = {
+    w.name: w for w in [
+        SoftmaxWorkload("softmax_4096x32768", 4096, 32768, BASE_SEED + 2),
+    ]
+}
+
+
+# --------------------------------------------------------------------------
+# attention inputs
+# --------------------------------------------------------------------------
+def _head_f32(w: AttnWorkload, b: int, h: int):
+    """float32 draws of one head's Q, K, V before rounding to the storage type."""
+    rng = np.random.default_rng([w.seed, b, h])
+    q = rng.standard_normal((w.N, w.d), dtype=np.float32)
+    k = rng.standard_normal((w.N, w.d), dtype=np.float32)
+    v = rng.standard_normal((w.N, w.d), dtype=np.float32)
+    if w.k_row_scale is not None:
+        lo, hi = w.k_row_scale
+        u = rng.uniform(lo, hi, size=(w.N, 1)).astype(np.float32)
+        k = k * u
+    if w.last_tile_max:
+        # Every query gets a large positive first coordinate and key N-3 gets a
+        # large first coordinate, so key N-3 (inside the last 64-key tile) is
+        # each row's argmax by a wide margin; then Q is scaled by 10 so the
+        # scores are O(100) and the final rescale factor is tiny.
+        q[:, 0] = np.abs(q[:, 0]) + 1.0
+        k[w.N - 3, 0] += 16.0 * math.sqrt(w.d)
+        q = q * np.float32(10.0)
+    return q, k, v
+
+
+def attn_head(w: AttnWorkload, b: int = 0, h: int = 0):
+    """One head's (q, k, v), each [N, d] in the workload's storage type."""
+    q, k, v = _head_f32(w, b, h)
+    return cast(q, w.dtype), cast(k, w.dtype), cast(v, w.dtype)
+
+
+def attn_full(w: AttnWorkload, threads: int = 8):
+    """Full (q, k, v), each [B, H, N, d] in the storage type (heads drawn in parallel)."""
+    dt = {"f32": np.float32, "f16": np.float16, "bf16": np.uint16}[w.dtype]
+    shape = (w.B, w.H, w.N, w.d)
+    q = np.empty(shape, dt)
+    k = np.empty(shape, dt)
+    v = np.empty(shape, dt)
+
+    def fill(bh):
+        b, h = divmod(bh, w.H)
+        q[b, h], k[b, h], v[b, h] = attn_head(w, b, h)
+
+    with ThreadPoolExecutor(max(1, threads)) as ex:
+        list(ex.map(fill, range(w.B * w.H)))
+    return q, k, v
+
+
+def attn_sample_rows(w: AttnWorkload, b: int, h: int, count: int | None = None) -> np.ndarray:
+    """Sorted distinct query rows checked for head (b, h).
+
+    Always includes the tile and diagonal boundaries {0, 1, 63, 64, 127, 128, N-1}
+    (those below N); the rest are drawn from a seeded stream of their own.
+    """
+    count = w.sampled_rows if count is None else count
+    if count is None or count >= w.N:
+        return np.arange(w.N, dtype=np.int64)
+    fixed = {r for r in (0, 1, 63, 64, 127, 128, w.N - 1) if 0 <= r < w.N}
+    rng = np.random.default_rng([w.seed, b, h, 7])
+    rest = rng.choice(w.N, size=min(w.N, count + len(fixed)), replace=False)
+    rows = list(fixed)
+    for r in rest:
+        if len(rows) >= count:
+            break
+        if int(r) not in fixed:
+            rows.append(int(r))
+    return np.array(sorted(rows), dtype=np.int64)
+
+
+# --------------------------------------------------------------------------
+# softmax inputs
+# --------------------------------------------------------------------------
+def softmax_input(w: SoftmaxWorkload, rows: slice | None = None, threads: int = 8) -> np.ndarray:
+    """X [rows, cols] fp32: N(0,1) with Bernoulli(spike_prob) entries set to spike_value.
+
+    Each row is drawn from its own seeded stream, so any subset of rows can be
+    regenerated alone.
+    """
+    r0, r1 = (0, w.rows) if rows is None else (rows.start or 0, rows.stop or w.rows)
+    x = np.empty((r1 - r0, w.cols), np.float32)
+
+    def fill(chunk):
+        for r in chunk:
+            rng = np.random.default_rng([w.seed, r])
+            row = rng.standard_normal(w.cols, dtype=np.float32)
+            mask = rng.random(w.cols) < w.spike_prob
+            if not mask.any():            # the recipe asks for at least one spike per row
+                mask[rng.integers(w.cols)] = True
+            row[mask] = np.float32(w.spike_value)
+            x[r - r0] = row
+
+    idx = list(range(r0, r1))
+    chunks = [idx[i::max(1, threads)] for i in range(max(1, threads))]
+    with ThreadPoolExecutor(max(1, threads)) as ex:
+        list(ex.map(fill, chunks))
+    return x
+
+
+# --------------------------------------------------------------------------
+# small random cases for edge-case tests
+# --------------------------------------------------------------------------
+def random_attn(B, H, N, d, dtype, seed, std=1.0):
+    """iid N(0, std^2) Q, K, V of shape [B, H, N, d] in the storage type."""
+    rng = np.random.default_rng([BASE_SEED + 500, seed, B, H, N, d])
+    shape = (B, H, N, d)
+    out = []
+    for _ in range(3):
+        x = rng.standard_normal(shape, dtype=np.float32) * np.float32(std)
+        out.append(cast(x, dtype))
+    return tuple(out)
+
+
+def random_rows(rows, cols, seed, std=1.0, spike_prob=0.0, spike_value=50.0):
+    """iid N(0, std^2) fp32 rows, optionally with spikes."""
+    rng = np.random.default_rng([BASE_SEED + 600, seed, rows, cols])
+    x = rng.standard_normal((rows, cols), dtype=np.float32) * np.float32(std)
+    if spike_prob > 0:
+        x[rng.random((rows, cols)) < spike_prob] = np.float32(spike_value)
+    return x
