@@ -1,0 +1,119 @@
+/*
+ * fa.h -- C ABI of the MI355X (gfx950) attention-forward and row-softmax library.
+ *
+ * Two operations, both from the pages on online softmax:
+ *
+ *  - fa_fwd*: the attention forward pass O = softmax(scale * Q K^T) V computed
+ *    tile by tile with the online-softmax recurrence, so the N x N score
+ *    matrix never reaches device memory.  The running statistics follow the
+ *    update equations of "Online softmax, and the register that can't move"
+ *    (section "Online softmax"): per query row, m_new = max(m_old, rowmax S),
+ *    l and O both rescaled by exp(m_old - m_new), O / l once after the last
+ *    key tile.  The causal rule (query i sees keys j <= i) and the skipping of
+ *    key tiles that lie wholly after the query tile follow the causal
+ *    paragraphs of "Online Softmax: Tiling Across a Reduction".  The per-row
+ *    statistic saved for a backward pass is the natural-log logsumexp
+ *    lse_i = ln sum_j exp(scale * q_i . k_j) over the visible keys (the same
+ *    page stores the final maximum and sum; one logsumexp carries both).
+ *
+ *  - online_softmax_rows: y = softmax(x) along each row, with the maximum and
+ *    the sum of exponentials gathered in one fused pass and merged across
+ *    threads by the associative (m, d) rule of the infra-guide page
+ *    "5.2 CUDA Online Softmax" (sections 2.1 and 4.2), then one normalise
+ *    pass.
+ *
+ * Conventions shared by every entry point
+ *  - All tensor pointers are DEVICE pointers owned by the caller; the library
+ *    allocates nothing and keeps no state between calls, so concurrent calls
+ *    on different streams are safe.
+ *  - Work is enqueued asynchronously on `stream` (0 = the null stream); the
+ *    call returns once the kernel is launched.  Outputs are valid after the
+ *    stream is synchronised.
+ *  - Return value: FA_OK or a negative fa_status.  Argument errors are found
+ *    on the host before anything is enqueued and nothing is written; a launch
+ *    failure reported by the HIP runtime is FA_ERR_HIP.  Nothing is printed
+ *    and nothing aborts.
+ *  - Layouts are dense row-major: Q, K, V, O are [B, H, N, d] (d fastest),
+ *    LSE is [B, H, N], softmax X and Y are [rows, cols].  Element offsets are
+ *    64-bit.
+ */
+#ifndef ONLINE_SOFTMAX_04_AMD_FA_H
+#define ONLINE_SOFTMAX_04_AMD_FA_H
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_INVALID_ARG = -1, /* null pointer, size < 1, bad scale, overlapping buffers, size overflow */
+  FA_ERR_UNSUPPORTED = -2, /* a head dimension the library has no kernel for (d other than 64, 128) */
+  FA_ERR_ALIGNMENT = -3,   /* a pointer without the alignment the operation needs */
+  FA_ERR_HIP = -4          /* the HIP runtime reported an error at launch */
+} fa_status;
+
+/*
+ * Attention forward, bfloat16 Q/K/V/O, fp32 accumulation and statistics.
+ *
+ *  q, k, v  [B, H, N, d] bfloat16, 16-byte aligned, read only (may alias each other).
+ *  o        [B, H, N, d] bfloat16, 16-byte aligned, written; must not overlap q, k, v or lse.
+ *  lse      [B, H, N] fp32, 4-byte aligned, written; may be NULL (not written).
+ *  B, H, N  >= 1; B*H*N*d must fit in 63 bits.
+ *  d        head dimension: 64 or 128 (else FA_ERR_UNSUPPORTED).
+ *  scale    softmax scale applied to the fp32 dot products (typically 1/sqrt(d));
+ *           must be finite and > 0.
+ *  causal   0: every query sees all N keys; 1: query i sees keys j <= i.
+ *  O is rounded to bfloat16 (nearest even) once, after the division by l.
+ */
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           int B, int H, int N, int d, float scale, int causal, hipStream_t stream);
+
+/* Same contract with IEEE half-precision Q/K/V/O. */
+int fa_fwd_f16(const void* q, const void* k, const void* v, void* o, float* lse,
+               int B, int H, int N, int d, float scale, int causal, hipStream_t stream);
+
+/* Same contract with fp32 Q/K/V/O: products and sums in fp32 throughout, no
+ * reduced-precision operand anywhere (the fp32 workloads' path). */
+int fa_fwd_f32(const void* q, const void* k, const void* v, void* o, float* lse,
+               int B, int H, int N, int d, float scale, int causal, hipStream_t stream);
+
+/*
+ * Row softmax: y[r, :] = exp(x[r, :] - max_r) / sum_j exp(x[r, j] - max_r).
+ *
+ *  x     [rows, cols] fp32, 4-byte aligned, read only.
+ *  y     [rows, cols] fp32, 4-byte aligned, written; must not overlap x.
+ *  rows, cols >= 1; rows*cols must fit in 63 bits.
+ *  Rows of up to 32768 columns (with cols a multiple of 4 and both pointers
+ *  16-byte aligned) are read from device memory once and written once; longer
+ *  or unaligned rows take a two-read path.  Inputs must be finite.
+ */
+int online_softmax_rows(const float* x, float* y, int rows, int cols, hipStream_t stream);
+
+/* Static description of an fa_status value (never NULL). */
+const char* fa_status_string(int status);
+
+/*
+ * Resources of the kernel an entry point would launch for a shape, for
+ * reports: registers per lane (arch + accumulation VGPRs as the runtime
+ * reports them), LDS bytes per workgroup, private (spill) bytes per lane,
+ * threads per workgroup and resident workgroups per compute unit.
+ *  op: 0 = fa_fwd, 1 = fa_fwd_f16, 2 = fa_fwd_f32, 3 = online_softmax_rows
+ *  (for op 3, `d` carries cols and `causal` is ignored).
+ */
+typedef struct {
+  int regs_per_lane;
+  int lds_bytes;
+  int private_bytes;
+  int threads_per_block;
+  int blocks_per_cu;
+} fa_kernel_attrs;
+
+int fa_kernel_attributes(int op, int d, int causal, fa_kernel_attrs* out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ONLINE_SOFTMAX_04_AMD_FA_H */

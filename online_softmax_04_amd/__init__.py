@@ -1,0 +1,178 @@
+"""Python binding of libfa.so: attention forward and row softmax on gfx950.
+
+The functions named like the C ABI (``fa_fwd``, ``fa_fwd_f16``, ``fa_fwd_f32``,
+``online_softmax_rows``) marshal arguments only: tensors become device
+pointers, the stream defaults to torch's current HIP stream, and a non-zero
+status becomes a ``FaError``.  Every step of the computation runs in the HIP
+kernels of libfa.so; there is no other implementation in this package.
+``attention`` and ``softmax`` allocate outputs with torch and call those.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+__all__ = [
+    "FaError", "lib", "fa_fwd", "fa_fwd_f16", "fa_fwd_f32", "online_softmax_rows",
+    "fa_status_string", "kernel_attributes", "attention", "softmax", "LIB_PATH",
+    "FA_OK", "FA_ERR_INVALID_ARG", "FA_ERR_UNSUPPORTED", "FA_ERR_ALIGNMENT", "FA_ERR_HIP",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
+
+FA_OK = 0
+FA_ERR_INVALID_ARG = -1
+FA_ERR_UNSUPPORTED = -2
+FA_ERR_ALIGNMENT = -3
+FA_ERR_HIP = -4
+
+OP_FA_FWD, OP_FA_FWD_F16, OP_FA_FWD_F32, OP_SOFTMAX = 0, 1, 2, 3
+
+
+class FaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {fa_status_string(status)} (status {status})")
+
+
+class _Attrs(ctypes.Structure):
+    _fields_ = [("regs_per_lane", ctypes.c_int), ("lds_bytes", ctypes.c_int),
+                ("private_bytes", ctypes.c_int), ("threads_per_block", ctypes.c_int),
+                ("blocks_per_cu", ctypes.c_int)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libfa.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m online_softmax_04_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+        for name in ("fa_fwd", "fa_fwd_f16", "fa_fwd_f32"):
+            fn = getattr(L, name)
+            fn.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp]
+            fn.restype = i
+        L.online_softmax_rows.argtypes = [vp, vp, i, i, vp]
+        L.online_softmax_rows.restype = i
+        L.fa_status_string.argtypes = [i]
+        L.fa_status_string.restype = ctypes.c_char_p
+        L.fa_kernel_attributes.argtypes = [i, i, i, ctypes.POINTER(_Attrs)]
+        L.fa_kernel_attributes.restype = i
+        _lib = L
+    return _lib
+
+
+def fa_status_string(status: int) -> str:
+    return lib().fa_status_string(int(status)).decode()
+
+
+def _ptr(x):
+    """Device address of a tensor-like (``data_ptr()``), an int, or None."""
+    if x is None:
+        return None
+    if hasattr(x, "data_ptr"):
+        return int(x.data_ptr())
+    return int(x)
+
+
+def _stream(stream):
+    if stream is not None:
+        return int(getattr(stream, "cuda_stream", stream))
+    import torch
+    if torch.cuda.is_available():
+        return int(torch.cuda.current_stream().cuda_stream)
+    return 0
+
+
+def _check(status: int, where: str):
+    if status != FA_OK:
+        raise FaError(status, where)
+
+
+def _attn(name, q, k, v, o, lse, B, H, N, d, scale, causal, stream):
+    fn = getattr(lib(), name)
+    _check(fn(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), int(B), int(H), int(N), int(d),
+              float(scale), int(causal), _stream(stream)), name)
+
+
+def fa_fwd(q, k, v, o, lse, B, H, N, d, scale, causal, stream=None):
+    """bf16 attention forward (see include/fa.h); q, k, v, o, lse are device buffers."""
+    _attn("fa_fwd", q, k, v, o, lse, B, H, N, d, scale, causal, stream)
+
+
+def fa_fwd_f16(q, k, v, o, lse, B, H, N, d, scale, causal, stream=None):
+    """fp16 attention forward (see include/fa.h)."""
+    _attn("fa_fwd_f16", q, k, v, o, lse, B, H, N, d, scale, causal, stream)
+
+
+def fa_fwd_f32(q, k, v, o, lse, B, H, N, d, scale, causal, stream=None):
+    """fp32 attention forward (see include/fa.h)."""
+    _attn("fa_fwd_f32", q, k, v, o, lse, B, H, N, d, scale, causal, stream)
+
+
+def online_softmax_rows(x, y, rows, cols, stream=None):
+    """Row softmax of an fp32 [rows, cols] device buffer into y (see include/fa.h)."""
+    _check(lib().online_softmax_rows(_ptr(x), _ptr(y), int(rows), int(cols), _stream(stream)),
+           "online_softmax_rows")
+
+
+def kernel_attributes(op: int, d: int, causal: bool = False) -> dict:
+    """Registers, LDS, spill bytes, block size and occupancy of the kernel an op launches."""
+    a = _Attrs()
+    _check(lib().fa_kernel_attributes(int(op), int(d), int(causal), ctypes.byref(a)),
+           "fa_kernel_attributes")
+    return {f: getattr(a, f) for f, _ in _Attrs._fields_}
+
+
+# ---------------------------------------------------------------------------
+# torch conveniences
+# ---------------------------------------------------------------------------
+def _entry_for(dtype):
+    import torch
+    return {torch.bfloat16: "fa_fwd", torch.float16: "fa_fwd_f16",
+            torch.float32: "fa_fwd_f32"}.get(dtype)
+
+
+def attention(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse=None,
+              stream=None):
+    """O, LSE = attention forward of [B, H, N, d] device tensors (bf16, fp16 or fp32).
+
+    Returns (o, lse) with o like q and lse fp32 [B, H, N].
+    """
+    import torch
+    for t in (q, k, v):
+        if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+            raise TypeError("q, k, v must be device tensors")
+        if not t.is_contiguous() or t.dim() != 4 or t.shape != q.shape or t.dtype != q.dtype:
+            raise ValueError("q, k, v must be contiguous [B, H, N, d] tensors of one dtype")
+    name = _entry_for(q.dtype)
+    if name is None:
+        raise TypeError(f"unsupported dtype {q.dtype}")
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    _attn(name, q, k, v, out, lse, B, H, N, d, scale, causal, stream)
+    return out, lse
+
+
+def softmax(x, out=None, stream=None):
+    """Row softmax of a contiguous fp32 [rows, cols] device tensor."""
+    import torch
+    if not isinstance(x, torch.Tensor) or x.device.type != "cuda" or x.dtype != torch.float32:
+        raise TypeError("x must be an fp32 device tensor")
+    if x.dim() != 2 or not x.is_contiguous():
+        raise ValueError("x must be a contiguous [rows, cols] tensor")
+    if out is None:
+        out = torch.empty_like(x)
+    online_softmax_rows(x, out, x.shape[0], x.shape[1], stream)
+    return out

@@ -1,0 +1,122 @@
+// C ABI of the library: argument validation on the host, then one kernel launch.
+// Validation happens before any HIP runtime call, so every error path below is
+// reachable and testable without a GPU.
+#include <climits>
+#include <cmath>
+#include <cstdint>
+
+#include "../../include/fa.h"
+#include "kernels.h"
+
+namespace {
+
+bool overlaps(const void* a, uint64_t abytes, const void* b, uint64_t bbytes) {
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return x < y + bbytes && y < x + abytes;
+}
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+// Bytes of a B*H*N*d tensor (0 on overflow of 63 bits).
+uint64_t tensor_bytes(int B, int H, int N, int d, uint64_t elem) {
+  unsigned __int128 n = (unsigned __int128)B * (unsigned __int128)H * (unsigned __int128)N *
+                        (unsigned __int128)d * elem;
+  if (n >= ((unsigned __int128)1 << 63)) return 0;
+  return (uint64_t)n;
+}
+
+int attn_entry(osm::Elem elem, const void* q, const void* k, const void* v, void* o, float* lse,
+               int B, int H, int N, int d, float scale, int causal, hipStream_t stream) {
+  if (!q || !k || !v || !o) return FA_ERR_INVALID_ARG;
+  if (B < 1 || H < 1 || N < 1 || d < 1) return FA_ERR_INVALID_ARG;
+  if (!std::isfinite(scale) || !(scale > 0.f)) return FA_ERR_INVALID_ARG;
+  if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
+  const uint64_t esz = elem == osm::Elem::f32 ? 4 : 2;
+  const uint64_t bytes = tensor_bytes(B, H, N, d, esz);
+  const uint64_t lse_bytes = tensor_bytes(B, H, N, 1, 4);
+  if (bytes == 0 || lse_bytes == 0) return FA_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  // one workgroup per (batch*head, query block) must fit a 1-D grid
+  const uint64_t rows_per_block = 128;
+  const uint64_t blocks = (uint64_t)B * (uint64_t)H * (((uint64_t)N + rows_per_block - 1) / rows_per_block);
+  if (blocks > (uint64_t)INT_MAX) return FA_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16)) return FA_ERR_ALIGNMENT;
+  if (lse && !aligned(lse, 4)) return FA_ERR_ALIGNMENT;
+  if (overlaps(o, bytes, q, bytes) || overlaps(o, bytes, k, bytes) || overlaps(o, bytes, v, bytes))
+    return FA_ERR_INVALID_ARG;
+  if (lse && (overlaps(lse, lse_bytes, o, bytes) || overlaps(lse, lse_bytes, q, bytes) ||
+              overlaps(lse, lse_bytes, k, bytes) || overlaps(lse, lse_bytes, v, bytes)))
+    return FA_ERR_INVALID_ARG;
+  hipError_t e = osm::launch_attn_fwd(elem, q, k, v, o, lse, B, H, N, d, scale, causal != 0, stream);
+  if (e != hipSuccess) return FA_ERR_HIP;
+  return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
+           int d, float scale, int causal, hipStream_t stream) {
+  return attn_entry(osm::Elem::bf16, q, k, v, o, lse, B, H, N, d, scale, causal, stream);
+}
+
+int fa_fwd_f16(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+               int N, int d, float scale, int causal, hipStream_t stream) {
+  return attn_entry(osm::Elem::f16, q, k, v, o, lse, B, H, N, d, scale, causal, stream);
+}
+
+int fa_fwd_f32(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+               int N, int d, float scale, int causal, hipStream_t stream) {
+  return attn_entry(osm::Elem::f32, q, k, v, o, lse, B, H, N, d, scale, causal, stream);
+}
+
+int online_softmax_rows(const float* x, float* y, int rows, int cols, hipStream_t stream) {
+  if (!x || !y) return FA_ERR_INVALID_ARG;
+  if (rows < 1 || cols < 1) return FA_ERR_INVALID_ARG;
+  const uint64_t bytes = tensor_bytes(rows, cols, 1, 1, 4);
+  if (bytes == 0) return FA_ERR_INVALID_ARG;
+  if (!aligned(x, 4) || !aligned(y, 4)) return FA_ERR_ALIGNMENT;
+  if (overlaps(x, bytes, y, bytes)) return FA_ERR_INVALID_ARG;
+  const bool vec_ok = aligned(x, 16) && aligned(y, 16) && (cols % 4 == 0);
+  hipError_t e = osm::launch_softmax(x, y, rows, cols, vec_ok, stream);
+  if (e != hipSuccess) return FA_ERR_HIP;
+  return FA_OK;
+}
+
+const char* fa_status_string(int status) {
+  switch (status) {
+    case FA_OK: return "FA_OK: success";
+    case FA_ERR_INVALID_ARG: return "FA_ERR_INVALID_ARG: null pointer, size, scale, overlap or overflow";
+    case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: head dimension without a kernel (64 and 128 are supported)";
+    case FA_ERR_ALIGNMENT: return "FA_ERR_ALIGNMENT: pointer not aligned as the operation requires";
+    case FA_ERR_HIP: return "FA_ERR_HIP: the HIP runtime reported a launch error";
+    default: return "unknown fa_status";
+  }
+}
+
+int fa_kernel_attributes(int op, int d, int causal, fa_kernel_attrs* out) {
+  if (!out) return FA_ERR_INVALID_ARG;
+  hipFuncAttributes attr;
+  int threads = 0, blocks = 0;
+  hipError_t e;
+  if (op >= 0 && op <= 2) {
+    if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+    const osm::Elem elem = op == 0 ? osm::Elem::bf16 : (op == 1 ? osm::Elem::f16 : osm::Elem::f32);
+    e = osm::attn_fwd_attributes(elem, d, causal != 0, &attr, &threads, &blocks);
+  } else if (op == 3) {
+    if (d < 1) return FA_ERR_INVALID_ARG;
+    e = osm::softmax_attributes(d, d % 4 == 0, &attr, &threads, &blocks);
+  } else {
+    return FA_ERR_INVALID_ARG;
+  }
+  if (e != hipSuccess) return FA_ERR_HIP;
+  out->regs_per_lane = attr.numRegs;
+  out->lds_bytes = (int)attr.sharedSizeBytes;
+  out->private_bytes = (int)attr.localSizeBytes;
+  out->threads_per_block = threads;
+  out->blocks_per_cu = blocks;
+  return FA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,214 @@
+// Row-wise online softmax for gfx950.
+//
+// Method (infra-guide "5.2 CUDA Online Softmax"): the row maximum m and the
+// sum of exponentials d are gathered in one fused pass; partial (m, d) pairs
+// held by different lanes merge with the associative rule
+//     m = max(m1, m2),  d = d1 * e^(m1 - m) + d2 * e^(m2 - m)      (section 4.2)
+// and a second pass normalises.  Two kernels:
+//
+//  * softmax_cached: the whole row is held in VGPRs (section 6, "register
+//    cache"), so the row is read from HBM once and written once -- the floor of
+//    8 bytes per fp32 element.  Each lane caches NV f32x4 chunks; chunk i of
+//    lane t is element group i*THREADS + t, so every load and store instruction
+//    of a wave covers 1 KiB of contiguous memory.  Instead of the per-element
+//    recurrence, a lane takes its slice as one tile: its max m_t, then
+//    e = 2^((x - m_t) log2 e) kept in place of x and d_t = sum e.  After the
+//    (m, d) merge, y = e * 2^((m_t - m) log2 e) / d, so no element is
+//    exponentiated twice.  Loads and stores are non-temporal: every byte is
+//    touched once.
+//
+//  * softmax_stream: rows longer than the cache, or not 16-byte aligned /
+//    not a multiple of 4 columns: pass 1 runs the per-chunk online recurrence
+//    while streaming the row (sections 2.2, 5), pass 2 re-reads and normalises.
+//
+// One workgroup per row; the grid is the row count (the hardware dispatcher
+// keeps every CU fed, so no software grid-stride loop is needed).
+#include "common.h"
+#include "kernels.h"
+
+namespace osm {
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Merge (mo, lo) into (m, l).  A side with m = -inf carries l = 0.
+__device__ __forceinline__ void merge_ml(float& m, float& l, float mo, float lo) {
+  const float M = fmaxf(m, mo);
+  const float Ms = (M == kNegInf) ? 0.f : M;  // both empty: keep l = 0, avoid -inf - -inf
+  l = l * exp2_fast((m - Ms) * kLog2e) + lo * exp2_fast((mo - Ms) * kLog2e);
+  m = M;
+}
+
+// Merge (m, l) over the workgroup; every thread returns the same pair.
+template <int THREADS>
+__device__ __forceinline__ void block_merge(float& m, float& l) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    const float mo = __shfl_xor(m, off);
+    const float lo = __shfl_xor(l, off);
+    merge_ml(m, l, mo, lo);  // symmetric: both partners compute the same bits
+  }
+  constexpr int W = THREADS / 64;
+  if constexpr (W > 1) {
+    __shared__ float sm[W], sl[W];
+    const int wave = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) {
+      sm[wave] = m;
+      sl[wave] = l;
+    }
+    __syncthreads();
+    m = sm[0];
+    l = sl[0];
+#pragma unroll
+    for (int w = 1; w < W; ++w) merge_ml(m, l, sm[w], sl[w]);
+  }
+}
+
+__device__ __forceinline__ float max4(f32x4 v) { return fmaxf(fmaxf(v.x, v.y), fmaxf(v.z, v.w)); }
+
+template <int THREADS, int NV>
+__global__ __launch_bounds__(THREADS) void softmax_cached(const float* __restrict__ x,
+                                                          float* __restrict__ y, int cols) {
+  const size_t row = blockIdx.x;
+  const f32x4* xr = reinterpret_cast<const f32x4*>(x + row * (size_t)cols);
+  f32x4* yr = reinterpret_cast<f32x4*>(y + row * (size_t)cols);
+  const int nvec = cols >> 2;
+  const int t = threadIdx.x;
+
+  f32x4 c[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int idx = i * THREADS + t;
+    if (idx < nvec) {
+      c[i] = __builtin_nontemporal_load(xr + idx);
+    } else {
+      c[i] = f32x4{kNegInf, kNegInf, kNegInf, kNegInf};
+    }
+  }
+  // the lane's slice as one tile: max, then exponentials against it
+  float m = kNegInf;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) m = fmaxf(m, max4(c[i]));
+  const float m_lane = m;
+  // x - m first, then the log2(e) factor: x - m <= 0, so the product can only
+  // overflow towards -inf (exponential 0), even for inputs near -FLT_MAX.
+  const float ms = (m == kNegInf) ? 0.f : m;  // a lane without elements keeps l = 0
+  float l = 0.f;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    c[i] = (c[i] - ms) * kLog2e;
+    c[i].x = exp2_fast(c[i].x);
+    c[i].y = exp2_fast(c[i].y);
+    c[i].z = exp2_fast(c[i].z);
+    c[i].w = exp2_fast(c[i].w);
+    l += (c[i].x + c[i].y) + (c[i].z + c[i].w);
+  }
+  block_merge<THREADS>(m, l);
+  // y = e * 2^((m_lane - m) log2 e) / l   (a lane without elements never stores)
+  const float f = exp2_fast((m_lane - m) * kLog2e) / l;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int idx = i * THREADS + t;
+    if (idx < nvec) {
+      const f32x4 v = c[i] * f;
+      __builtin_nontemporal_store(v, yr + idx);
+    }
+  }
+}
+
+template <int THREADS, bool VEC>
+__global__ __launch_bounds__(THREADS) void softmax_stream(const float* __restrict__ x,
+                                                          float* __restrict__ y, int cols) {
+  const size_t row = blockIdx.x;
+  const float* xr = x + row * (size_t)cols;
+  float* yr = y + row * (size_t)cols;
+  const int t = threadIdx.x;
+  float m = kNegInf, l = 0.f;
+  if constexpr (VEC) {
+    const int nvec = cols >> 2;
+    const f32x4* x4 = reinterpret_cast<const f32x4*>(xr);
+    for (int idx = t; idx < nvec; idx += THREADS) {
+      const f32x4 v = x4[idx];
+      const float mn = fmaxf(m, max4(v));  // step 1: new running max
+      const f32x4 e = (v - mn) * kLog2e;
+      l = l * exp2_fast((m - mn) * kLog2e) +  // step 2: rescale, add the chunk
+          (exp2_fast(e.x) + exp2_fast(e.y)) + (exp2_fast(e.z) + exp2_fast(e.w));
+      m = mn;
+    }
+  } else {
+    for (int j = t; j < cols; j += THREADS) {
+      const float v = xr[j];
+      const float mn = fmaxf(m, v);
+      l = l * exp2_fast((m - mn) * kLog2e) + exp2_fast((v - mn) * kLog2e);
+      m = mn;
+    }
+  }
+  block_merge<THREADS>(m, l);
+  const float inv = 1.f / l;
+  if constexpr (VEC) {
+    const int nvec = cols >> 2;
+    const f32x4* x4 = reinterpret_cast<const f32x4*>(xr);
+    f32x4* y4 = reinterpret_cast<f32x4*>(yr);
+    for (int idx = t; idx < nvec; idx += THREADS) {
+      const f32x4 e = (x4[idx] - m) * kLog2e;
+      const f32x4 o = f32x4{exp2_fast(e.x), exp2_fast(e.y), exp2_fast(e.z), exp2_fast(e.w)} * inv;
+      __builtin_nontemporal_store(o, y4 + idx);
+    }
+  } else {
+    for (int j = t; j < cols; j += THREADS) yr[j] = exp2_fast((xr[j] - m) * kLog2e) * inv;
+  }
+}
+
+struct CachedConfig {
+  int capacity;  // columns
+  const void* fn;
+  int threads;
+};
+
+}  // namespace
+
+// Smallest register-cache instance that holds the row, or the streaming kernel.
+static void pick_softmax(int cols, bool vec_ok, const void** fn, int* threads) {
+  static const CachedConfig table[] = {
+      {256, (const void*)softmax_cached<64, 1>, 64},
+      {1024, (const void*)softmax_cached<64, 4>, 64},
+      {2048, (const void*)softmax_cached<128, 4>, 128},
+      {4096, (const void*)softmax_cached<256, 4>, 256},
+      {8192, (const void*)softmax_cached<256, 8>, 256},
+      {16384, (const void*)softmax_cached<512, 8>, 512},
+      {32768, (const void*)softmax_cached<512, 16>, 512},
+  };
+  if (vec_ok) {
+    for (const auto& c : table) {
+      if (cols <= c.capacity) {
+        *fn = c.fn;
+        *threads = c.threads;
+        return;
+      }
+    }
+    *fn = (const void*)softmax_stream<512, true>;
+  } else {
+    *fn = (const void*)softmax_stream<512, false>;
+  }
+  *threads = 512;
+}
+
+hipError_t launch_softmax(const float* x, float* y, int rows, int cols, bool vec_ok,
+                          hipStream_t stream) {
+  const void* fn;
+  int threads;
+  pick_softmax(cols, vec_ok, &fn, &threads);
+  void* args[] = {(void*)&x, (void*)&y, (void*)&cols};
+  return hipLaunchKernel(fn, dim3(rows), dim3(threads), args, 0, stream);
+}
+
+hipError_t softmax_attributes(int cols, bool vec_ok, hipFuncAttributes* attr, int* threads,
+                              int* blocks_per_cu) {
+  const void* fn;
+  pick_softmax(cols, vec_ok, &fn, threads);
+  hipError_t e = hipFuncGetAttributes(attr, fn);
+  if (e != hipSuccess) return e;
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, fn, *threads, 0);
+}
+
+}  // namespace osm

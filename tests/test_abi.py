@@ -1,0 +1,143 @@
+"""The C ABI without a GPU: the library loads, exports what include/fa.h declares,
+and rejects bad arguments on the host before any HIP call is made."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import online_softmax_04_amd as fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADERS = [os.path.join(ROOT, "include", f) for f in os.listdir(os.path.join(ROOT, "include"))
+           if f.endswith(".h")]
+
+# Fake device addresses: validation rejects every call below before touching them.
+A = 0x7f0000000000
+MB = 1 << 20
+
+
+def declared_functions():
+    names = []
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names += re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\([^;]*\)\s*;", text, flags=re.M)
+    return names
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("fa_fwd", "fa_fwd_f16", "fa_fwd_f32", "online_softmax_rows", "fa_status_string",
+              "fa_kernel_attributes"):
+        assert n in names
+
+
+@pytest.mark.parametrize("name", declared_functions())
+def test_library_exports_declared_symbol(name):
+    lib = ctypes.CDLL(fa.LIB_PATH)
+    assert hasattr(lib, name), f"libfa.so does not export {name}"
+
+
+def test_status_strings():
+    for s in (fa.FA_OK, fa.FA_ERR_INVALID_ARG, fa.FA_ERR_UNSUPPORTED, fa.FA_ERR_ALIGNMENT,
+              fa.FA_ERR_HIP):
+        assert fa.fa_status_string(s).startswith("FA_")
+    assert fa.fa_status_string(12345) == "unknown fa_status"
+
+
+def call_attn(name="fa_fwd", q=A, k=A + 64 * MB, v=A + 128 * MB, o=A + 192 * MB,
+              lse=A + 256 * MB, B=1, H=2, N=128, d=64, scale=0.125, causal=0):
+    fn = getattr(fa.lib(), name)
+    return fn(q, k, v, o, lse, B, H, N, d, scale, causal, None)
+
+
+ENTRIES = ["fa_fwd", "fa_fwd_f16", "fa_fwd_f32"]
+
+
+@pytest.mark.parametrize("name", ENTRIES)
+@pytest.mark.parametrize("kw", [dict(q=0), dict(k=0), dict(v=0), dict(o=0)])
+def test_attn_null_pointer(name, kw):
+    assert call_attn(name, **kw) == fa.FA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("name", ENTRIES)
+@pytest.mark.parametrize("kw", [dict(B=0), dict(H=0), dict(N=0), dict(d=0), dict(B=-1),
+                                dict(N=-5)])
+def test_attn_bad_sizes(name, kw):
+    assert call_attn(name, **kw) == fa.FA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("name", ENTRIES)
+@pytest.mark.parametrize("scale", [0.0, -0.125, math.inf, -math.inf, math.nan])
+def test_attn_bad_scale(name, scale):
+    assert call_attn(name, scale=scale) == fa.FA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("name", ENTRIES)
+def test_attn_bad_causal_flag(name):
+    assert call_attn(name, causal=2) == fa.FA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("name", ENTRIES)
+@pytest.mark.parametrize("d", [1, 16, 32, 63, 96, 127, 192, 256])
+def test_attn_unsupported_head_dim(name, d):
+    """Head dims without a kernel are an error, never a silent slow path."""
+    assert call_attn(name, d=d) == fa.FA_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("name", ENTRIES)
+def test_attn_size_overflow(name):
+    assert call_attn(name, B=1 << 20, H=1 << 20, N=1 << 20, d=128) == fa.FA_ERR_INVALID_ARG
+    # more workgroups than a 1-D grid holds
+    assert call_attn(name, B=1 << 16, H=1 << 16, N=256, d=64) == fa.FA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("name", ENTRIES)
+@pytest.mark.parametrize("kw", [dict(q=A + 2), dict(k=A + 64 * MB + 8), dict(v=A + 128 * MB + 4),
+                                dict(o=A + 192 * MB + 2), dict(lse=A + 256 * MB + 2)])
+def test_attn_alignment(name, kw):
+    assert call_attn(name, **kw) == fa.FA_ERR_ALIGNMENT
+
+
+@pytest.mark.parametrize("name", ENTRIES)
+@pytest.mark.parametrize("kw", [dict(o=A), dict(o=A + 64 * MB + 1024), dict(o=A + 128 * MB - 1024),
+                                dict(lse=A + 192 * MB + 16), dict(lse=A)])
+def test_attn_overlap(name, kw):
+    assert call_attn(name, **kw) == fa.FA_ERR_INVALID_ARG
+
+
+def call_softmax(x=A, y=A + 64 * MB, rows=4, cols=100):
+    return fa.lib().online_softmax_rows(x, y, rows, cols, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=0), fa.FA_ERR_INVALID_ARG), (dict(y=0), fa.FA_ERR_INVALID_ARG),
+    (dict(rows=0), fa.FA_ERR_INVALID_ARG), (dict(cols=0), fa.FA_ERR_INVALID_ARG),
+    (dict(rows=-3), fa.FA_ERR_INVALID_ARG),
+    (dict(x=A + 2), fa.FA_ERR_ALIGNMENT), (dict(y=A + 64 * MB + 1), fa.FA_ERR_ALIGNMENT),
+    (dict(y=A + 1200), fa.FA_ERR_INVALID_ARG), (dict(y=A), fa.FA_ERR_INVALID_ARG),
+    (dict(x=A + 64 * MB - 400), fa.FA_ERR_INVALID_ARG),
+])
+def test_softmax_validation(kw, status):
+    assert call_softmax(**kw) == status
+
+
+def test_python_wrappers_raise():
+    with pytest.raises(fa.FaError) as e:
+        fa.fa_fwd(0, A, A, A, None, 1, 1, 16, 64, 0.1, 0)
+    assert e.value.status == fa.FA_ERR_INVALID_ARG
+    with pytest.raises(fa.FaError) as e:
+        fa.online_softmax_rows(A, A + 64 * MB, 0, 8)
+    assert e.value.status == fa.FA_ERR_INVALID_ARG
+
+
+def test_product_path_has_no_cpu_fallback():
+    """The package never reaches the oracle and never computes on the host."""
+    pkg = os.path.join(ROOT, "online_softmax_04_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "oracle" not in text, f"{f} mentions the oracle"
+                assert "import numpy" not in text, f"{f} imports numpy"

@@ -1,0 +1,103 @@
+"""Row softmax on the GPU (through the C ABI) against the fp64 oracle.
+
+The full 4096 x 32768 workload is compared element by element; edge cases
+cover every register-cache size class and its boundaries, the streaming path
+(rows longer than the cache, unaligned pointers, columns not a multiple of 4),
+constant rows, spiked rows and extreme magnitudes.  Gate: max-abs <= 1e-4.
+"""
+import numpy as np
+import pytest
+import torch
+
+import online_softmax_04_amd as fa
+import oracle
+import workloads
+from gpu_util import gate, say, to_f64
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def orc():
+    return oracle.load()
+
+
+def run_gpu(x: np.ndarray, offset: int = 0):
+    """Softmax of x on the GPU; offset > 0 places both buffers `offset` floats past
+    a 16-byte boundary (forcing the unaligned path)."""
+    rows, cols = x.shape
+    n = rows * cols
+    xb = torch.empty(n + offset, dtype=torch.float32, device="cuda")
+    yb = torch.empty(n + offset, dtype=torch.float32, device="cuda")
+    xd, yd = xb[offset:], yb[offset:]
+    xd.copy_(torch.from_numpy(np.ascontiguousarray(x).ravel()))
+    fa.online_softmax_rows(xd, yd, rows, cols)
+    torch.cuda.synchronize()
+    return yd.view(rows, cols)
+
+
+def test_workload(orc):
+    w = workloads.SOFTMAX["softmax_4096x32768"]
+    say(f"[softmax workload {w.name}] rows={w.rows} cols={w.cols}")
+    x = workloads.softmax_input(w)
+    y = run_gpu(x)
+    got = to_f64(y)
+    ref = orc.softmax_rows(x)
+    gate(w.name, got, ref, "f32")
+    sums = got.sum(axis=1)
+    assert np.max(np.abs(sums - 1.0)) < 1e-4
+    # relative accuracy where it matters: the +50 entries carry the mass
+    spikes = x == 50.0
+    assert np.max(np.abs(got[spikes] - ref[spikes]) / ref[spikes]) < 1e-5
+
+
+def test_workload_is_deterministic():
+    w = workloads.SOFTMAX["softmax_4096x32768"]
+    x = workloads.softmax_input(w, rows=slice(0, 256))
+    say("[softmax determinism]")
+    assert torch.equal(run_gpu(x), run_gpu(x))
+
+
+EDGE_COLS = [1, 2, 3, 4, 5, 63, 64, 65, 255, 256, 257, 1000, 1023, 1024, 1025, 2048, 4095, 4096,
+             4100, 8192, 8196, 16384, 16388, 32764, 32768, 32772, 50000, 65536]
+
+
+@pytest.mark.parametrize("cols", EDGE_COLS)
+@pytest.mark.parametrize("offset", [0, 1])
+def test_edge_cols(orc, cols, offset):
+    rows = 5
+    say(f"[softmax edge] cols={cols} offset={offset}")
+    x = workloads.random_rows(rows, cols, seed=cols, std=3.0, spike_prob=0.01)
+    gate(f"cols={cols} off={offset}", to_f64(run_gpu(x, offset)), orc.softmax_rows(x), "f32")
+
+
+@pytest.mark.parametrize("cols", [7, 4096, 32768, 40000])
+def test_special_rows(orc, cols):
+    say(f"[softmax special rows] cols={cols}")
+    x = np.zeros((4, cols), np.float32)
+    x[0] = 1.5                                   # constant row -> 1/cols
+    x[1] = -1e4                                  # constant, very negative
+    x[1, cols // 2] = 80.0                       # one spike holds all the mass
+    x[2] = np.linspace(-60, 60, cols, dtype=np.float32)
+    x[3] = -3e38                                 # extreme but finite
+    x[3, 0] = 0.0
+    got = to_f64(run_gpu(x))
+    gate(f"special cols={cols}", got, orc.softmax_rows(x), "f32")
+    assert np.allclose(got[0], 1.0 / cols, rtol=1e-5, atol=0)
+    assert got[1, cols // 2] == 1.0
+
+
+def test_many_rows_small_cols(orc):
+    x = workloads.random_rows(70000, 33, seed=3)
+    say("[softmax many rows]")
+    gate("70000x33", to_f64(run_gpu(x)), orc.softmax_rows(x), "f32")
+
+
+def test_wrapper():
+    x = torch.randn(3, 100, device="cuda")
+    y = fa.softmax(x)
+    assert torch.allclose(y.sum(dim=1), torch.ones(3, device="cuda"), atol=1e-5)
+    with pytest.raises(TypeError):
+        fa.softmax(x.double())
+    with pytest.raises(ValueError):
+        fa.softmax(x.t())
