@@ -1,0 +1,342 @@
+#!/usr/bin/env python3
+"""Benchmark of the hot path on one MI355X: attention forward + row online softmax.
+
+One step = one attention forward over the batched causal workload (B=8, H=32,
+N=8192, d=128, bf16, K rows scaled by U(0.5, 2)) followed by one row softmax
+over the 4096 x 32768 fp32 workload, inputs already resident in device memory.
+
+Prints ONE JSON line:
+  value       attention TFLOP/s = 4*N^2*d*B*H/2 (causal) / mean attention
+              kernel time, from HIP events on the stream the kernels run on;
+  softmax     GB/s = 8 bytes per element (one read of X, one write of Y) /
+              mean softmax kernel time;
+  roofline    the attention kernel against the dense bf16 MFMA peak, with
+              HBM traffic from the committed rocprofv3 counter summary when
+              it was taken on the current kernel source;
+  cpu_baseline  the fp64 oracle timed on this host's cores over a bounded
+              sample of query rows of the same workload.
+
+Other modes:
+  --ingest-counters DIR_FETCH DIR_WRITE   turn two rocprofv3 --pmc runs
+        (FETCH_SIZE, then WRITE_SIZE) of this script into the traffic
+        summary under profiles/.
+  --ingest-trace DIR   turn a rocprofv3 --kernel-trace --stats run of this
+        script into the kernel-duration summary under profiles/.
+"""
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attn fwd TFLOP/s at B=8,H=32,N=8192,d=128 bf16 + % MFMA peak; softmax GB/s"
+ATTN_WORKLOAD = "attn_bf16_b8h32n8192_causal"
+SOFTMAX_WORKLOAD = "softmax_4096x32768"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBPS = 8000.0         # MI355X HBM3E, published
+COPY_BYTES = 256 << 20         # probe copy kernel: 256 MiB read + 256 MiB written
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.md")
+KERNEL_SOURCES = {
+    "attn": ["online_softmax_04_amd/csrc/attn_fwd.hip", "online_softmax_04_amd/csrc/common.h"],
+    "softmax": ["online_softmax_04_amd/csrc/softmax.hip", "online_softmax_04_amd/csrc/common.h"],
+}
+# kernel-name fragments of the three dispatches the counters are read for; the
+# probe copy is torch's elementwise multiply by 1 (reads and writes 256 MiB)
+KERNEL_NAME_PART = {"attn": "attn_fwd_mfma", "softmax": "softmax_cached", "copy": "MulFunctor"}
+
+
+def source_hash(kind: str) -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kind]:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+# ---------------------------------------------------------------------------
+# traffic summary (rocprofv3 counters)
+# ---------------------------------------------------------------------------
+def _counter_rows(d):
+    """Per-dispatch counter rows of a rocprofv3 --pmc run: its CSV output, or the
+    counters_collection view of its rocpd database."""
+    import csv
+    import sqlite3
+    rows = []
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            rows += list(csv.DictReader(fh))
+    if not rows:
+        for f in glob.glob(os.path.join(d, "**", "*.db"), recursive=True):
+            con = sqlite3.connect(f)
+            for did, name, cname, val in con.execute(
+                    "select dispatch_id, kernel_name, counter_name, value from counters_collection"):
+                rows.append({"Dispatch_Id": did, "Kernel_Name": name, "Counter_Name": cname,
+                             "Counter_Value": val})
+    if not rows:
+        raise SystemExit(f"no counter rows under {d}")
+    return rows
+
+
+def _per_kernel(rows, counter):
+    """Mean counter value per dispatch for each kernel family (attn, softmax, copy)."""
+    per_dispatch = {}
+    for r in rows:
+        if r.get("Counter_Name") != counter:
+            continue
+        name = r.get("Kernel_Name", "")
+        for kind, part in KERNEL_NAME_PART.items():
+            if part in name:
+                key = (kind, r.get("Dispatch_Id"))
+                per_dispatch[key] = per_dispatch.get(key, 0.0) + float(r["Counter_Value"])
+    out = {}
+    for (kind, _), val in per_dispatch.items():
+        out.setdefault(kind, []).append(val)
+    return {k: sum(v) / len(v) for k, v in out.items()}
+
+
+def ingest_counters(dir_fetch: str, dir_write: str):
+    fetch = _per_kernel(_counter_rows(dir_fetch), "FETCH_SIZE")
+    write = _per_kernel(_counter_rows(dir_write), "WRITE_SIZE")
+    for need in ("attn", "softmax", "copy"):
+        if need not in fetch or need not in write:
+            raise SystemExit(f"counters for {need} missing (fetch {sorted(fetch)}, write {sorted(write)})")
+    # FETCH_SIZE / WRITE_SIZE are in KiB per dispatch; scale each by what it
+    # reads for the probe copy of known size
+    f_scale = COPY_BYTES / (fetch["copy"] * 1024.0)
+    w_scale = COPY_BYTES / (write["copy"] * 1024.0)
+    out = {"fetch_scale": f_scale, "write_scale": w_scale, "copy_bytes": COPY_BYTES, "kernels": {}}
+    for kind in ("attn", "softmax"):
+        out["kernels"][kind] = {
+            "source_sha": source_hash(kind),
+            "fetch_kib_raw": fetch[kind], "write_kib_raw": write[kind],
+            "fetch_bytes": fetch[kind] * 1024.0 * f_scale,
+            "write_bytes": write[kind] * 1024.0 * w_scale,
+        }
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as fh:
+        fh.write("# HBM traffic per dispatch (rocprofv3 counters)\n\n")
+        fh.write("Commands (run from the repository root on one MI355X):\n\n")
+        fh.write("    rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch -o run -- "
+                 "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline\n")
+        fh.write("    rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write -o run -- "
+                 "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline\n")
+        fh.write("    python3 bench.py --ingest-counters gpurun_out/pmc_fetch gpurun_out/pmc_write\n\n")
+        fh.write("FETCH_SIZE and WRITE_SIZE are KiB per dispatch summed over the TCC "
+                 "channels; each is scaled by the ratio of known bytes to the counter's "
+                 f"reading for a plain {COPY_BYTES >> 20} MiB device copy in the same run "
+                 f"(fetch x{f_scale:.4f}, write x{w_scale:.4f}).\n\n")
+        fh.write("| kernel | source sha | FETCH_SIZE KiB | WRITE_SIZE KiB | read bytes | written bytes |\n")
+        fh.write("|---|---|---|---|---|---|\n")
+        for kind, k in out["kernels"].items():
+            fh.write(f"| {kind} | {k['source_sha']} | {k['fetch_kib_raw']:.0f} | {k['write_kib_raw']:.0f} "
+                     f"| {k['fetch_bytes']:.4g} | {k['write_bytes']:.4g} |\n")
+        fh.write("\n```json\n" + json.dumps(out, indent=1) + "\n```\n")
+    print(json.dumps(out))
+
+
+def ingest_trace(d: str):
+    """Write the per-kernel duration summary of a rocprofv3 --kernel-trace --stats run."""
+    import csv
+    files = glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no kernel_stats.csv under {d}")
+    rows = list(csv.DictReader(open(files[0])))
+    path = os.path.join(ROOT, "profiles", f"kernel_trace_{ATTN_WORKLOAD}+{SOFTMAX_WORKLOAD}.md")
+    with open(path, "w") as fh:
+        fh.write(f"# Kernel durations: {ATTN_WORKLOAD} + {SOFTMAX_WORKLOAD}\n\n")
+        fh.write("Command (run from the repository root on one MI355X):\n\n")
+        fh.write("    rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof_trace "
+                 "-o run -- python3 bench.py --steps 20 --warmup 3 --no-cpu-baseline\n")
+        fh.write("    python3 bench.py --ingest-trace gpurun_out/prof_trace\n\n")
+        fh.write(f"Kernel sources: attention sha {source_hash('attn')}, softmax sha "
+                 f"{source_hash('softmax')}.\n\n")
+        fh.write("| kernel | calls | average (us) | min (us) | max (us) | share |\n|---|---|---|---|---|---|\n")
+        for r in rows:
+            name = r["Name"]
+            short = name if len(name) < 90 else name[:87] + "..."
+            fh.write(f"| `{short}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+                     f"{float(r['Percentage']):.2f}% |\n")
+    print(open(path).read())
+
+
+def load_traffic(kind: str):
+    """Scaled HBM bytes per dispatch of `kind`, or None if absent or stale."""
+    try:
+        text = open(TRAFFIC_FILE).read()
+        blob = json.loads(text.split("```json", 1)[1].split("```", 1)[0])
+        k = blob["kernels"][kind]
+    except (OSError, IndexError, KeyError, ValueError):
+        return None
+    if k.get("source_sha") != source_hash(kind):
+        return None
+    return k["fetch_bytes"] + k["write_bytes"]
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the fp64 oracle on a bounded sample of the attention workload
+# ---------------------------------------------------------------------------
+def cpu_baseline(w, q, k, v, target_s: float = 12.0):
+    import numpy as np
+    import oracle
+    import workloads
+
+    orc = oracle.load()
+    threads = oracle.default_threads()
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+
+    def run(rows_per_head):
+        flops, t0 = 0.0, time.perf_counter()
+        for b, h in heads:
+            rows = workloads.attn_sample_rows(w, b, h, count=rows_per_head)
+            orc.attention_head(q[b, h], k[b, h], v[b, h], w.sm_scale, w.causal, rows,
+                               dtype=w.dtype, threads=threads)
+            vis = (rows + 1) if w.causal else np.full(rows.shape, w.N)
+            flops += float(np.sum(4.0 * vis * w.d))
+        return flops, time.perf_counter() - t0
+
+    rows = 16                             # grow the sample until it costs ~target_s
+    flops, secs = run(rows)
+    while secs < target_s / 3 and rows < 2048:
+        rows = int(min(2048, rows * max(2.0, min(8.0, target_s / max(secs, 1e-3)))))
+        flops, secs = run(rows)
+    return {
+        "value": flops / secs / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+        "sample": f"{rows} seeded query rows in each of the {len(heads)} heads "
+                  f"({flops:.3g} FLOP counted as 4*visible_keys*d per row) in {secs:.1f} s; "
+                  "fp64 three-pass definition, one materialised score row at a time",
+        "extrapolated_full_s": w.flops / (flops / secs),
+    }
+
+
+# ---------------------------------------------------------------------------
+# main benchmark
+# ---------------------------------------------------------------------------
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--ingest-trace", metavar="TRACE_DIR")
+    args = ap.parse_args()
+    if args.ingest_counters:
+        ingest_counters(*args.ingest_counters)
+        return
+    if args.ingest_trace:
+        ingest_trace(args.ingest_trace)
+        return
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path is "
+              "built and measured on a single MI355X", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import online_softmax_04_amd as fa
+    import workloads
+
+    dev = torch.device("cuda:0")
+    w = workloads.ATTN[ATTN_WORKLOAD]
+    sw = workloads.SOFTMAX[SOFTMAX_WORKLOAD]
+    print(f"[bench] generating {w.name} and {sw.name}", file=sys.stderr, flush=True)
+    q, k, v = workloads.attn_full(w, threads=16)
+    x = workloads.softmax_input(sw, threads=16)
+    to = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+    qd, kd, vd = to(q), to(k), to(v)
+    od = torch.empty_like(qd)
+    lsed = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+    xd = torch.from_numpy(x).to(dev)
+    yd = torch.empty_like(xd)
+    cs = torch.randn(COPY_BYTES // 4, device=dev)
+    cd = torch.empty_like(cs)
+    stream = torch.cuda.current_stream()
+    print("[bench] inputs resident; warming up", file=sys.stderr, flush=True)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        fa.fa_fwd(qd, kd, vd, od, lsed, w.B, w.H, w.N, w.d, w.sm_scale, 1, stream)
+        if ev is not None:
+            ev[1].record(stream)
+        fa.online_softmax_rows(xd, yd, sw.rows, sw.cols, stream)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    # probe copy: the known-size kernel that scales the byte counters
+    torch.mul(cs, 1.0, out=cd)
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record(stream)
+    for _ in range(5):
+        torch.mul(cs, 1.0, out=cd)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    copy_ms = c0.elapsed_time(c1) / 5
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    attn_ms = sum(e[0].elapsed_time(e[1]) for e in events) / args.steps
+    sm_ms = sum(e[1].elapsed_time(e[2]) for e in events) / args.steps
+    print(f"[bench] timed {args.steps} steps: attention {attn_ms:.3f} ms, softmax {sm_ms * 1e3:.1f} us",
+          file=sys.stderr, flush=True)
+
+    tflops = w.flops / (attn_ms * 1e-3) / 1e12
+    sm_bytes = sw.algorithmic_bytes
+    sm_gbps = sm_bytes / (sm_ms * 1e-3) / 1e9
+    attrs = fa.kernel_attributes(fa.OP_FA_FWD, w.d, True)
+    sm_attrs = fa.kernel_attributes(fa.OP_SOFTMAX, sw.cols)
+    attn_traffic = load_traffic("attn")
+    sm_traffic = load_traffic("softmax")
+    out = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name} + {sw.name}", "B": w.B, "H": w.H, "N": w.N, "d": w.d,
+                   "causal": True, "softmax_rows": sw.rows, "softmax_cols": sw.cols},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": attn_traffic, "kernel": "attn_fwd_mfma<bf16,128,causal>",
+                     "flop_per_launch": w.flops, "avg_launch_ms": round(attn_ms, 5)},
+        "softmax": {"value": round(sm_gbps, 1), "unit": "GB/s",
+                    "roofline": {"bound": "hbm", "achieved": round(sm_gbps, 1),
+                                 "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                                 "frac": round(sm_gbps / PEAK_HBM_GBPS, 4), "traffic": sm_traffic,
+                                 "kernel": "softmax_cached<512,16>",
+                                 "bytes_per_launch": sm_bytes, "avg_launch_us": round(sm_ms * 1e3, 2)},
+                    "copy_gbps": round(2 * COPY_BYTES / (copy_ms * 1e-3) / 1e9, 1)},
+        "kernel_resources": {"attention": attrs, "softmax": sm_attrs},
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the fp64 oracle on the host", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(w, q, k, v)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -62,6 +62,7 @@ typedef enum {
  *  lse      [B, H, N] fp32, 4-byte aligned, written; may be NULL (not written).
  *  B, H, N  >= 1; B*H*N*d must fit in 63 bits.
  *  d        head dimension: 64 or 128 (else FA_ERR_UNSUPPORTED).
+ *           One head (N*d elements) must span less than 2 GiB (else FA_ERR_UNSUPPORTED).
  *  scale    softmax scale applied to the fp32 dot products (typically 1/sqrt(d));
  *           must be finite and > 0.
  *  causal   0: every query sees all N keys; 1: query i sees keys j <= i.

@@ -35,18 +35,22 @@
 // the sum over keys does not depend on their order.
 //
 // Loader.  K and V tiles are double-buffered in LDS: while tile t is consumed,
-// tile t+1 is fetched into registers with coalesced 16-byte loads and written
-// to the other buffer after the MFMAs; one barrier per tile.  K rows are padded
-// by 16 bytes; V is transposed in registers (4 keys x D/16 dims per thread) and
-// stored as V^T rows padded by 16 bytes.  Rows past N are clamped to N-1 on
-// load and their scores masked to -inf.
+// tile t+1 is fetched into registers and written to the other buffers after
+// the MFMAs of tile t; one barrier per tile.
+//
+// Loader.  Global traffic uses buffer loads whose base is advanced by whole
+// tiles on the scalar unit, so each load needs no vector address arithmetic,
+// and rows past N fall outside the buffer's range and read as zero (their
+// scores are masked).  K rows are padded by 16 bytes in LDS; V is transposed
+// in registers (4 keys x D/16 dims per thread) and stored as V^T rows padded
+// by 16 bytes, 16 lanes per row so the stores do not collide in LDS banks.
 //
 // Causal.  Key tiles wholly after the query block are never visited, tiles
 // wholly before it run without a mask, and only tiles straddling the diagonal
 // (or the ragged end of the sequence) mask element by element ("Online Softmax:
-// Tiling Across a Reduction", causal paragraphs).  A wave whose 32 queries all
-// precede a tile skips its arithmetic for that tile.  Query blocks are handed
-// out longest first.
+// Tiling Across a Reduction", causal paragraphs).  A wave stops computing at
+// the last tile holding a key visible to one of its queries.  Query blocks are
+// handed out longest first.
 #include "common.h"
 #include "kernels.h"
 
@@ -58,6 +62,15 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+
+// Word 3 of a raw buffer resource on gfx9-family parts (32-bit data format,
+// no swizzle): out-of-range loads return zero and out-of-range stores are dropped.
+constexpr int kBufferWord3 = 0x00020000;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  const int n = bytes <= 0 ? 0 : (bytes >= 0x7fffffff ? 0x7fffffff : (int)bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, kBufferWord3);
+}
 
 template <typename T>
 struct Mma;
@@ -95,13 +108,16 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_mfma(
   constexpr int KS = D + 8;            // K tile row stride in LDS (elements)
   constexpr int VS = kBN + 8;          // V^T tile row stride in LDS (elements)
   constexpr int K_ELEMS = kBN * KS;
-  constexpr int STAGE = K_ELEMS + D * VS;
+  constexpr int V_ELEMS = D * VS;
   constexpr int ND = D / 32;           // 32-dim blocks of O^T per wave
   constexpr int NK = D / 16;           // 16-deep MFMA steps of K Q^T
-  constexpr int KCH = kBN * D / 8 / kThreads;  // 16-byte K chunks per thread
+  constexpr int CPR = D / 8;           // 16-byte chunks per K row
+  constexpr int KCH = kBN * CPR / kThreads;  // K rows per thread
   constexpr int VD = D / 16;           // head dims per thread in the V transpose
-  static_assert(KCH >= 1 && VD % 2 == 0, "tile shape");
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * STAGE];
+  constexpr int ROW_BYTES = D * 2;
+  static_assert(KCH >= 1 && VD % 2 == 0 && 4 * ROW_BYTES < 4096, "tile shape");
+  __shared__ __attribute__((aligned(16))) uint16_t kbuf[2 * K_ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t vbuf[2 * V_ELEMS];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -124,17 +140,17 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_mfma(
   const size_t base = (size_t)bh * (size_t)N * D;
   const uint16_t* Kh = K + base;
   const uint16_t* Vh = V + base;
-
   const int qw0 = i0 + wave * 32;  // first query of this wave
   const int qi = qw0 + l32;        // this lane's query
 
   // ---- Q^T fragments: B operand, lane = query, 8 consecutive head dims -------------
   v8 qf[NK];
   {
-    const uint16_t* qp = Q + base + (size_t)min(qi, N - 1) * D + 8 * hf;
+    const auto rq = make_rsrc(Q + base + (size_t)qw0 * D, (int64_t)(N - qw0) * ROW_BYTES);
+    const int off = l32 * ROW_BYTES + 16 * hf;
 #pragma unroll
     for (int kb = 0; kb < NK; ++kb)
-      qf[kb] = __builtin_bit_cast(v8, *reinterpret_cast<const u32x4*>(qp + kb * 16));
+      qf[kb] = __builtin_bit_cast(v8, __builtin_amdgcn_raw_buffer_load_b128(rq, off + 32 * kb, 0, 0));
   }
 
   f32x16 o[ND];
@@ -144,43 +160,50 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_mfma(
 
   const int nk_all = (N + kBN - 1) / kBN;
   const int n_kt = CAUSAL ? min(nk_all, (i0 + kBM - 1) / kBN + 1) : nk_all;
+  // tiles holding a key visible to some query of this wave
+  const int n_kt_w = CAUSAL ? min(n_kt, (qw0 + 31) / kBN + 1) : n_kt;
 
-  // ---- loader: registers <- global (tile t), LDS stage <- registers ----------------
+  // ---- loader: registers <- global (tile t), LDS buffer <- registers ----------------
+  const int krow = (tid / CPR) * KCH;  // K rows krow .. krow+KCH-1 of the tile
+  const int kcol = (tid % CPR) * 8;
+  const int kgoff = krow * ROW_BYTES + kcol * 2;
+  // V: keys 4*va .. 4*va+3 of the tile, head dims vb*VD .. vb*VD+VD-1.  The key
+  // group is the fast index so that 16 consecutive lanes store their 8-byte
+  // V^T pieces into 128 contiguous (permuted) bytes of one V^T row: distinct
+  // banks.  (With the head-dim group fast, the lanes' rows sit 8 rows apart,
+  // a multiple of 128 bytes, and all 16 hit the same banks.)
+  const int va = tid & 15, vb = tid >> 4;
+  const int vgoff = 4 * va * ROW_BYTES + vb * VD * 2;
+  const int vpos = 4 * ((va & ~3) | ((va & 1) << 1) | ((va >> 1) & 1));  // permuted key slot
   u32x4 kreg[KCH];
   unsigned vreg[4][VD / 2];
-  const int va = tid >> 4;  // V: keys 4*va .. 4*va+3 of the tile
-  const int vb = tid & 15;  //    head dims vb*VD .. vb*VD+VD-1
-  const int vpos = 4 * ((va & ~3) | ((va & 1) << 1) | ((va >> 1) & 1));  // permuted key slot
 
-  auto gload = [&](int t) {
-    const int j0 = t * kBN;
+  auto load_k = [&](int t) {
+    const auto r = make_rsrc(Kh + (size_t)t * kBN * D, (int64_t)(N - t * kBN) * ROW_BYTES);
 #pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int ch = tid + i * kThreads;
-      const int row = ch / (D / 8), col = (ch % (D / 8)) * 8;
-      kreg[i] = *reinterpret_cast<const u32x4*>(Kh + (size_t)min(j0 + row, N - 1) * D + col);
-    }
+    for (int i = 0; i < KCH; ++i)
+      kreg[i] = __builtin_amdgcn_raw_buffer_load_b128(r, kgoff + i * ROW_BYTES, 0, 0);
+  };
+  auto store_k = [&](int b) {
+    uint16_t* Ks = kbuf + b * K_ELEMS;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const uint16_t* vp = Vh + (size_t)min(j0 + 4 * va + r, N - 1) * D + vb * VD;
+    for (int i = 0; i < KCH; ++i) *reinterpret_cast<u32x4*>(Ks + (krow + i) * KS + kcol) = kreg[i];
+  };
+  auto load_v = [&](int t) {
+    const auto r = make_rsrc(Vh + (size_t)t * kBN * D, (int64_t)(N - t * kBN) * ROW_BYTES);
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
       if constexpr (VD == 8) {
-        const u32x4 x = *reinterpret_cast<const u32x4*>(vp);
-        vreg[r][0] = x[0]; vreg[r][1] = x[1]; vreg[r][2] = x[2]; vreg[r][3] = x[3];
+        const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(r, vgoff + rr * ROW_BYTES, 0, 0);
+        vreg[rr][0] = x[0]; vreg[rr][1] = x[1]; vreg[rr][2] = x[2]; vreg[rr][3] = x[3];
       } else {
-        const u32x2 x = *reinterpret_cast<const u32x2*>(vp);
-        vreg[r][0] = x[0]; vreg[r][1] = x[1];
+        const u32x2 x = __builtin_amdgcn_raw_buffer_load_b64(r, vgoff + rr * ROW_BYTES, 0, 0);
+        vreg[rr][0] = x[0]; vreg[rr][1] = x[1];
       }
     }
   };
-  auto swrite = [&](int st) {
-    uint16_t* Ks = lds + st * STAGE;
-    uint16_t* Vt = Ks + K_ELEMS;
-#pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int ch = tid + i * kThreads;
-      const int row = ch / (D / 8), col = (ch % (D / 8)) * 8;
-      *reinterpret_cast<u32x4*>(Ks + row * KS + col) = kreg[i];
-    }
+  auto store_v = [&](int b) {
+    uint16_t* Vt = vbuf + b * V_ELEMS;
 #pragma unroll
     for (int cc = 0; cc < VD; ++cc) {
       const int w = cc >> 1;
@@ -195,109 +218,126 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_mfma(
       *reinterpret_cast<u32x2*>(Vt + (vb * VD + cc) * VS + vpos) = u32x2{k01, k23};
     }
   };
+  // S^T = K Q^T for the tile in K buffer b: two 32-key halves
+  auto qk = [&](int b, f32x16 (&s)[2]) {
+    const uint16_t* Ks = kbuf + b * K_ELEMS;
+    s[0] = f32x16{};
+    s[1] = f32x16{};
+#pragma unroll
+    for (int kb = 0; kb < NK; ++kb) {
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh) {
+        const v8 kf = __builtin_bit_cast(
+            v8, *reinterpret_cast<const u32x4*>(Ks + (kh * 32 + l32) * KS + kb * 16 + 8 * hf));
+        s[kh] = Mma<T>::run(kf, qf[kb], s[kh]);
+      }
+    }
+  };
 
-  gload(0);
-  swrite(0);
-  __syncthreads();
-
-  for (int t = 0; t < n_kt; ++t) {
+  // One tile: S = K Q^T, then m, l and O updated with P = 2^(c S - m_new).
+  auto step = [&](int t) {
     const int j0 = t * kBN;
-    if (t + 1 < n_kt) gload(t + 1);
-    const uint16_t* Ks = lds + (t & 1) * STAGE;
-    const uint16_t* Vt = Ks + K_ELEMS;
-
-    if (!CAUSAL || j0 <= qw0 + 31) {  // wave-uniform: some key of the tile is visible
-      // ---- S^T = K Q^T: two 32-key halves ------------------------------------------
-      f32x16 s[2] = {f32x16{}, f32x16{}};
-#pragma unroll
-      for (int kb = 0; kb < NK; ++kb) {
-#pragma unroll
-        for (int kh = 0; kh < 2; ++kh) {
-          const v8 kf = __builtin_bit_cast(
-              v8, *reinterpret_cast<const u32x4*>(Ks + (kh * 32 + l32) * KS + kb * 16 + 8 * hf));
-          s[kh] = Mma<T>::run(kf, qf[kb], s[kh]);
-        }
-      }
-      // ---- mask: keys past N, and keys after the query when causal ------------------
-      if ((j0 + kBN > N) || (CAUSAL && j0 + kBN - 1 > qw0)) {
-#pragma unroll
-        for (int kh = 0; kh < 2; ++kh) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = j0 + 32 * kh + 8 * (r >> 2) + 4 * hf + (r & 3);
-            if (key >= N || (CAUSAL && key > qi)) s[kh][r] = kNegInf;
-          }
-        }
-      }
-      // ---- online softmax: m, l, O rescaled by 2^(m_old - m_new) ---------------------
-      float mx = kNegInf;
-#pragma unroll
-      for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kh][r]);
-      mx = max_halves(mx);
-      const float m_new = fmaxf(m_run, mx * c);
-      const float m_sub = (m_new == kNegInf) ? 0.f : m_new;  // a fully masked row stays empty
-      const float alpha = exp2_fast(m_run - m_sub);
-      float ls = 0.f;
+    f32x16 s[2];
+    qk(t & 1, s);
+    // keys past N, and keys after the query when causal (wave-uniform test)
+    if ((j0 + kBN > N) || (CAUSAL && j0 + kBN - 1 > qw0)) {
 #pragma unroll
       for (int kh = 0; kh < 2; ++kh) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float p = exp2_fast(fmaf(s[kh][r], c, -m_sub));
-          s[kh][r] = p;
-          ls += p;
-        }
-      }
-      l_run = fmaf(l_run, alpha, ls);
-      m_run = m_new;
-      if (__any(alpha != 1.f)) {
-#pragma unroll
-        for (int db = 0; db < ND; ++db) o[db] *= alpha;
-      }
-      // ---- P^T -> 16-bit B operands; O^T += V^T P^T ---------------------------------
-      v8 pf[2][2];
-#pragma unroll
-      for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) pf[kh][kb][e] = (T)s[kh][8 * kb + e];
-#pragma unroll
-      for (int db = 0; db < ND; ++db) {
-#pragma unroll
-        for (int kh = 0; kh < 2; ++kh) {
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb) {
-            const v8 vf = __builtin_bit_cast(
-                v8, *reinterpret_cast<const u32x4*>(Vt + (db * 32 + l32) * VS + 32 * kh +
-                                                    16 * kb + 8 * hf));
-            o[db] = Mma<T>::run(vf, pf[kh][kb], o[db]);
-          }
+          const int key = j0 + 32 * kh + 8 * (r >> 2) + 4 * hf + (r & 3);
+          if (key >= N || (CAUSAL && key > qi)) s[kh][r] = kNegInf;
         }
       }
     }
-    if (t + 1 < n_kt) swrite((t + 1) & 1);
+    // ---- online softmax: m, l, O rescaled by 2^(m_old - m_new) ---------------------
+    float mx = kNegInf;
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kh][r]);
+    mx = max_halves(mx);
+    const float m_new = fmaxf(m_run, mx * c);
+    const float m_sub = (m_new == kNegInf) ? 0.f : m_new;  // a fully masked row stays empty
+    const float alpha = exp2_fast(m_run - m_sub);
+    float ls = 0.f;
+    v8 pf[2][2];  // P^T as 16-bit B operands: [32-key half][16-key step]
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = exp2_fast(fmaf(s[kh][r], c, -m_sub));
+        ls += p;
+        pf[kh][r >> 3][r & 7] = (T)p;
+      }
+    }
+    l_run = fmaf(l_run, alpha, ls);
+    m_run = m_new;
+    if (__any(alpha != 1.f)) {  // wave-uniform; skipped while no row's max moves
+#pragma unroll
+      for (int db = 0; db < ND; ++db) o[db] *= alpha;
+    }
+    // ---- O^T += V^T P^T ---------------------------------------------------------------
+    const uint16_t* Vt = vbuf + (t & 1) * V_ELEMS;
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int db = 0; db < ND; ++db) {  // ND independent accumulators in flight
+          const v8 vf = __builtin_bit_cast(
+              v8, *reinterpret_cast<const u32x4*>(Vt + (db * 32 + l32) * VS + 32 * kh + 16 * kb +
+                                                  8 * hf));
+          o[db] = Mma<T>::run(vf, pf[kh][kb], o[db]);
+        }
+      }
+    }
+  };
+
+  // ---- prologue: tile 0 into LDS --------------------------------------------------------
+  load_k(0);
+  load_v(0);
+  store_k(0);
+  store_v(0);
+  __syncthreads();
+  // Retire the Q loads here.  Left pending, they would make the first MFMA that
+  // reads Q inside the loop wait on the vector-memory counter, which by then
+  // also counts the next tile's prefetch.
+#pragma unroll
+  for (int kb = 0; kb < NK; ++kb) asm volatile("" ::"v"(qf[kb]));
+
+  for (int t = 0; t < n_kt; ++t) {
+    if (t + 1 < n_kt) {  // prefetch tile t+1 into registers while tile t computes
+      load_k(t + 1);
+      load_v(t + 1);
+    }
+    if (t < n_kt_w) step(t);
+    if (t + 1 < n_kt) {  // the other buffers were last read in iteration t-1
+      store_k((t + 1) & 1);
+      store_v((t + 1) & 1);
+    }
     __syncthreads();
   }
 
-  // ---- epilogue: O / l, logsumexp ----------------------------------------------------
+  // ---- epilogue: O / l, logsumexp --------------------------------------------------
   const float l_tot = sum_halves(l_run);
   const float inv = 1.f / l_tot;
-  if (qi < N) {
-    uint16_t* op = O + base + (size_t)qi * D;
+  {
+    // rows past N fall outside the buffer and are dropped
+    const auto ro = make_rsrc(O + base + (size_t)qw0 * D, (int64_t)(N - qw0) * ROW_BYTES);
+    const int off = l32 * ROW_BYTES + 8 * hf;
 #pragma unroll
     for (int db = 0; db < ND; ++db) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int d0 = db * 32 + 8 * g + 4 * hf;
-        *reinterpret_cast<u32x2*>(op + d0) =
-            u32x2{pack2<T>(o[db][4 * g] * inv, o[db][4 * g + 1] * inv),
-                  pack2<T>(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv)};
+        const u32x2 w = u32x2{pack2<T>(o[db][4 * g] * inv, o[db][4 * g + 1] * inv),
+                              pack2<T>(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv)};
+        __builtin_amdgcn_raw_buffer_store_b64(w, ro, off + (db * 32 + 8 * g) * 2, 0, 0);
       }
     }
-    if (LSE != nullptr && hf == 0) LSE[(size_t)bh * N + qi] = (m_run + log2f(l_tot)) * kLn2;
   }
+  if (LSE != nullptr && hf == 0 && qi < N)
+    LSE[(size_t)bh * N + qi] = (m_run + log2f(l_tot)) * kLn2;
 }
 
 // ------------------------------------------------------------------------------------

@@ -5,7 +5,7 @@
 #include <cmath>
 #include <cstdint>
 
-#include "../../include/fa.h"
+#include "fa.h"
 #include "kernels.h"
 
 namespace {
@@ -36,6 +36,8 @@ int attn_entry(osm::Elem elem, const void* q, const void* k, const void* v, void
   const uint64_t lse_bytes = tensor_bytes(B, H, N, 1, 4);
   if (bytes == 0 || lse_bytes == 0) return FA_ERR_INVALID_ARG;
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  // one head's tensor is addressed with 32-bit byte offsets
+  if ((uint64_t)N * (uint64_t)d * esz >= ((uint64_t)1 << 31)) return FA_ERR_UNSUPPORTED;
   // one workgroup per (batch*head, query block) must fit a 1-D grid
   const uint64_t rows_per_block = 128;
   const uint64_t blocks = (uint64_t)B * (uint64_t)H * (((uint64_t)N + rows_per_block - 1) / rows_per_block);
