@@ -14,8 +14,12 @@
 // c = scale * log2(e) folded into one FMA per score, so m is kept in units of
 // c * score; the logsumexp written out is ln 2 * (m + log2 l).
 //
-// Work decomposition.  A workgroup of 4 waves owns 128 consecutive queries of
-// one (batch, head); each wave owns 32 of them.  Key tiles are 64 keys.
+// Work decomposition.  A workgroup of 8 waves owns 256 consecutive queries of
+// one (batch, head); each wave owns 32 of them, and all 8 share each K/V tile
+// staged in LDS.  Key tiles are 64 keys.  The waves form two groups of four
+// that run half a tile apart (slot schedule in the kernel): in every phase one
+// wave per SIMD issues MFMAs while the other runs the softmax on the vector
+// ALU, so the matrix unit is not left idle during the softmax.
 //
 // Orientation.  The score tile is computed transposed, S^T = K Q^T, with K from
 // LDS as the A operand and the wave's Q^T held in VGPRs for the whole loop as
@@ -34,16 +38,14 @@
 // (within each 16-key group, bits 2 and 3 of the key index are swapped), since
 // the sum over keys does not depend on their order.
 //
-// Loader.  K and V tiles are double-buffered in LDS: while tile t is consumed,
-// tile t+1 is fetched into registers and written to the other buffers after
-// the MFMAs of tile t; one barrier per tile.
-//
 // Loader.  Global traffic uses buffer loads whose base is advanced by whole
 // tiles on the scalar unit, so each load needs no vector address arithmetic,
 // and rows past N fall outside the buffer's range and read as zero (their
-// scores are masked).  K rows are padded by 16 bytes in LDS; V is transposed
-// in registers (4 keys x D/16 dims per thread) and stored as V^T rows padded
-// by 16 bytes, 16 lanes per row so the stores do not collide in LDS banks.
+// scores are masked).  K and V have separate double buffers in LDS, filled from
+// registers two slots after the loads are issued.  K rows are padded by 16
+// bytes; V is transposed in registers (4 keys x D/32 dims per thread) and
+// stored as V^T rows padded by 16 bytes, 16 lanes per row so the stores do not
+// collide in LDS banks.
 //
 // Causal.  Key tiles wholly after the query block are never visited, tiles
 // wholly before it run without a mask, and only tiles straddling the diagonal
@@ -95,33 +97,59 @@ __device__ __forceinline__ unsigned pack2(float a, float b) {
          ((unsigned)__builtin_bit_cast(unsigned short, (T)b) << 16);
 }
 
-constexpr int kBM = 128;  // queries per workgroup
-constexpr int kBN = 64;   // keys per tile
-constexpr int kThreads = 256;
+constexpr int kBM = 256;       // queries per workgroup
+constexpr int kBN = 64;        // keys per tile
+constexpr int kThreads = 512;  // 8 waves: two groups of 4, one wave of each group per SIMD
+
+// 16-byte chunk swizzles of the K and V tiles in LDS (rows of D bf16/fp16
+// values, unpadded): physical chunk = logical chunk ^ swizzle(row).  They make
+// the MFMA operand reads conflict-free on gfx950's LDS: K is read as 16-byte
+// pieces of 32 consecutive rows at one chunk position, V through transposed
+// 8-byte reads of 4 consecutive rows x 32 bytes per 16 lanes.
+template <int D>
+__device__ __forceinline__ int kswz(int row) {
+  return D == 128 ? (row & 15) : ((row >> 1) & 7);
+}
+template <int D>
+__device__ __forceinline__ int vswz(int row) {
+  return D == 128 ? 4 * (row & 3) : 4 * ((row >> 1) & 1);
+}
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+
+// One wave-wide buffer load straight into LDS: lane i's 16 bytes (at byte
+// offset voff of the buffer) land at lds + 16 i.  Kept out of the kernel
+// templates: used in a template body, this builtin makes the host pass drop
+// the kernel's launch stub.
+__device__ __forceinline__ void load16_to_lds(__amdgpu_buffer_rsrc_t r, unsigned char* lds, int voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, voff, 0, 0, 0);
+}
 
 template <typename T, int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 2) void attn_fwd_mfma(
+__global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE, int BH,
     int N, int n_mtiles, float c, int xcd_groups) {
   using v8 = typename Mma<T>::v8;
-  constexpr int KS = D + 8;            // K tile row stride in LDS (elements)
-  constexpr int VS = kBN + 8;          // V^T tile row stride in LDS (elements)
-  constexpr int K_ELEMS = kBN * KS;
-  constexpr int V_ELEMS = D * VS;
-  constexpr int ND = D / 32;           // 32-dim blocks of O^T per wave
-  constexpr int NK = D / 16;           // 16-deep MFMA steps of K Q^T
-  constexpr int CPR = D / 8;           // 16-byte chunks per K row
-  constexpr int KCH = kBN * CPR / kThreads;  // K rows per thread
-  constexpr int VD = D / 16;           // head dims per thread in the V transpose
   constexpr int ROW_BYTES = D * 2;
-  static_assert(KCH >= 1 && VD % 2 == 0 && 4 * ROW_BYTES < 4096, "tile shape");
-  __shared__ __attribute__((aligned(16))) uint16_t kbuf[2 * K_ELEMS];
-  __shared__ __attribute__((aligned(16))) uint16_t vbuf[2 * V_ELEMS];
+  constexpr int TILE_BYTES = kBN * ROW_BYTES;  // one K or V tile
+  constexpr int ND = D / 32;                   // 32-dim blocks of O^T per wave
+  constexpr int NK = D / 16;                   // 16-deep MFMA steps of K Q^T
+  constexpr int CPR = D / 8;                   // 16-byte chunks per row
+  constexpr int RPI = 1024 / ROW_BYTES;        // rows per 1 KiB wave-wide load
+  constexpr int NI = TILE_BYTES / 1024 / 8;    // such loads per wave per tile
+  static_assert(NI >= 1, "tile shape");
+  __shared__ __attribute__((aligned(1024))) unsigned char kbuf[2 * TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) unsigned char vbuf[2 * TILE_BYTES];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hf = lane >> 5;
+  // Waves w and w + 4 share a SIMD; they belong to different groups, which run
+  // half a tile apart (see the slot schedule below).
+  const int group = wave >> 2;
 
   // ---- which (batch*head, query block) this workgroup owns ---------------------
   int id = blockIdx.x, bh, mt;
@@ -140,13 +168,18 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_mfma(
   const size_t base = (size_t)bh * (size_t)N * D;
   const uint16_t* Kh = K + base;
   const uint16_t* Vh = V + base;
-  const int qw0 = i0 + wave * 32;  // first query of this wave
-  const int qi = qw0 + l32;        // this lane's query
+  // 32-query blocks of the workgroup interleave between the groups, so both
+  // groups reach the causal diagonal at nearly the same key tile
+  const int qw0 = i0 + 32 * (2 * (wave & 3) + group);  // first query of this wave
+  const int qi = qw0 + l32;                             // this lane's query
+  // qw0 is uniform across the wave; the buffer descriptors built from it must
+  // be scalar, or every access through them becomes a per-lane loop
+  const int qw0_s = __builtin_amdgcn_readfirstlane(qw0);
 
   // ---- Q^T fragments: B operand, lane = query, 8 consecutive head dims -------------
   v8 qf[NK];
   {
-    const auto rq = make_rsrc(Q + base + (size_t)qw0 * D, (int64_t)(N - qw0) * ROW_BYTES);
+    const auto rq = make_rsrc(Q + base + (size_t)qw0_s * D, (int64_t)(N - qw0_s) * ROW_BYTES);
     const int off = l32 * ROW_BYTES + 16 * hf;
 #pragma unroll
     for (int kb = 0; kb < NK; ++kb)
@@ -156,71 +189,75 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_mfma(
   f32x16 o[ND];
 #pragma unroll
   for (int db = 0; db < ND; ++db) o[db] = f32x16{};
+  f32x16 s[2] = {f32x16{}, f32x16{}};
+  v8 pf[2][2];  // P^T as 16-bit B operands: [32-key half][16-key step]
   float m_run = kNegInf, l_run = 0.f;
 
   const int nk_all = (N + kBN - 1) / kBN;
   const int n_kt = CAUSAL ? min(nk_all, (i0 + kBM - 1) / kBN + 1) : nk_all;
   // tiles holding a key visible to some query of this wave
-  const int n_kt_w = CAUSAL ? min(n_kt, (qw0 + 31) / kBN + 1) : n_kt;
+  int n_w = CAUSAL ? min(n_kt, (qw0 + 31) / kBN + 1) : n_kt;
+  // Without the causal limit the compiler would prove n_w == n_kt, drop the
+  // per-wave tests and merge the slots into blocks it schedules with more
+  // values live than fit in registers; keep the tests in place.
+  asm volatile("" : "+v"(n_w));
 
-  // ---- loader: registers <- global (tile t), LDS buffer <- registers ----------------
-  const int krow = (tid / CPR) * KCH;  // K rows krow .. krow+KCH-1 of the tile
-  const int kcol = (tid % CPR) * 8;
-  const int kgoff = krow * ROW_BYTES + kcol * 2;
-  // V: keys 4*va .. 4*va+3 of the tile, head dims vb*VD .. vb*VD+VD-1.  The key
-  // group is the fast index so that 16 consecutive lanes store their 8-byte
-  // V^T pieces into 128 contiguous (permuted) bytes of one V^T row: distinct
-  // banks.  (With the head-dim group fast, the lanes' rows sit 8 rows apart,
-  // a multiple of 128 bytes, and all 16 hit the same banks.)
-  const int va = tid & 15, vb = tid >> 4;
-  const int vgoff = 4 * va * ROW_BYTES + vb * VD * 2;
-  const int vpos = 4 * ((va & ~3) | ((va & 1) << 1) | ((va >> 1) & 1));  // permuted key slot
-  u32x4 kreg[KCH];
-  unsigned vreg[4][VD / 2];
-
+  // ---- loader: global -> LDS directly, no registers ------------------------------------
+  // A wave-wide 16-byte-per-lane buffer load with the LDS flag writes lane i's
+  // 16 bytes at (LDS base + 16 i): each of the wave's NI loads fills RPI whole
+  // rows, and each lane fetches the global chunk that its LDS slot holds under
+  // the swizzle.  Rows past N fall outside the buffer and land as zeros.
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+  int kgoff[NI], vgoff[NI];
+#pragma unroll
+  for (int j = 0; j < NI; ++j) {
+    const int row = (wave * NI + j) * RPI + lane / CPR;
+    const int p = lane % CPR;
+    kgoff[j] = row * ROW_BYTES + (p ^ kswz<D>(row)) * 16;
+    vgoff[j] = row * ROW_BYTES + (p ^ vswz<D>(row)) * 16;
+  }
   auto load_k = [&](int t) {
     const auto r = make_rsrc(Kh + (size_t)t * kBN * D, (int64_t)(N - t * kBN) * ROW_BYTES);
 #pragma unroll
-    for (int i = 0; i < KCH; ++i)
-      kreg[i] = __builtin_amdgcn_raw_buffer_load_b128(r, kgoff + i * ROW_BYTES, 0, 0);
-  };
-  auto store_k = [&](int b) {
-    uint16_t* Ks = kbuf + b * K_ELEMS;
-#pragma unroll
-    for (int i = 0; i < KCH; ++i) *reinterpret_cast<u32x4*>(Ks + (krow + i) * KS + kcol) = kreg[i];
+    for (int j = 0; j < NI; ++j)
+      load16_to_lds(r, kbuf + (t & 1) * TILE_BYTES + (wave_s * NI + j) * 1024, kgoff[j]);
   };
   auto load_v = [&](int t) {
     const auto r = make_rsrc(Vh + (size_t)t * kBN * D, (int64_t)(N - t * kBN) * ROW_BYTES);
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      if constexpr (VD == 8) {
-        const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(r, vgoff + rr * ROW_BYTES, 0, 0);
-        vreg[rr][0] = x[0]; vreg[rr][1] = x[1]; vreg[rr][2] = x[2]; vreg[rr][3] = x[3];
-      } else {
-        const u32x2 x = __builtin_amdgcn_raw_buffer_load_b64(r, vgoff + rr * ROW_BYTES, 0, 0);
-        vreg[rr][0] = x[0]; vreg[rr][1] = x[1];
-      }
-    }
+    for (int j = 0; j < NI; ++j)
+      load16_to_lds(r, vbuf + (t & 1) * TILE_BYTES + (wave_s * NI + j) * 1024, vgoff[j]);
   };
-  auto store_v = [&](int b) {
-    uint16_t* Vt = vbuf + b * V_ELEMS;
+  // direct loads write LDS behind the compiler's back: wait for them explicitly
+  auto loads_landed = [&]() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
+
+  // ---- operand read offsets -------------------------------------------------------------
+  // K (A operand of S^T = K Q^T): row l32 (+32 for the second key half), logical
+  // chunk 2 kb + hf.  Rows 32 apart share a swizzle.
+  int kroff[NK];
 #pragma unroll
-    for (int cc = 0; cc < VD; ++cc) {
-      const int w = cc >> 1;
-      unsigned k01, k23;  // keys (4va, 4va+1) and (4va+2, 4va+3) of head dim vb*VD+cc
-      if ((cc & 1) == 0) {
-        k01 = (vreg[0][w] & 0xffffu) | (vreg[1][w] << 16);
-        k23 = (vreg[2][w] & 0xffffu) | (vreg[3][w] << 16);
-      } else {
-        k01 = (vreg[0][w] >> 16) | (vreg[1][w] & 0xffff0000u);
-        k23 = (vreg[2][w] >> 16) | (vreg[3][w] & 0xffff0000u);
-      }
-      *reinterpret_cast<u32x2*>(Vt + (vb * VD + cc) * VS + vpos) = u32x2{k01, k23};
-    }
-  };
-  // S^T = K Q^T for the tile in K buffer b: two 32-key halves
-  auto qk = [&](int b, f32x16 (&s)[2]) {
-    const uint16_t* Ks = kbuf + b * K_ELEMS;
+  for (int kb = 0; kb < NK; ++kb) kroff[kb] = l32 * ROW_BYTES + ((2 * kb + hf) ^ kswz<D>(l32)) * 16;
+  // V^T (A operand of O^T = V^T P^T) through ds_read_b64_tr_b16: within each
+  // group of 16 lanes, the lane at position q supplies the address of row
+  // R + q/4, head dims C + 4 (q % 4) .. +3, and receives V[R + k][C + q] for
+  // k = 0..3.  With R = 32 kh + 16 kb + 4 hf and C = 32 db + 16 ((lane >> 4) & 1)
+  // the lane gets its head dim (32 db + lane % 32) at the keys of B-operand
+  // positions 8 hf .. 8 hf + 3; a second read 8 rows further gives 8 hf + 4 ..
+  // 8 hf + 7 (the P^T key permutation).  Row steps of 4 keep the swizzle.
+  int vroff[ND];
+  {
+    const int q = lane & 15;
+    const int row = 4 * hf + (q >> 2);
+    const int col = 16 * ((lane >> 4) & 1) + 4 * (q & 3);
+#pragma unroll
+    for (int db = 0; db < ND; ++db)
+      vroff[db] = row * ROW_BYTES + (((col + 32 * db) >> 3) ^ vswz<D>(row)) * 16 + (col & 7) * 2;
+  }
+
+  // ---- the three pieces of a tile --------------------------------------------------------
+  // QK(t): S^T = K(t) Q^T, two 32-key halves, from K buffer t % 2.
+  auto qk = [&](int t) {
+    const unsigned char* Kt = kbuf + (t & 1) * TILE_BYTES;
     s[0] = f32x16{};
     s[1] = f32x16{};
 #pragma unroll
@@ -228,17 +265,15 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_mfma(
 #pragma unroll
       for (int kh = 0; kh < 2; ++kh) {
         const v8 kf = __builtin_bit_cast(
-            v8, *reinterpret_cast<const u32x4*>(Ks + (kh * 32 + l32) * KS + kb * 16 + 8 * hf));
+            v8, *reinterpret_cast<const u32x4*>(Kt + kroff[kb] + kh * 32 * ROW_BYTES));
         s[kh] = Mma<T>::run(kf, qf[kb], s[kh]);
       }
     }
   };
-
-  // One tile: S = K Q^T, then m, l and O updated with P = 2^(c S - m_new).
-  auto step = [&](int t) {
+  // SM(t): online softmax of S(t): m, l and O rescaled by 2^(m_old - m_new),
+  // P = 2^(c S - m_new) packed to 16 bits.
+  auto sm = [&](int t) {
     const int j0 = t * kBN;
-    f32x16 s[2];
-    qk(t & 1, s);
     // keys past N, and keys after the query when causal (wave-uniform test)
     if ((j0 + kBN > N) || (CAUSAL && j0 + kBN - 1 > qw0)) {
 #pragma unroll
@@ -250,7 +285,6 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_mfma(
         }
       }
     }
-    // ---- online softmax: m, l, O rescaled by 2^(m_old - m_new) ---------------------
     float mx = kNegInf;
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh)
@@ -261,7 +295,6 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_mfma(
     const float m_sub = (m_new == kNegInf) ? 0.f : m_new;  // a fully masked row stays empty
     const float alpha = exp2_fast(m_run - m_sub);
     float ls = 0.f;
-    v8 pf[2][2];  // P^T as 16-bit B operands: [32-key half][16-key step]
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh) {
 #pragma unroll
@@ -277,54 +310,111 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_mfma(
 #pragma unroll
       for (int db = 0; db < ND; ++db) o[db] *= alpha;
     }
-    // ---- O^T += V^T P^T ---------------------------------------------------------------
-    const uint16_t* Vt = vbuf + (t & 1) * V_ELEMS;
+  };
+  // PV(t): O^T += V^T(t) P^T(t), from V buffer t % 2.
+  auto pv = [&](int t) {
+    const unsigned char* Vt = vbuf + (t & 1) * TILE_BYTES;
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
         for (int db = 0; db < ND; ++db) {  // ND independent accumulators in flight
-          const v8 vf = __builtin_bit_cast(
-              v8, *reinterpret_cast<const u32x4*>(Vt + (db * 32 + l32) * VS + 32 * kh + 16 * kb +
-                                                  8 * hf));
+          const unsigned char* pa = Vt + vroff[db] + (32 * kh + 16 * kb) * ROW_BYTES;
+          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)pa);
+          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(pa + 8 * ROW_BYTES));
+          const v8 vf = __builtin_bit_cast(v8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
           o[db] = Mma<T>::run(vf, pf[kh][kb], o[db]);
         }
       }
     }
   };
 
-  // ---- prologue: tile 0 into LDS --------------------------------------------------------
+  // PV(tp) then QK(tq) in one block, with the LDS operand reads running a fixed
+  // distance ahead of the MFMAs that consume them: enough reads in flight to
+  // cover LDS latency, few enough registers to avoid spilling.
+  auto pv_qk = [&](int tp, int tq) {
+    pv(tp);
+    qk(tq);
+    // PV MFMAs take two transposed reads each, QK MFMAs one read
+    constexpr int kAhead = 4;               // MFMAs whose operands are read ahead
+    constexpr int kPv = 4 * ND, kQk = 2 * NK;
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * kAhead, 0);  // DS reads
+#pragma unroll
+    for (int i = 0; i < kPv + kQk; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+      const int j = i + kAhead;                           // operand reads for MFMA j
+      if (j < kPv) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      else if (j < kPv + kQk) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+  };
+
+  // ---- slot schedule ----------------------------------------------------------------
+  // Each tile t takes two slots separated by workgroup barriers:
+  //   slot X(t): group 0 runs SM(t)          group 1 runs PV(t-1), QK(t)
+  //   slot Y(t): group 0 runs PV(t), QK(t+1) group 1 runs SM(t)
+  // so on every SIMD one wave keeps the matrix unit busy while the other runs
+  // the vector-ALU softmax.  K(t+1) and V(t) are read from Y(t) to X(t+1); they
+  // are loaded into LDS during Y(t-1) and X(t) (into the buffers of K(t-1) and
+  // V(t-1), last read in X(t-1)) and published by the barrier that ends X(t).
   load_k(0);
-  load_v(0);
-  store_k(0);
-  store_v(0);
+  loads_landed();
   __syncthreads();
   // Retire the Q loads here.  Left pending, they would make the first MFMA that
-  // reads Q inside the loop wait on the vector-memory counter, which by then
-  // also counts the next tile's prefetch.
+  // reads Q wait on the vector-memory counter, which then also counts the tile
+  // loads in flight.
 #pragma unroll
   for (int kb = 0; kb < NK; ++kb) asm volatile("" ::"v"(qf[kb]));
-
+  // slot Y(-1): load K(1), V(0); group 0 computes S(0)
+  if (n_kt > 1) load_k(1);
+  load_v(0);
+  if (group == 0) {
+    __builtin_amdgcn_s_setprio(1);
+    qk(0);
+    __builtin_amdgcn_s_setprio(0);
+  }
+  __syncthreads();
   for (int t = 0; t < n_kt; ++t) {
-    if (t + 1 < n_kt) {  // prefetch tile t+1 into registers while tile t computes
-      load_k(t + 1);
-      load_v(t + 1);
+    // ---- slot X(t)
+    if (group == 0) {
+      if (t < n_w) sm(t);
+    } else {
+      __builtin_amdgcn_s_setprio(1);
+      if (t >= 1 && t < n_w) {
+        pv_qk(t - 1, t);
+      } else {
+        if (t >= 1 && t - 1 < n_w) pv(t - 1);
+        if (t < n_w) qk(t);
+      }
+      __builtin_amdgcn_s_setprio(0);
     }
-    if (t < n_kt_w) step(t);
-    if (t + 1 < n_kt) {  // the other buffers were last read in iteration t-1
-      store_k((t + 1) & 1);
-      store_v((t + 1) & 1);
+    loads_landed();  // K(t+1), V(t)
+    __syncthreads();
+    // ---- slot Y(t)
+    if (t + 2 < n_kt) load_k(t + 2);
+    if (t + 1 < n_kt) load_v(t + 1);
+    if (group == 0) {
+      __builtin_amdgcn_s_setprio(1);
+      if (t + 1 < n_w) {
+        pv_qk(t, t + 1);
+      } else if (t < n_w) {
+        pv(t);
+      }
+      __builtin_amdgcn_s_setprio(0);
+    } else {
+      if (t < n_w) sm(t);
     }
     __syncthreads();
   }
+  // slot X(n_kt): group 1 finishes the last PV
+  if (group == 1 && n_kt - 1 < n_w) pv(n_kt - 1);
 
   // ---- epilogue: O / l, logsumexp --------------------------------------------------
   const float l_tot = sum_halves(l_run);
   const float inv = 1.f / l_tot;
   {
     // rows past N fall outside the buffer and are dropped
-    const auto ro = make_rsrc(O + base + (size_t)qw0 * D, (int64_t)(N - qw0) * ROW_BYTES);
+    const auto ro = make_rsrc(O + base + (size_t)qw0_s * D, (int64_t)(N - qw0_s) * ROW_BYTES);
     const int off = l32 * ROW_BYTES + 8 * hf;
 #pragma unroll
     for (int db = 0; db < ND; ++db) {
@@ -439,12 +529,13 @@ const void* mfma_fn() {
 }
 
 const void* pick_attn(Elem elem, int d, bool causal, int* threads, int* rows_per_block) {
-  *threads = 256;
   if (elem == Elem::f32) {
+    *threads = 256;
     *rows_per_block = 4 * (64 / (d / 64));
     if (d == 64) return causal ? (const void*)attn_fwd_f32<64, true> : (const void*)attn_fwd_f32<64, false>;
     return causal ? (const void*)attn_fwd_f32<128, true> : (const void*)attn_fwd_f32<128, false>;
   }
+  *threads = kThreads;
   *rows_per_block = kBM;
   if (elem == Elem::bf16) {
     if (d == 64) return causal ? mfma_fn<__bf16, 64, true>() : mfma_fn<__bf16, 64, false>();
