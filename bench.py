@@ -140,27 +140,41 @@ def ingest_counters(dir_fetch: str, dir_write: str):
     print(json.dumps(out))
 
 
-def ingest_trace(d: str):
-    """Write the per-kernel duration summary of a rocprofv3 --kernel-trace --stats run."""
+def ingest_trace(d: str, warmup: int):
+    """Write the per-kernel duration summary of a rocprofv3 --kernel-trace --stats run of the
+    default benchmark.  Besides rocprofv3's own statistics over every call, the summary gives
+    the mean over the timed calls only (each kernel's calls after the first `warmup`), which is
+    what the benchmark's HIP events measure."""
     import csv
-    files = glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)
-    if not files:
-        raise SystemExit(f"no kernel_stats.csv under {d}")
-    rows = list(csv.DictReader(open(files[0])))
+    stats = glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)
+    traces = glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True)
+    if not stats or not traces:
+        raise SystemExit(f"no kernel_stats.csv / kernel_trace.csv under {d}")
+    rows = list(csv.DictReader(open(stats[0])))
+    per_call = {}
+    for r in csv.DictReader(open(traces[0])):
+        per_call.setdefault(r["Kernel_Name"], []).append(
+            (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
     path = os.path.join(ROOT, "profiles", f"kernel_trace_{ATTN_WORKLOAD}+{SOFTMAX_WORKLOAD}.md")
     with open(path, "w") as fh:
         fh.write(f"# Kernel durations: {ATTN_WORKLOAD} + {SOFTMAX_WORKLOAD}\n\n")
         fh.write("Command (run from the repository root on one MI355X):\n\n")
         fh.write("    rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof_trace "
-                 "-o run -- python3 bench.py --steps 20 --warmup 3 --no-cpu-baseline\n")
-        fh.write("    python3 bench.py --ingest-trace gpurun_out/prof_trace\n\n")
+                 "-o run -- python3 bench.py --no-cpu-baseline\n")
+        fh.write(f"    python3 bench.py --ingest-trace gpurun_out/prof_trace --warmup {warmup}\n\n")
         fh.write(f"Kernel sources: attention sha {source_hash('attn')}, softmax sha "
                  f"{source_hash('softmax')}.\n\n")
-        fh.write("| kernel | calls | average (us) | min (us) | max (us) | share |\n|---|---|---|---|---|---|\n")
+        fh.write(f"\"timed mean\" skips each kernel's first {warmup} calls (the benchmark's untimed "
+                 "warm-up steps, while the clock ramps up).\n\n")
+        fh.write("| kernel | calls | timed mean (us) | mean of all calls (us) | min (us) | max (us) | share |\n"
+                 "|---|---|---|---|---|---|---|\n")
         for r in rows:
             name = r["Name"]
             short = name if len(name) < 90 else name[:87] + "..."
-            fh.write(f"| `{short}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+            calls = per_call.get(name, [])
+            timed = calls[warmup:] if len(calls) > warmup else []
+            tm = f"{sum(timed) / len(timed):.2f}" if timed else "-"
+            fh.write(f"| `{short}` | {r['Calls']} | {tm} | {float(r['AverageNs']) / 1e3:.2f} | "
                      f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
                      f"{float(r['Percentage']):.2f}% |\n")
     print(open(path).read())
@@ -182,7 +196,7 @@ def load_traffic(kind: str):
 # ---------------------------------------------------------------------------
 # CPU baseline: the fp64 oracle on a bounded sample of the attention workload
 # ---------------------------------------------------------------------------
-def cpu_baseline(w, q, k, v, target_s: float = 12.0):
+def cpu_baseline(w, q, k, v, target_s: float = 15.0):
     import numpy as np
     import oracle
     import workloads
@@ -201,10 +215,13 @@ def cpu_baseline(w, q, k, v, target_s: float = 12.0):
             flops += float(np.sum(4.0 * vis * w.d))
         return flops, time.perf_counter() - t0
 
-    rows = 16                             # grow the sample until it costs ~target_s
+    rows = 16                             # calibrate on a small sample ...
     flops, secs = run(rows)
-    while secs < target_s / 3 and rows < 2048:
-        rows = int(min(2048, rows * max(2.0, min(8.0, target_s / max(secs, 1e-3)))))
+    while secs < 1.0 and rows < 2048:
+        rows = min(2048, rows * 4)
+        flops, secs = run(rows)
+    if secs < target_s / 2 and rows < 2048:  # ... then time one sample sized to ~target_s
+        rows = int(min(2048, rows * target_s / secs))
         flops, secs = run(rows)
     return {
         "value": flops / secs / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
@@ -222,7 +239,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--ingest-trace", metavar="TRACE_DIR")
@@ -231,7 +248,7 @@ def main():
         ingest_counters(*args.ingest_counters)
         return
     if args.ingest_trace:
-        ingest_trace(args.ingest_trace)
+        ingest_trace(args.ingest_trace, args.warmup)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path is "

@@ -67,6 +67,12 @@ typedef enum {
  *           must be finite and > 0.
  *  causal   0: every query sees all N keys; 1: query i sees keys j <= i.
  *  O is rounded to bfloat16 (nearest even) once, after the division by l.
+ *  Arithmetic: scores and all statistics in fp32; P is rounded to bfloat16
+ *  for the P V product, and l sums that same rounded P, so each output row is
+ *  a convex combination of V rows.  The maximum subtracted before
+ *  exponentiation is a reference that moves to the running row maximum only
+ *  when that has grown by more than a factor 2^8; since O and l carry the
+ *  same factor, O / l and lse do not depend on when it moves.
  */
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            int B, int H, int N, int d, float scale, int causal, hipStream_t stream);

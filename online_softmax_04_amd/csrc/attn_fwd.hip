@@ -12,7 +12,17 @@
 // and O / l once after the last tile.  m starts at -inf, so the first rescale
 // factor is exactly 0 ("Day 97", Solution).  Exponentials run in base 2 with
 // c = scale * log2(e) folded into one FMA per score, so m is kept in units of
-// c * score; the logsumexp written out is ln 2 * (m + log2 l).
+// c * score; the logsumexp written out is ln 2 * (m + log2 l).  The row sum
+// in l is taken over P after its rounding to 16 bits, the same values that
+// multiply V.
+//
+// The m carried here is a reference point that trails the running maximum by
+// at most kSlack = 8 (a factor 2^8): it moves to the new maximum only when
+// that exceeds it by more than kSlack.  Any reference gives the same O / l and
+// m + log2 l, because l and O are scaled by the same 2^(-m); the eager rule
+// above is the case kSlack = 0.  Every exponential stays at or below 2^8, far
+// from fp32 and bf16/fp16 overflow, and the rescale of O (D/2 multiplies per
+// lane) runs only on the rare tiles where some row's reference moves.
 //
 // Work decomposition.  A workgroup of 8 waves owns 256 consecutive queries of
 // one (batch, head); each wave owns 32 of them, and all 8 share each K/V tile
@@ -38,14 +48,14 @@
 // (within each 16-key group, bits 2 and 3 of the key index are swapped), since
 // the sum over keys does not depend on their order.
 //
-// Loader.  Global traffic uses buffer loads whose base is advanced by whole
-// tiles on the scalar unit, so each load needs no vector address arithmetic,
-// and rows past N fall outside the buffer's range and read as zero (their
-// scores are masked).  K and V have separate double buffers in LDS, filled from
-// registers two slots after the loads are issued.  K rows are padded by 16
-// bytes; V is transposed in registers (4 keys x D/32 dims per thread) and
-// stored as V^T rows padded by 16 bytes, 16 lanes per row so the stores do not
-// collide in LDS banks.
+// Loader.  K and V tiles go from global memory straight into LDS with buffer
+// loads that write LDS directly (no register staging), 16 bytes per lane.  The
+// buffer base is advanced by whole tiles on the scalar unit, so a load needs no
+// vector address arithmetic, and rows past N fall outside the buffer's range
+// and read as zero (their scores are masked).  K and V have separate double
+// buffers.  Both are stored row-major with 16-byte chunks XOR-swizzled by row
+// so that the MFMA operand reads spread over the LDS banks; V^T operands are
+// read with the transposing ds_read_b64_tr_b16.
 //
 // Causal.  Key tiles wholly after the query block are never visited, tiles
 // wholly before it run without a mask, and only tiles straddling the diagonal
@@ -91,12 +101,27 @@ struct Mma<_Float16> {
   }
 };
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+// acc + x.lo + x.hi for a word holding two 16-bit values (one dot2 instruction)
+template <typename T>
+__device__ __forceinline__ float add_pair(unsigned x, float acc);
+template <>
+__device__ __forceinline__ float add_pair<__bf16>(unsigned x, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x), __builtin_bit_cast(bf16x2, 0x3f803f80u), acc, false);
+}
+template <>
+__device__ __forceinline__ float add_pair<_Float16>(unsigned x, float acc) {
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, x), __builtin_bit_cast(f16x2, 0x3c003c00u), acc, false);
+}
+
 template <typename T>
 __device__ __forceinline__ unsigned pack2(float a, float b) {
   return (unsigned)__builtin_bit_cast(unsigned short, (T)a) |
          ((unsigned)__builtin_bit_cast(unsigned short, (T)b) << 16);
 }
 
+constexpr float kSlack = 8.f;  // how far (log2 units) the running maximum may pass m
 constexpr int kBM = 256;       // queries per workgroup
 constexpr int kBN = 64;        // keys per tile
 constexpr int kThreads = 512;  // 8 waves: two groups of 4, one wave of each group per SIMD
@@ -271,7 +296,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(
     }
   };
   // SM(t): online softmax of S(t): m, l and O rescaled by 2^(m_old - m_new),
-  // P = 2^(c S - m_new) packed to 16 bits.
+  // P = 2^(c S - m_new) packed to 16 bits, with m the trailing reference.
   auto sm = [&](int t) {
     const int j0 = t * kBN;
     // keys past N, and keys after the query when causal (wave-uniform test)
@@ -291,22 +316,30 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kh][r]);
     mx = max_halves(mx);
-    const float m_new = fmaxf(m_run, mx * c);
+    const float m_cand = fmaxf(m_run, mx * c);
+    const float m_new = (m_cand > m_run + kSlack) ? m_cand : m_run;  // -inf moves to any finite max
     const float m_sub = (m_new == kNegInf) ? 0.f : m_new;  // a fully masked row stays empty
     const float alpha = exp2_fast(m_run - m_sub);
-    float ls = 0.f;
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = exp2_fast(fmaf(s[kh][r], c, -m_sub));
-        ls += p;
-        pf[kh][r >> 3][r & 7] = (T)p;
-      }
+      for (int r = 0; r < 16; ++r) pf[kh][r >> 3][r & 7] = (T)exp2_fast(fmaf(s[kh][r], c, -m_sub));
     }
-    l_run = fmaf(l_run, alpha, ls);
+    // l sums the 16-bit P that the PV product consumes, so O / l weights V
+    // by exactly the rounded P normalised to 1: a rounding error d of one weight
+    // then moves O by d p (v - O) / l, not by d p v / l.
+    float ls[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const u32x4 w = __builtin_bit_cast(u32x4, pf[kh][kb]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ls[e] = add_pair<T>(w[e], ls[e]);
+      }
+    l_run = fmaf(l_run, alpha, (ls[0] + ls[1]) + (ls[2] + ls[3]));
     m_run = m_new;
-    if (__any(alpha != 1.f)) {  // wave-uniform; skipped while no row's max moves
+    if (__any(alpha != 1.f)) {  // wave-uniform; skipped while no row's reference moves
 #pragma unroll
       for (int db = 0; db < ND; ++db) o[db] *= alpha;
     }
@@ -350,13 +383,16 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(
   };
 
   // ---- slot schedule ----------------------------------------------------------------
-  // Each tile t takes two slots separated by workgroup barriers:
+  // Each tile t takes two slots:
   //   slot X(t): group 0 runs SM(t)          group 1 runs PV(t-1), QK(t)
   //   slot Y(t): group 0 runs PV(t), QK(t+1) group 1 runs SM(t)
   // so on every SIMD one wave keeps the matrix unit busy while the other runs
   // the vector-ALU softmax.  K(t+1) and V(t) are read from Y(t) to X(t+1); they
   // are loaded into LDS during Y(t-1) and X(t) (into the buffers of K(t-1) and
-  // V(t-1), last read in X(t-1)) and published by the barrier that ends X(t).
+  // V(t-1), last read in X(t-1)) and published by the workgroup barrier that
+  // ends X(t).  That barrier is the only one per tile: no LDS buffer changes
+  // hands between Y(t) and X(t+1), and meeting once per tile keeps the two
+  // groups in opposite phases.
   load_k(0);
   loads_landed();
   __syncthreads();
@@ -404,7 +440,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(
     } else {
       if (t < n_w) sm(t);
     }
-    __syncthreads();
   }
   // slot X(n_kt): group 1 finishes the last PV
   if (group == 1 && n_kt - 1 < n_w) pv(n_kt - 1);

@@ -127,6 +127,31 @@ def test_large_scores_force_rescales(orc, dtype, causal):
                          causal, o, lse, max_abs=2.5e-2)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("step", [0.5, 3.0, 7.9, 8.1, 30.0])
+def test_rising_scores(orc, dtype, causal, step):
+    """Scores that climb by about `step` (in log2 units, c * score) per 64-key
+    tile, so the running maximum keeps moving by a controlled amount: below
+    the kernel's 2^8 slack (its reference maximum lags and O is not rescaled),
+    right at it, and far above it (rescaled on every tile).  Row i climbs at
+    rate (1 + u_i / 2), u_i uniform, on top of N(0, 1) noise in the other head
+    dims.  Late rows are peaked, so the element gate is the large-score bound
+    2.5e-2; the relative L2 gate stays 5e-3."""
+    B, H, N, d = 1, 2, 1024, 128
+    say(f"[attention rising scores] dtype={dtype} causal={causal} step={step}")
+    scale = 1.0 / np.sqrt(d)
+    q, k, v = workloads.random_attn(B, H, N, d, "f32", seed=int(step * 10) + 3)
+    rng = np.random.default_rng([17, int(step * 10)])
+    rate = np.float32(step / (64 * scale * np.log2(np.e)))
+    q[..., 0] = np.float32(1.0) + np.float32(0.5) * rng.random((B, H, N), dtype=np.float32)
+    k[..., 0] = rate * np.arange(N, dtype=np.float32)[None, None, :]
+    q, k, v = (workloads.cast(t, dtype) for t in (q, k, v))
+    o, lse = run_gpu(q, k, v, dtype, scale, causal)
+    check_against_oracle(orc, f"rising {dtype} c{int(causal)} step{step}", q, k, v, dtype, scale,
+                         causal, o, lse, max_abs=2.5e-2)
+
+
 def test_lse_optional(orc):
     q, k, v = workloads.random_attn(1, 2, 200, 64, "bf16", seed=5)
     say("[attention lse=NULL]")
