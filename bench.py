@@ -215,13 +215,13 @@ def cpu_baseline(w, q, k, v, target_s: float = 15.0):
             flops += float(np.sum(4.0 * vis * w.d))
         return flops, time.perf_counter() - t0
 
-    rows = 16                             # calibrate on a small sample ...
+    # Grow the sample until one timing costs at least 2/3 of target_s.  Each step aims at
+    # target_s by linear extrapolation; a per-head fixed cost makes small samples look slow,
+    # so the extrapolation undershoots and the loop repeats.
+    rows = 16
     flops, secs = run(rows)
-    while secs < 1.0 and rows < 2048:
-        rows = min(2048, rows * 4)
-        flops, secs = run(rows)
-    if secs < target_s / 2 and rows < 2048:  # ... then time one sample sized to ~target_s
-        rows = int(min(2048, rows * target_s / secs))
+    while secs < target_s * 2 / 3 and rows < 2048:
+        rows = int(min(2048, rows * min(8.0, max(1.5, target_s / max(secs, 1e-3)))))
         flops, secs = run(rows)
     return {
         "value": flops / secs / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
