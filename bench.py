@@ -140,6 +140,105 @@ def ingest_counters(dir_fetch: str, dir_write: str):
     print(json.dumps(out))
 
 
+MFMA_FILE = os.path.join(ROOT, "profiles", f"mfma_{ATTN_WORKLOAD}.md")
+MFMA_PASS_A = "SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES GRBM_GUI_ACTIVE"
+MFMA_PASS_B = ("SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE "
+               "SQ_INSTS_VMEM SQ_INSTS_SALU SQ_INSTS_VALU_TRANS_F32")
+
+
+def kernel_mfma_count(w) -> int:
+    """32x32x16 MFMAs one attn_fwd_mfma launch issues on workload w: every wave runs QK and
+    PV (D/16 + D/16 MFMAs per 32-key block, two blocks per 64-key tile) on each key tile up
+    to the last one holding a key visible to one of its 32 queries."""
+    bm, bn = 256, 64
+    per_tile = 2 * (w.d // 16) * 2
+    n_mt = -(-w.N // bm)
+    nk_all = -(-w.N // bn)
+    total = 0
+    for mt in range(n_mt):
+        i0 = mt * bm
+        n_kt = min(nk_all, (i0 + bm - 1) // bn + 1) if w.causal else nk_all
+        for wave in range(8):
+            qw0 = i0 + 32 * (2 * (wave & 3) + (wave >> 2))
+            n_w = min(n_kt, (qw0 + 31) // bn + 1) if w.causal else n_kt
+            total += n_w * per_tile
+    return total * w.B * w.H
+
+
+def ingest_mfma(dir_a: str, dir_b: str):
+    """Write the MFMA-utilisation summary of the attention kernel from two rocprofv3 --pmc
+    passes of the benchmark (MFMA_PASS_A, then MFMA_PASS_B)."""
+    import csv
+    import workloads
+    w = workloads.ATTN[ATTN_WORKLOAD]
+    vals, durs = {}, {}
+    for d in (dir_a, dir_b):
+        for r in _counter_rows(d):
+            if KERNEL_NAME_PART["attn"] not in r.get("Kernel_Name", ""):
+                continue
+            key = (d, r["Dispatch_Id"])
+            vals.setdefault(key, {})
+            vals[key][r["Counter_Name"]] = vals[key].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+            if "Start_Timestamp" in r:
+                durs[key] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
+    if not vals:
+        raise SystemExit("no attention dispatches in the counter runs")
+    mean = {}
+    for key, cs in vals.items():
+        for name, v in cs.items():
+            mean.setdefault(name, []).append(v)
+    mean = {k: sum(v) / len(v) for k, v in mean.items()}
+    dur = sum(durs.values()) / len(durs) if durs else float("nan")
+    cu, simd, xcc = 256, 4, 8
+    for f in glob.glob(os.path.join(dir_a, "**", "*agent_info.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            if r.get("Agent_Type") == "GPU":
+                cu, simd = int(r["Cu_Count"]), int(r["Simd_Per_Cu"])
+                xcc = int(r.get("Num_Xcc") or xcc)
+    n_mfma = kernel_mfma_count(w)
+    mfma_flop = n_mfma * 32 * 32 * 16 * 2
+    counted_flop = mean.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", float("nan")) * 512
+    busy = mean.get("SQ_VALU_MFMA_BUSY_CYCLES", float("nan"))
+    active = mean.get("GRBM_GUI_ACTIVE", float("nan")) / xcc  # the counter sums the XCDs
+    util = busy / (active * cu * simd)
+    clock = active / dur / 1e9
+    lines = [
+        f"# MFMA utilisation: attn_fwd_mfma<bf16,128,causal> on {ATTN_WORKLOAD}\n",
+        "Commands (run from the repository root on one MI355X):\n",
+        f"    rocprofv3 --pmc {MFMA_PASS_A} --output-format csv -d gpurun_out/pmc_mfma_a -o run -- "
+        "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline",
+        f"    rocprofv3 --pmc {MFMA_PASS_B} --output-format csv -d gpurun_out/pmc_mfma_b -o run -- "
+        "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline",
+        "    python3 bench.py --ingest-mfma gpurun_out/pmc_mfma_a gpurun_out/pmc_mfma_b\n",
+        f"Kernel source sha {source_hash('attn')}; means over {len(vals)} profiled dispatches "
+        f"(mean duration under the profiler {dur * 1e3:.3f} ms).\n",
+        "| quantity | value |", "|---|---|",
+        f"| algorithmic FLOP (4 N^2 d B H / 2) | {w.flops:.4g} |",
+        f"| MFMA FLOP the tile schedule issues ({n_mfma} 32x32x16 MFMAs) | {mfma_flop:.4g} |",
+        f"| MFMA FLOP counted (SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512) | {counted_flop:.4g} |",
+        f"| SQ_VALU_MFMA_BUSY_CYCLES (summed over SIMDs) | {busy:.4g} |",
+        f"| busy cycles per MFMA | {busy / n_mfma:.2f} |",
+        f"| GRBM_GUI_ACTIVE per XCD (GPU cycles; the counter sums {xcc} XCDs) | {active:.4g} |",
+        f"| mean shader clock = GRBM_GUI_ACTIVE / duration | {clock:.3f} GHz |",
+        f"| **MFMA pipe utilisation = busy / (active x {cu} CUs x {simd} SIMDs)** | **{util:.1%}** |",
+        f"| achieved algorithmic rate under the profiler | {w.flops / dur / 1e12:.1f} TFLOP/s |",
+        f"| same, as a fraction of the clock-for-clock peak ({cu * simd} SIMDs x 1024 FLOP/clk at "
+        f"{clock:.2f} GHz) | {w.flops / dur / (cu * simd * 1024 * clock * 1e9):.1%} |",
+        f"| same, as a fraction of the published 2.5 PFLOP/s | {w.flops / dur / 2.5e15:.1%} |",
+        "",
+        "Instruction mix per dispatch (second pass):\n",
+        "| counter | value | per MFMA |", "|---|---|---|",
+    ]
+    for name in MFMA_PASS_B.split():
+        v = mean.get(name, float("nan"))
+        lines.append(f"| {name} | {v:.4g} | {v / n_mfma:.3f} |")
+    lines.append("")
+    os.makedirs(os.path.dirname(MFMA_FILE), exist_ok=True)
+    with open(MFMA_FILE, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print(open(MFMA_FILE).read())
+
+
 def ingest_trace(d: str, warmup: int):
     """Write the per-kernel duration summary of a rocprofv3 --kernel-trace --stats run of the
     default benchmark.  Besides rocprofv3's own statistics over every call, the summary gives
@@ -243,12 +342,16 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--ingest-trace", metavar="TRACE_DIR")
+    ap.add_argument("--ingest-mfma", nargs=2, metavar=("PASS_A_DIR", "PASS_B_DIR"))
     args = ap.parse_args()
     if args.ingest_counters:
         ingest_counters(*args.ingest_counters)
         return
     if args.ingest_trace:
         ingest_trace(args.ingest_trace, args.warmup)
+        return
+    if args.ingest_mfma:
+        ingest_mfma(*args.ingest_mfma)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path is "
@@ -307,8 +410,10 @@ def main():
         step(events[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    attn_ms = sum(e[0].elapsed_time(e[1]) for e in events) / args.steps
-    sm_ms = sum(e[1].elapsed_time(e[2]) for e in events) / args.steps
+    attn_each = sorted(e[0].elapsed_time(e[1]) for e in events)
+    sm_each = sorted(e[1].elapsed_time(e[2]) for e in events)
+    attn_ms = sum(attn_each) / args.steps
+    sm_ms = sum(sm_each) / args.steps
     print(f"[bench] timed {args.steps} steps: attention {attn_ms:.3f} ms, softmax {sm_ms * 1e3:.1f} us",
           file=sys.stderr, flush=True)
 
@@ -337,13 +442,17 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": attn_traffic, "kernel": "attn_fwd_mfma<bf16,128,causal>",
-                     "flop_per_launch": w.flops, "avg_launch_ms": round(attn_ms, 5)},
+                     "flop_per_launch": w.flops, "avg_launch_ms": round(attn_ms, 5),
+                     "median_launch_ms": round(attn_each[len(attn_each) // 2], 5),
+                     "min_launch_ms": round(attn_each[0], 5)},
         "softmax": {"value": round(sm_gbps, 1), "unit": "GB/s",
                     "roofline": {"bound": "hbm", "achieved": round(sm_gbps, 1),
                                  "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                                  "frac": round(sm_gbps / PEAK_HBM_GBPS, 4), "traffic": sm_traffic,
                                  "kernel": "softmax_cached<512,16>",
-                                 "bytes_per_launch": sm_bytes, "avg_launch_us": round(sm_ms * 1e3, 2)},
+                                 "bytes_per_launch": sm_bytes, "avg_launch_us": round(sm_ms * 1e3, 2),
+                                 "median_launch_us": round(sm_each[len(sm_each) // 2] * 1e3, 2),
+                                 "min_launch_us": round(sm_each[0] * 1e3, 2)},
                     "copy_gbps": round(2 * COPY_BYTES / (copy_ms * 1e-3) / 1e9, 1)},
         "kernel_resources": {"attention": attrs, "softmax": sm_attrs},
     }
