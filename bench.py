@@ -449,7 +449,7 @@ def main():
                     "roofline": {"bound": "hbm", "achieved": round(sm_gbps, 1),
                                  "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                                  "frac": round(sm_gbps / PEAK_HBM_GBPS, 4), "traffic": sm_traffic,
-                                 "kernel": "softmax_cached<512,16>",
+                                 "kernel": "softmax_cached<1024,8>",
                                  "bytes_per_launch": sm_bytes, "avg_launch_us": round(sm_ms * 1e3, 2),
                                  "median_launch_us": round(sm_each[len(sm_each) // 2] * 1e3, 2),
                                  "min_launch_us": round(sm_each[0] * 1e3, 2)},

@@ -66,8 +66,11 @@ __device__ __forceinline__ void block_merge(float& m, float& l) {
 
 __device__ __forceinline__ float max4(f32x4 v) { return fmaxf(fmaxf(v.x, v.y), fmaxf(v.z, v.w)); }
 
+// At 1024 threads the instance is held to 64 VGPRs (8 waves per SIMD), so two
+// rows are resident per compute unit; at the compiler's own choice (69) only one is.
 template <int THREADS, int NV>
-__global__ __launch_bounds__(THREADS) void softmax_cached(const float* __restrict__ x,
+__global__ __launch_bounds__(THREADS)
+__attribute__((amdgpu_waves_per_eu(THREADS >= 1024 ? 8 : 1, 8))) void softmax_cached(const float* __restrict__ x,
                                                           float* __restrict__ y, int cols) {
   const size_t row = blockIdx.x;
   const f32x4* xr = reinterpret_cast<const f32x4*>(x + row * (size_t)cols);
@@ -176,7 +179,7 @@ static void pick_softmax(int cols, bool vec_ok, const void** fn, int* threads) {
       {4096, (const void*)softmax_cached<256, 4>, 256},
       {8192, (const void*)softmax_cached<256, 8>, 256},
       {16384, (const void*)softmax_cached<512, 8>, 512},
-      {32768, (const void*)softmax_cached<512, 16>, 512},
+      {32768, (const void*)softmax_cached<1024, 8>, 1024},
   };
   if (vec_ok) {
     for (const auto& c : table) {
