@@ -26,8 +26,9 @@
 //
 // Work decomposition.  A workgroup of 8 waves owns 256 consecutive queries of
 // one (batch, head); each wave owns 32 of them, and all 8 share each K/V tile
-// staged in LDS.  Key tiles are 64 keys.  The waves form two groups of four
-// that run half a tile apart (slot schedule in the kernel): in every phase one
+// staged in LDS.  Key tiles are 64 keys at d = 128 and 128 keys at d = 64.  The
+// waves form two groups of four that run half a tile apart (slot schedule in
+// the kernel): in every phase one
 // wave per SIMD issues MFMAs while the other runs the softmax on the vector
 // ALU, so the matrix unit is not left idle during the softmax.
 //
@@ -123,7 +124,10 @@ __device__ __forceinline__ unsigned pack2(float a, float b) {
 
 constexpr float kSlack = 8.f;  // how far (log2 units) the running maximum may pass m
 constexpr int kBM = 256;       // queries per workgroup
-constexpr int kBN = 64;        // keys per tile
+// keys per tile: 128 at d = 64, where the per-tile fixed costs weigh most and the
+// registers allow it (208 VGPRs); 64 at d = 128 (198 VGPRs, 128 would need 250+)
+template <int D>
+constexpr int kBN = D == 64 ? 128 : 64;
 constexpr int kThreads = 512;  // 8 waves: two groups of 4, one wave of each group per SIMD
 
 // 16-byte chunk swizzles of the K and V tiles in LDS (rows of D bf16/fp16
@@ -159,9 +163,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(
     int N, int n_mtiles, float c, int xcd_groups) {
   using v8 = typename Mma<T>::v8;
   constexpr int ROW_BYTES = D * 2;
-  constexpr int TILE_BYTES = kBN * ROW_BYTES;  // one K or V tile
+  constexpr int BN = kBN<D>;                  // keys per tile
+  constexpr int TILE_BYTES = BN * ROW_BYTES;   // one K or V tile
   constexpr int ND = D / 32;                   // 32-dim blocks of O^T per wave
   constexpr int NK = D / 16;                   // 16-deep MFMA steps of K Q^T
+  constexpr int NH = BN / 32;                  // 32-key blocks of a tile
   constexpr int CPR = D / 8;                   // 16-byte chunks per row
   constexpr int RPI = 1024 / ROW_BYTES;        // rows per 1 KiB wave-wide load
   constexpr int NI = TILE_BYTES / 1024 / 8;    // such loads per wave per tile
@@ -214,14 +220,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(
   f32x16 o[ND];
 #pragma unroll
   for (int db = 0; db < ND; ++db) o[db] = f32x16{};
-  f32x16 s[2] = {f32x16{}, f32x16{}};
-  v8 pf[2][2];  // P^T as 16-bit B operands: [32-key half][16-key step]
+  f32x16 s[NH];
+  v8 pf[NH][2];  // P^T as 16-bit B operands: [32-key block][16-key step]
   float m_run = kNegInf, l_run = 0.f;
 
-  const int nk_all = (N + kBN - 1) / kBN;
-  const int n_kt = CAUSAL ? min(nk_all, (i0 + kBM - 1) / kBN + 1) : nk_all;
+  const int nk_all = (N + BN - 1) / BN;
+  const int n_kt = CAUSAL ? min(nk_all, (i0 + kBM - 1) / BN + 1) : nk_all;
   // tiles holding a key visible to some query of this wave
-  int n_w = CAUSAL ? min(n_kt, (qw0 + 31) / kBN + 1) : n_kt;
+  int n_w = CAUSAL ? min(n_kt, (qw0 + 31) / BN + 1) : n_kt;
   // Without the causal limit the compiler would prove n_w == n_kt, drop the
   // per-wave tests and merge the slots into blocks it schedules with more
   // values live than fit in registers; keep the tests in place.
@@ -242,13 +248,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(
     vgoff[j] = row * ROW_BYTES + (p ^ vswz<D>(row)) * 16;
   }
   auto load_k = [&](int t) {
-    const auto r = make_rsrc(Kh + (size_t)t * kBN * D, (int64_t)(N - t * kBN) * ROW_BYTES);
+    const auto r = make_rsrc(Kh + (size_t)t * BN * D, (int64_t)(N - t * BN) * ROW_BYTES);
 #pragma unroll
     for (int j = 0; j < NI; ++j)
       load16_to_lds(r, kbuf + (t & 1) * TILE_BYTES + (wave_s * NI + j) * 1024, kgoff[j]);
   };
   auto load_v = [&](int t) {
-    const auto r = make_rsrc(Vh + (size_t)t * kBN * D, (int64_t)(N - t * kBN) * ROW_BYTES);
+    const auto r = make_rsrc(Vh + (size_t)t * BN * D, (int64_t)(N - t * BN) * ROW_BYTES);
 #pragma unroll
     for (int j = 0; j < NI; ++j)
       load16_to_lds(r, vbuf + (t & 1) * TILE_BYTES + (wave_s * NI + j) * 1024, vgoff[j]);
@@ -280,15 +286,15 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(
   }
 
   // ---- the three pieces of a tile --------------------------------------------------------
-  // QK(t): S^T = K(t) Q^T, two 32-key halves, from K buffer t % 2.
+  // QK(t): S^T = K(t) Q^T, one accumulator per 32-key block, from K buffer t % 2.
   auto qk = [&](int t) {
     const unsigned char* Kt = kbuf + (t & 1) * TILE_BYTES;
-    s[0] = f32x16{};
-    s[1] = f32x16{};
+#pragma unroll
+    for (int kh = 0; kh < NH; ++kh) s[kh] = f32x16{};
 #pragma unroll
     for (int kb = 0; kb < NK; ++kb) {
 #pragma unroll
-      for (int kh = 0; kh < 2; ++kh) {
+      for (int kh = 0; kh < NH; ++kh) {
         const v8 kf = __builtin_bit_cast(
             v8, *reinterpret_cast<const u32x4*>(Kt + kroff[kb] + kh * 32 * ROW_BYTES));
         s[kh] = Mma<T>::run(kf, qf[kb], s[kh]);
@@ -298,11 +304,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(
   // SM(t): online softmax of S(t): m, l and O rescaled by 2^(m_old - m_new),
   // P = 2^(c S - m_new) packed to 16 bits, with m the trailing reference.
   auto sm = [&](int t) {
-    const int j0 = t * kBN;
+    const int j0 = t * BN;
     // keys past N, and keys after the query when causal (wave-uniform test)
-    if ((j0 + kBN > N) || (CAUSAL && j0 + kBN - 1 > qw0)) {
+    if ((j0 + BN > N) || (CAUSAL && j0 + BN - 1 > qw0)) {
 #pragma unroll
-      for (int kh = 0; kh < 2; ++kh) {
+      for (int kh = 0; kh < NH; ++kh) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = j0 + 32 * kh + 8 * (r >> 2) + 4 * hf + (r & 3);
@@ -312,7 +318,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(
     }
     float mx = kNegInf;
 #pragma unroll
-    for (int kh = 0; kh < 2; ++kh)
+    for (int kh = 0; kh < NH; ++kh)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kh][r]);
     mx = max_halves(mx);
@@ -321,7 +327,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(
     const float m_sub = (m_new == kNegInf) ? 0.f : m_new;  // a fully masked row stays empty
     const float alpha = exp2_fast(m_run - m_sub);
 #pragma unroll
-    for (int kh = 0; kh < 2; ++kh) {
+    for (int kh = 0; kh < NH; ++kh) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) pf[kh][r >> 3][r & 7] = (T)exp2_fast(fmaf(s[kh][r], c, -m_sub));
     }
@@ -330,7 +336,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(
     // then moves O by d p (v - O) / l, not by d p v / l.
     float ls[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kh = 0; kh < 2; ++kh)
+    for (int kh = 0; kh < NH; ++kh)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         const u32x4 w = __builtin_bit_cast(u32x4, pf[kh][kb]);
@@ -348,7 +354,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(
   auto pv = [&](int t) {
     const unsigned char* Vt = vbuf + (t & 1) * TILE_BYTES;
 #pragma unroll
-    for (int kh = 0; kh < 2; ++kh) {
+    for (int kh = 0; kh < NH; ++kh) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
@@ -371,7 +377,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(
     qk(tq);
     // PV MFMAs take two transposed reads each, QK MFMAs one read
     constexpr int kAhead = 4;               // MFMAs whose operands are read ahead
-    constexpr int kPv = 4 * ND, kQk = 2 * NK;
+    constexpr int kPv = 2 * NH * ND, kQk = NH * NK;
     __builtin_amdgcn_sched_group_barrier(0x100, 2 * kAhead, 0);  // DS reads
 #pragma unroll
     for (int i = 0; i < kPv + kQk; ++i) {
