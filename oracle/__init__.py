@@ -1,4 +1,4 @@
-"""fp64 CPU oracle for attention forward and row softmax (ctypes wrapper of oracle.c).
+"""fp64 CPU oracle for attention forward and backward and row softmax (ctypes wrapper of oracle.c).
 
 TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the benchmark's CPU
 baseline may import this package; the product path never does.  It shares no
@@ -55,6 +55,8 @@ class Oracle:
         lib.oracle_online_normaliser.restype = None
         lib.oracle_attention_tiled_row.argtypes = [dp, dp, dp, L, L, D, I, L, L, dp, dp, dp]
         lib.oracle_attention_tiled_row.restype = L
+        lib.oracle_attention_backward.argtypes = [dp, dp, dp, dp, L, L, D, I, dp, dp, dp, dp, dp, I]
+        lib.oracle_attention_backward.restype = None
         self.lib = lib
         self.path = path
 
@@ -128,6 +130,22 @@ class Oracle:
         self.lib.oracle_attention_probs(self._p(q), self._p(k), n, d, float(scale),
                                         int(bool(causal)), int(i), self._p(p))
         return p
+
+    def attention_backward_head(self, q, k, v, dout, scale: float, causal: bool,
+                                dtype: str | None = None, threads: int | None = None):
+        """Gradients of one head: (dQ, dK, dV) [N, d] each, plus the row statistic
+        lse [N] and D [N] (D_i = sum_j P_ij dP_ij) that the recomputation uses."""
+        q, k, v, dout = (self.to_f64(t, dtype) for t in (q, k, v, dout))
+        n, d = q.shape
+        if k.shape != (n, d) or v.shape != (n, d) or dout.shape != (n, d):
+            raise ValueError("q, k, v, dout must share the shape [N, d]")
+        dq, dk, dv = (np.empty((n, d), np.float64) for _ in range(3))
+        lse, dd = np.empty(n, np.float64), np.empty(n, np.float64)
+        self.lib.oracle_attention_backward(self._p(q), self._p(k), self._p(v), self._p(dout), n, d,
+                                           float(scale), int(bool(causal)), self._p(dq),
+                                           self._p(dk), self._p(dv), self._p(lse), self._p(dd),
+                                           threads or default_threads())
+        return dq, dk, dv, lse, dd
 
     # -- online forms ----------------------------------------------------------
     def online_normaliser(self, x) -> tuple[float, float]:

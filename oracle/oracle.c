@@ -1,5 +1,5 @@
 /*
- * oracle.c -- plain fp64 CPU reference for attention forward and row softmax.
+ * oracle.c -- plain fp64 CPU reference for attention forward and backward and row softmax.
  *
  * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may call, link or
  * load this file; only the tests, the smoke check and the benchmark's CPU
@@ -33,7 +33,21 @@
  *                                 rescaled by exp(m_old - m_new), O/l once at
  *                                 the end.  It records every rescale factor.
  *
- * All arrays are row-major and owned by the caller.  Threads split rows only.
+ * The backward pass (gradients of O with respect to Q, K and V for an
+ * upstream gradient dO) is the chain rule through that definition:
+ *
+ *   oracle_attention_backward -- dV = P^T dO, dP = dO V^T,
+ *                                dS = P o (dP - D) with D_i = sum_j P_ij dP_ij,
+ *                                dQ = scale dS K, dK = scale dS^T Q,
+ *                                in the order the backward-pass paragraphs of
+ *                                "Online softmax, and the register that can't
+ *                                move" describe: the forward statistics of
+ *                                every row first, then every score recomputed
+ *                                from Q and K and normalised with the saved
+ *                                statistic in one step (no running update).
+ *
+ * All arrays are row-major and owned by the caller.  Threads split rows (or,
+ * in the second backward pass, key columns) only.
  */
 #include <math.h>
 #include <pthread.h>
@@ -231,4 +245,88 @@ long oracle_attention_tiled_row(const double* q, const double* k, const double* 
   *lse = m + log(l);
   free(s);
   return t;
+}
+
+/* ------------------------------------------------------------------------ */
+/* backward pass by recomputation                                            */
+/* ------------------------------------------------------------------------ */
+typedef struct {
+  const double *q, *k, *v, *dout;
+  long n, d;
+  double scale;
+  int causal;
+  double *dq, *dk, *dv; /* [n][d] each */
+  double *lse, *dd;     /* [n] each: saved row statistic and D_i */
+} bwd_ctx;
+
+/* pass 1, query row i: scores, their statistics (lse_i), dP_ij = <dO_i, v_j>,
+ * D_i = sum_j P_ij dP_ij and dQ_i = scale sum_j P_ij (dP_ij - D_i) k_j */
+static void backward_row(void* p, long i, double* scratch) {
+  bwd_ctx* c = (bwd_ctx*)p;
+  const long n = c->n, d = c->d;
+  double* s = scratch;       /* scores of row i */
+  double* dp = scratch + n;  /* dP of row i */
+  attn_ctx ac = {c->q, c->k, c->v, n, d, c->scale, c->causal, NULL, NULL, NULL};
+  const long nvis = score_row(&ac, i, s);
+  double m = -INFINITY;
+  for (long j = 0; j < nvis; ++j)
+    if (s[j] > m) m = s[j];
+  double l = 0.0;
+  for (long j = 0; j < nvis; ++j) l += exp(s[j] - m);
+  const double* doi = c->dout + i * d;
+  for (long j = 0; j < nvis; ++j) {
+    const double* vj = c->v + j * d;
+    double acc = 0.0;
+    for (long e = 0; e < d; ++e) acc += doi[e] * vj[e];
+    dp[j] = acc;
+  }
+  double di = 0.0;
+  for (long j = 0; j < nvis; ++j) di += exp(s[j] - m) / l * dp[j];
+  double* dqi = c->dq + i * d;
+  for (long e = 0; e < d; ++e) dqi[e] = 0.0;
+  for (long j = 0; j < nvis; ++j) {
+    const double ds = exp(s[j] - m) / l * (dp[j] - di);
+    const double* kj = c->k + j * d;
+    for (long e = 0; e < d; ++e) dqi[e] += c->scale * ds * kj[e];
+  }
+  c->lse[i] = m + log(l);
+  c->dd[i] = di;
+}
+
+/* pass 2, key column j: for every query i that sees key j, the score is
+ * recomputed and normalised with the saved statistic, P_ij = exp(s_ij - lse_i);
+ * dV_j = sum_i P_ij dO_i and dK_j = scale sum_i P_ij (dP_ij - D_i) q_i */
+static void backward_col(void* p, long j, double* scratch) {
+  (void)scratch;
+  bwd_ctx* c = (bwd_ctx*)p;
+  const long n = c->n, d = c->d;
+  const double* kj = c->k + j * d;
+  const double* vj = c->v + j * d;
+  double* dkj = c->dk + j * d;
+  double* dvj = c->dv + j * d;
+  for (long e = 0; e < d; ++e) dkj[e] = dvj[e] = 0.0;
+  for (long i = c->causal ? j : 0; i < n; ++i) {
+    const double* qi = c->q + i * d;
+    const double* doi = c->dout + i * d;
+    double sij = 0.0, dpij = 0.0;
+    for (long e = 0; e < d; ++e) {
+      sij += qi[e] * kj[e];
+      dpij += doi[e] * vj[e];
+    }
+    const double pij = exp(c->scale * sij - c->lse[i]);
+    const double ds = pij * (dpij - c->dd[i]);
+    for (long e = 0; e < d; ++e) {
+      dvj[e] += pij * doi[e];
+      dkj[e] += c->scale * ds * qi[e];
+    }
+  }
+}
+
+void oracle_attention_backward(const double* q, const double* k, const double* v,
+                               const double* dout, long n, long d, double scale, int causal,
+                               double* dq, double* dk, double* dv, double* lse, double* dd,
+                               int nthreads) {
+  bwd_ctx c = {q, k, v, dout, n, d, scale, causal, dq, dk, dv, lse, dd};
+  parallel_rows(backward_row, &c, n, 2 * n, nthreads);
+  parallel_rows(backward_col, &c, n, 0, nthreads);
 }

@@ -291,4 +291,114 @@ def pin_last_tile_case(orc):
         _close(o, o_ref[i], 1e-12, f"last-tile tiled row {i}")
 
 
+# ---------------------------------------------------------------------------
+# backward-pass pins
+# ---------------------------------------------------------------------------
+def _loss(orc, q, k, v, g, scale, causal):
+    """L = sum_ie O_ie g_ie, whose gradient with upstream dO = g is the backward pass."""
+    o, _ = orc.attention_head(q, k, v, scale, causal)
+    return float(np.sum(o * g))
+
+
+def pin_backward_finite_differences(orc):
+    """Every entry of dQ, dK and dV against a central difference of the forward oracle
+    (step 1e-5: truncation ~1e-10, rounding ~1e-11)."""
+    r = _rng(30)
+    n, d, scale = 6, 4, 0.7
+    q, k, v, g = (r.normal(size=(n, d)) for _ in range(4))
+    h = 1e-5
+    for causal in (False, True):
+        dq, dk, dv, _, _ = orc.attention_backward_head(q, k, v, g, scale, causal)
+        for name, x, grad in (("dQ", q, dq), ("dK", k, dk), ("dV", v, dv)):
+            num = np.zeros_like(x)
+            for idx in np.ndindex(x.shape):
+                xp, xm = x.copy(), x.copy()
+                xp[idx] += h
+                xm[idx] -= h
+                args_p = [xp if t is x else t for t in (q, k, v)]
+                args_m = [xm if t is x else t for t in (q, k, v)]
+                num[idx] = (_loss(orc, *args_p, g, scale, causal) -
+                            _loss(orc, *args_m, g, scale, causal)) / (2 * h)
+            _close(grad, num, 1e-7, f"{name} finite difference causal={causal}")
+
+
+def pin_backward_autograd(orc):
+    """torch.autograd in float64 on the CPU, an implementation written independently of
+    this oracle, on a 40 x 16 head."""
+    import torch
+    r = _rng(31)
+    n, d, scale = 40, 16, 0.25
+    q, k, v, g = (r.normal(size=(n, d)) for _ in range(4))
+    for causal in (False, True):
+        tq, tk, tv = (torch.tensor(t, dtype=torch.float64, requires_grad=True) for t in (q, k, v))
+        s = scale * tq @ tk.T
+        if causal:
+            s = s.masked_fill(torch.triu(torch.ones(n, n, dtype=torch.bool), 1), float("-inf"))
+        o = torch.softmax(s, dim=-1) @ tv
+        o.backward(torch.tensor(g))
+        dq, dk, dv, _, _ = orc.attention_backward_head(q, k, v, g, scale, causal)
+        _close(dq, tq.grad.numpy(), 1e-12, f"dQ autograd causal={causal}")
+        _close(dk, tk.grad.numpy(), 1e-12, f"dK autograd causal={causal}")
+        _close(dv, tv.grad.numpy(), 1e-12, f"dV autograd causal={causal}")
+
+
+def pin_backward_column_sums(orc):
+    """Rows of P sum to one, so sum_j dV_j = sum_i dO_i; rows of dS sum to zero, so
+    sum_j dK_j = 0."""
+    r = _rng(32)
+    n, d = 50, 8
+    q, k, v, g = (r.normal(0, 1.5, size=(n, d)) for _ in range(4))
+    for causal in (False, True):
+        _, dk, dv, _, _ = orc.attention_backward_head(q, k, v, g, 0.6, causal)
+        _close(dv.sum(axis=0), g.sum(axis=0), 1e-12, f"sum dV causal={causal}")
+        _close(dk.sum(axis=0), np.zeros(d), 1e-12, f"sum dK causal={causal}")
+
+
+def pin_backward_statistics(orc):
+    """D_i equals <dO_i, O_i> (O = P V), and the saved statistic equals the forward LSE."""
+    r = _rng(33)
+    n, d = 45, 9
+    q, k, v, g = (r.normal(size=(n, d)) for _ in range(4))
+    for causal in (False, True):
+        _, _, _, lse, dd = orc.attention_backward_head(q, k, v, g, 0.35, causal)
+        o, lse_f = orc.attention_head(q, k, v, 0.35, causal)
+        _close(dd, np.sum(g * o, axis=1), 1e-13, f"D = dO . O causal={causal}")
+        _close(lse, lse_f, 1e-14, f"saved statistic causal={causal}")
+
+
+def pin_backward_zero_query(orc):
+    """Q = 0: P_ij = 1/n_i over the n_i visible keys, so dK = 0,
+    dV_j = sum over the queries i that see j of dO_i / n_i, and
+    dQ_i = (scale / n_i) sum_j (dP_ij - mean_j dP_ij) k_j with dP_ij = <dO_i, v_j>."""
+    r = _rng(34)
+    n, d, scale = 23, 5, 0.45
+    k, v, g = (r.normal(size=(n, d)) for _ in range(3))
+    q = np.zeros((n, d))
+    for causal in (False, True):
+        dq, dk, dv, _, _ = orc.attention_backward_head(q, k, v, g, scale, causal)
+        cnt = np.arange(1, n + 1) if causal else np.full(n, n)
+        dv_ref = np.zeros((n, d))
+        dq_ref = np.zeros((n, d))
+        for i in range(n):
+            vis = cnt[i]
+            dv_ref[:vis] += g[i] / vis
+            dp = v[:vis] @ g[i]
+            dq_ref[i] = scale / vis * ((dp - dp.mean())[:, None] * k[:vis]).sum(axis=0)
+        _close(dk, np.zeros((n, d)), 1e-15, f"zero-q dK causal={causal}")
+        _close(dv, dv_ref, 1e-14, f"zero-q dV causal={causal}")
+        _close(dq, dq_ref, 1e-14, f"zero-q dQ causal={causal}")
+
+
+def pin_backward_causal_edges(orc):
+    """Causal: query 0 sees only key 0 (P = 1, so dS = 0 and dQ_0 = 0), and the last key
+    is seen only by the last query: dV_last = P_last,last dO_last."""
+    r = _rng(35)
+    n, d = 12, 6
+    q, k, v, g = (r.normal(size=(n, d)) for _ in range(4))
+    dq, _, dv, _, _ = orc.attention_backward_head(q, k, v, g, 0.8, True)
+    p_last = orc.attention_probs(q, k, 0.8, True, n - 1)
+    _close(dq[0], np.zeros(d), 1e-15, "causal dQ_0")
+    _close(dv[n - 1], p_last[n - 1] * g[n - 1], 1e-15, "causal dV_last")
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -32,6 +32,19 @@ MUTATIONS = [
     ("tiled_tile_max_weights", "psum += exp(s[j] - m_new);", "psum += exp(s[j] - rowmax);"),
     ("tiled_no_final_divide", "o[e] = o[e] / l;", "o[e] = o[e];"),
     ("probs_not_normalised", "p[j] = exp(p[j] - m) / l;", "p[j] = exp(p[j] - m);"),
+    ("bwd_row_drop_d", "const double ds = exp(s[j] - m) / l * (dp[j] - di);",
+     "const double ds = exp(s[j] - m) / l * dp[j];"),
+    ("bwd_col_drop_d", "const double ds = pij * (dpij - c->dd[i]);", "const double ds = pij * dpij;"),
+    ("bwd_d_sign", "di += exp(s[j] - m) / l * dp[j];", "di -= exp(s[j] - m) / l * dp[j];"),
+    ("bwd_dq_no_scale", "dqi[e] += c->scale * ds * kj[e];", "dqi[e] += ds * kj[e];"),
+    ("bwd_dk_transposed", "dkj[e] += c->scale * ds * qi[e];", "dkj[e] += c->scale * ds * kj[e];"),
+    ("bwd_dv_uses_v", "dvj[e] += pij * doi[e];", "dvj[e] += pij * vj[e];"),
+    ("bwd_col_unnormalised", "const double pij = exp(c->scale * sij - c->lse[i]);",
+     "const double pij = exp(c->scale * sij);"),
+    ("bwd_col_causal_off_by_one", "for (long i = c->causal ? j : 0; i < n; ++i) {",
+     "for (long i = c->causal ? j + 1 : 0; i < n; ++i) {"),
+    ("bwd_dp_uses_k", "    const double* vj = c->v + j * d;\n    double acc = 0.0;",
+     "    const double* vj = c->k + j * d;\n    double acc = 0.0;"),
     ("partition_drops_rows", "jobs[t].end = (t + 1) * per < nrows ? (t + 1) * per : nrows;",
      "jobs[t].end = (t + 1) * per < nrows ? (t + 1) * per - 1 : nrows;"),
 ]
