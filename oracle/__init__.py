@@ -55,7 +55,8 @@ class Oracle:
         lib.oracle_online_normaliser.restype = None
         lib.oracle_attention_tiled_row.argtypes = [dp, dp, dp, L, L, D, I, L, L, dp, dp, dp]
         lib.oracle_attention_tiled_row.restype = L
-        lib.oracle_attention_backward.argtypes = [dp, dp, dp, dp, L, L, D, I, dp, dp, dp, dp, dp, I]
+        lib.oracle_attention_backward.argtypes = [dp, dp, dp, dp, dp, L, L, D, I, dp, dp, dp, dp, dp,
+                                                  dp, dp, dp, I]
         lib.oracle_attention_backward.restype = None
         self.lib = lib
         self.path = path
@@ -132,19 +133,30 @@ class Oracle:
         return p
 
     def attention_backward_head(self, q, k, v, dout, scale: float, causal: bool,
-                                dtype: str | None = None, threads: int | None = None):
+                                dtype: str | None = None, threads: int | None = None, o=None,
+                                magnitudes: bool = False):
         """Gradients of one head: (dQ, dK, dV) [N, d] each, plus the row statistic
-        lse [N] and D [N] (D_i = sum_j P_ij dP_ij) that the recomputation uses."""
+        lse [N] and D [N] (D_i = sum_j P_ij dP_ij) that the recomputation uses.
+        With ``o`` (the forward output as a caller stores it), D_i = <dO_i, o_i>.
+        With ``magnitudes``, three more [N, d] arrays follow: the sums of the
+        absolute values of the terms of dQ, dK and dV."""
         q, k, v, dout = (self.to_f64(t, dtype) for t in (q, k, v, dout))
+        o = None if o is None else self.to_f64(o, dtype)
         n, d = q.shape
-        if k.shape != (n, d) or v.shape != (n, d) or dout.shape != (n, d):
-            raise ValueError("q, k, v, dout must share the shape [N, d]")
+        if k.shape != (n, d) or v.shape != (n, d) or dout.shape != (n, d) or (
+                o is not None and o.shape != (n, d)):
+            raise ValueError("q, k, v, dout (and o) must share the shape [N, d]")
         dq, dk, dv = (np.empty((n, d), np.float64) for _ in range(3))
         lse, dd = np.empty(n, np.float64), np.empty(n, np.float64)
-        self.lib.oracle_attention_backward(self._p(q), self._p(k), self._p(v), self._p(dout), n, d,
+        mags = [np.empty((n, d), np.float64) for _ in range(3)] if magnitudes else [None] * 3
+        self.lib.oracle_attention_backward(self._p(q), self._p(k), self._p(v), self._p(dout),
+                                           None if o is None else self._p(o), n, d,
                                            float(scale), int(bool(causal)), self._p(dq),
                                            self._p(dk), self._p(dv), self._p(lse), self._p(dd),
+                                           *(None if m is None else self._p(m) for m in mags),
                                            threads or default_threads())
+        if magnitudes:
+            return (dq, dk, dv, lse, dd, *mags)
         return dq, dk, dv, lse, dd
 
     # -- online forms ----------------------------------------------------------

@@ -37,7 +37,8 @@
  * upstream gradient dO) is the chain rule through that definition:
  *
  *   oracle_attention_backward -- dV = P^T dO, dP = dO V^T,
- *                                dS = P o (dP - D) with D_i = sum_j P_ij dP_ij,
+ *                                dS = P o (dP - D) with D_i = sum_j P_ij dP_ij
+ *                                (= <dO_i, O_i>; optionally from a given O),
  *                                dQ = scale dS K, dK = scale dS^T Q,
  *                                in the order the backward-pass paragraphs of
  *                                "Online softmax, and the register that can't
@@ -257,6 +258,8 @@ typedef struct {
   int causal;
   double *dq, *dk, *dv; /* [n][d] each */
   double *lse, *dd;     /* [n] each: saved row statistic and D_i */
+  const double* o_in;   /* [n][d] or NULL: the forward output a caller holds */
+  double *mq, *mk, *mv; /* [n][d] each or NULL: sums of the absolute values of the terms */
 } bwd_ctx;
 
 /* pass 1, query row i: scores, their statistics (lse_i), dP_ij = <dO_i, v_j>,
@@ -281,13 +284,23 @@ static void backward_row(void* p, long i, double* scratch) {
     dp[j] = acc;
   }
   double di = 0.0;
-  for (long j = 0; j < nvis; ++j) di += exp(s[j] - m) / l * dp[j];
+  if (c->o_in) { /* D_i = <dO_i, O_i> with the O the caller holds */
+    const double* oi = c->o_in + i * d;
+    for (long e = 0; e < d; ++e) di += doi[e] * oi[e];
+  } else {
+    for (long j = 0; j < nvis; ++j) di += exp(s[j] - m) / l * dp[j];
+  }
   double* dqi = c->dq + i * d;
+  double* mqi = c->mq ? c->mq + i * d : NULL;
   for (long e = 0; e < d; ++e) dqi[e] = 0.0;
+  if (mqi)
+    for (long e = 0; e < d; ++e) mqi[e] = 0.0;
   for (long j = 0; j < nvis; ++j) {
     const double ds = exp(s[j] - m) / l * (dp[j] - di);
     const double* kj = c->k + j * d;
     for (long e = 0; e < d; ++e) dqi[e] += c->scale * ds * kj[e];
+    if (mqi)
+      for (long e = 0; e < d; ++e) mqi[e] += c->scale * fabs(ds * kj[e]);
   }
   c->lse[i] = m + log(l);
   c->dd[i] = di;
@@ -304,7 +317,11 @@ static void backward_col(void* p, long j, double* scratch) {
   const double* vj = c->v + j * d;
   double* dkj = c->dk + j * d;
   double* dvj = c->dv + j * d;
+  double* mkj = c->mk ? c->mk + j * d : NULL;
+  double* mvj = c->mv ? c->mv + j * d : NULL;
   for (long e = 0; e < d; ++e) dkj[e] = dvj[e] = 0.0;
+  if (mkj)
+    for (long e = 0; e < d; ++e) mkj[e] = mvj[e] = 0.0;
   for (long i = c->causal ? j : 0; i < n; ++i) {
     const double* qi = c->q + i * d;
     const double* doi = c->dout + i * d;
@@ -319,14 +336,26 @@ static void backward_col(void* p, long j, double* scratch) {
       dvj[e] += pij * doi[e];
       dkj[e] += c->scale * ds * qi[e];
     }
+    if (mkj)
+      for (long e = 0; e < d; ++e) {
+        mvj[e] += fabs(pij * doi[e]);
+        mkj[e] += c->scale * fabs(ds * qi[e]);
+      }
   }
 }
 
+/* o_in may be NULL (D from the definition) or the forward output a caller holds,
+ * rounded as it is stored: D_i = <dO_i, O_i> then uses it, as a backward pass that
+ * receives O does; everything else is unchanged.  mq, mk, mv may be NULL, or
+ * receive the same sums over absolute values of their terms (scale sum_j |dS_ij k_j|,
+ * scale sum_i |dS_ij q_i|, sum_i |P_ij dO_i|): the magnitudes that rounding errors
+ * of P and dS scale with. */
 void oracle_attention_backward(const double* q, const double* k, const double* v,
-                               const double* dout, long n, long d, double scale, int causal,
-                               double* dq, double* dk, double* dv, double* lse, double* dd,
+                               const double* dout, const double* o_in, long n, long d,
+                               double scale, int causal, double* dq, double* dk, double* dv,
+                               double* lse, double* dd, double* mq, double* mk, double* mv,
                                int nthreads) {
-  bwd_ctx c = {q, k, v, dout, n, d, scale, causal, dq, dk, dv, lse, dd};
+  bwd_ctx c = {q, k, v, dout, n, d, scale, causal, dq, dk, dv, lse, dd, o_in, mq, mk, mv};
   parallel_rows(backward_row, &c, n, 2 * n, nthreads);
   parallel_rows(backward_col, &c, n, 0, nthreads);
 }

@@ -366,6 +366,55 @@ def pin_backward_statistics(orc):
         _close(lse, lse_f, 1e-14, f"saved statistic causal={causal}")
 
 
+def pin_backward_given_output(orc):
+    """Passing the forward output O gives D_i = <dO_i, O_i>: with the exact O the
+    gradients are those of the definition; with O rounded to bf16 only D moves, by
+    <dO_i, O_i - round(O_i)>."""
+    r = _rng(36)
+    n, d, scale = 30, 8, 0.5
+    q, k, v, g = (r.normal(size=(n, d)) for _ in range(4))
+    for causal in (False, True):
+        o, _ = orc.attention_head(q, k, v, scale, causal)
+        ref = orc.attention_backward_head(q, k, v, g, scale, causal)
+        got = orc.attention_backward_head(q, k, v, g, scale, causal, o=o)
+        for a, b, what in zip(got, ref, ("dQ", "dK", "dV", "lse", "D")):
+            _close(a, b, 1e-12, f"given exact O {what} causal={causal}")
+        orr = workloads.bf16_bits_to_f32(workloads.f32_to_bf16_bits(o.astype(np.float32))).astype(np.float64)
+        got = orc.attention_backward_head(q, k, v, g, scale, causal, o=orr)
+        _close(got[4], ref[4] + np.sum(g * (orr - o), axis=1), 1e-13, f"given rounded O D causal={causal}")
+        _close(got[2], ref[2], 1e-13, f"given rounded O leaves dV causal={causal}")
+
+
+def pin_backward_magnitudes(orc):
+    """The sums of absolute values bound the sums themselves, change nothing else, and
+    equal them where every term is non-negative: with dO >= 0, dV_j = sum_i P_ij dO_i
+    has only non-negative terms (P >= 0)."""
+    r = _rng(37)
+    n, d, scale = 33, 6, 0.4
+    q, k, v = (r.normal(size=(n, d)) for _ in range(3))
+    g = np.abs(r.normal(size=(n, d)))
+    for causal in (False, True):
+        plain = orc.attention_backward_head(q, k, v, g, scale, causal)
+        dq, dk, dv, lse, dd, mq, mk, mv = orc.attention_backward_head(q, k, v, g, scale, causal,
+                                                                       magnitudes=True)
+        for a, b, what in zip((dq, dk, dv, lse, dd), plain, ("dQ", "dK", "dV", "lse", "D")):
+            _close(a, b, 0.0, f"magnitudes change {what} causal={causal}")
+        for m, x, what in ((mq, dq, "dQ"), (mk, dk, "dK"), (mv, dv, "dV")):
+            assert np.all(m >= np.abs(x) - 1e-15), f"|{what}| exceeds its magnitude sum"
+        _close(mv, dv, 1e-14, f"dV magnitude with dO >= 0 causal={causal}")
+        # mixed signs: every magnitude bounds its sum, and the bound is not attained
+        gm = r.normal(size=(n, d))
+        dq2, dk2, dv2, _, _, mq2, mk2, mv2 = orc.attention_backward_head(q, k, v, gm, scale, causal,
+                                                                          magnitudes=True)
+        for m, x, what in ((mq2, dq2, "dQ"), (mk2, dk2, "dK"), (mv2, dv2, "dV")):
+            assert np.all(m >= np.abs(x) - 1e-15), f"|{what}| exceeds its magnitude sum (mixed signs)"
+            assert np.mean(m) > 1.2 * np.mean(np.abs(x)), f"{what} magnitude equals the sum (mixed signs)"
+        # dQ_i's terms scale |dS_ij| |k_j|: with k replaced by |k| and dS of one sign per
+        # row... simplest exact case: one visible key gives dS = 0, so mq = 0 on causal row 0
+        if causal:
+            _close(mq[0], np.zeros(d), 1e-15, "magnitude of dQ_0 under the causal mask")
+
+
 def pin_backward_zero_query(orc):
     """Q = 0: P_ij = 1/n_i over the n_i visible keys, so dK = 0,
     dV_j = sum over the queries i that see j of dO_i / n_i, and

@@ -45,6 +45,11 @@ MUTATIONS = [
      "for (long i = c->causal ? j + 1 : 0; i < n; ++i) {"),
     ("bwd_dp_uses_k", "    const double* vj = c->v + j * d;\n    double acc = 0.0;",
      "    const double* vj = c->k + j * d;\n    double acc = 0.0;"),
+    ("bwd_given_o_ignored", "for (long e = 0; e < d; ++e) di += doi[e] * oi[e];",
+     "for (long e = 0; e < d; ++e) di += doi[e] * doi[e];"),
+    ("bwd_magnitude_signed", "mvj[e] += fabs(pij * doi[e]);", "mvj[e] += pij * doi[e];"),
+    ("bwd_magnitude_wrong_operand", "mqi[e] += c->scale * fabs(ds * kj[e]);",
+     "mqi[e] += c->scale * fabs(ds * c->q[i * d + e]);"),
     ("partition_drops_rows", "jobs[t].end = (t + 1) * per < nrows ? (t + 1) * per : nrows;",
      "jobs[t].end = (t + 1) * per < nrows ? (t + 1) * per - 1 : nrows;"),
 ]
