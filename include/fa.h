@@ -1,7 +1,7 @@
 /*
  * fa.h -- C ABI of the MI355X (gfx950) attention-forward and row-softmax library.
  *
- * Two operations, both from the pages on online softmax:
+ * Three operations, all from the pages on online softmax:
  *
  *  - fa_fwd*: the attention forward pass O = softmax(scale * Q K^T) V computed
  *    tile by tile with the online-softmax recurrence, so the N x N score
@@ -15,6 +15,9 @@
  *    statistic saved for a backward pass is the natural-log logsumexp
  *    lse_i = ln sum_j exp(scale * q_i . k_j) over the visible keys (the same
  *    page stores the final maximum and sum; one logsumexp carries both).
+ *
+ *  - fa_bwd*: the gradients of that forward pass, by recomputation from the
+ *    saved statistic (backward-pass paragraphs of the same page).
  *
  *  - online_softmax_rows: y = softmax(x) along each row, with the maximum and
  *    the sum of exponentials gathered in one fused pass and merged across
@@ -39,6 +42,8 @@
  */
 #ifndef ONLINE_SOFTMAX_04_AMD_FA_H
 #define ONLINE_SOFTMAX_04_AMD_FA_H
+
+#include <stddef.h>
 
 #include <hip/hip_runtime_api.h>
 
@@ -87,6 +92,42 @@ int fa_fwd_f32(const void* q, const void* k, const void* v, void* o, float* lse,
                int B, int H, int N, int d, float scale, int causal, hipStream_t stream);
 
 /*
+ * Attention backward: the gradients dQ, dK, dV of O = softmax(scale * Q K^T) V
+ * for an upstream gradient dO, bfloat16 operands, fp32 accumulation.
+ *
+ * The N x N weights are not stored by the forward pass; they are recomputed
+ * tile by tile from Q and K and normalised in one step with the saved per-row
+ * statistic (the backward-pass paragraphs of "Online softmax, and the register
+ * that can't move"): P = exp(scale * q_i . k_j - lse_i).  With D_i = <dO_i, O_i>:
+ *   dV = P^T dO,  dS = P o (dO V^T - D),  dQ = scale dS K,  dK = scale dS^T Q.
+ *
+ *  q, k, v, o, dout [B, H, N, d] bfloat16, 16-byte aligned, read only; o is
+ *           the forward output for these q, k, v (it enters through D only).
+ *  lse      [B, H, N] fp32, 4-byte aligned, read only: the natural-log
+ *           logsumexp that fa_fwd writes.
+ *  dq, dk, dv [B, H, N, d] bfloat16, 16-byte aligned, written; they must not
+ *           overlap each other, the workspace or any input.
+ *  workspace  fp32, 16-byte aligned, at least fa_bwd_workspace_bytes(B, H, N)
+ *           bytes, owned by the caller, overwritten (it carries D between the
+ *           two kernels of the call; no state survives the call).
+ *  B, H, N, d, scale, causal: as for fa_fwd (d is 64 or 128).
+ *  Arithmetic: scores, P, dP, dS and all sums in fp32; P and dS are rounded
+ *  to bfloat16 for their matrix products; outputs are rounded once.
+ */
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+           const float* lse, void* dq, void* dk, void* dv, float* workspace, int B, int H, int N,
+           int d, float scale, int causal, hipStream_t stream);
+
+/* Same contract with IEEE half-precision q, k, v, o, dout, dq, dk, dv. */
+int fa_bwd_f16(const void* q, const void* k, const void* v, const void* o, const void* dout,
+               const float* lse, void* dq, void* dk, void* dv, float* workspace, int B, int H,
+               int N, int d, float scale, int causal, hipStream_t stream);
+
+/* Workspace bytes fa_bwd needs for these sizes (4 B H N), 0 if a size is < 1
+ * or the product overflows. */
+size_t fa_bwd_workspace_bytes(int B, int H, int N);
+
+/*
  * Row softmax: y[r, :] = exp(x[r, :] - max_r) / sum_j exp(x[r, j] - max_r).
  *
  *  x     [rows, cols] fp32, 4-byte aligned, read only.
@@ -106,7 +147,8 @@ const char* fa_status_string(int status);
  * reports: registers per lane (arch + accumulation VGPRs as the runtime
  * reports them), LDS bytes per workgroup, private (spill) bytes per lane,
  * threads per workgroup and resident workgroups per compute unit.
- *  op: 0 = fa_fwd, 1 = fa_fwd_f16, 2 = fa_fwd_f32, 3 = online_softmax_rows
+ *  op: 0 = fa_fwd, 1 = fa_fwd_f16, 2 = fa_fwd_f32, 3 = online_softmax_rows,
+ *  4 = fa_bwd's dQ kernel, 5 = fa_bwd's dK/dV kernel
  *  (for op 3, `d` carries cols and `causal` is ignored).
  */
 typedef struct {

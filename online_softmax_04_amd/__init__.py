@@ -28,6 +28,7 @@ FA_ERR_ALIGNMENT = -3
 FA_ERR_HIP = -4
 
 OP_FA_FWD, OP_FA_FWD_F16, OP_FA_FWD_F32, OP_SOFTMAX = 0, 1, 2, 3
+OP_FA_BWD_DQ, OP_FA_BWD_DKDV = 4, 5
 
 
 class FaError(RuntimeError):
@@ -58,6 +59,12 @@ def lib() -> ctypes.CDLL:
             fn = getattr(L, name)
             fn.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp]
             fn.restype = i
+        for name in ("fa_bwd", "fa_bwd_f16"):
+            fn = getattr(L, name)
+            fn.argtypes = [vp] * 10 + [i, i, i, i, f, i, vp]
+            fn.restype = i
+        L.fa_bwd_workspace_bytes.argtypes = [i, i, i]
+        L.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
         L.online_softmax_rows.argtypes = [vp, vp, i, i, vp]
         L.online_softmax_rows.restype = i
         L.fa_status_string.argtypes = [i]
@@ -116,6 +123,30 @@ def fa_fwd_f32(q, k, v, o, lse, B, H, N, d, scale, causal, stream=None):
     _attn("fa_fwd_f32", q, k, v, o, lse, B, H, N, d, scale, causal, stream)
 
 
+def _bwd(name, q, k, v, o, dout, lse, dq, dk, dv, workspace, B, H, N, d, scale, causal, stream):
+    fn = getattr(lib(), name)
+    _check(fn(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk),
+              _ptr(dv), _ptr(workspace), int(B), int(H), int(N), int(d), float(scale), int(causal),
+              _stream(stream)), name)
+
+
+def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, B, H, N, d, scale, causal, stream=None):
+    """bf16 attention backward (see include/fa.h); every argument buffer is on the device."""
+    _bwd("fa_bwd", q, k, v, o, dout, lse, dq, dk, dv, workspace, B, H, N, d, scale, causal, stream)
+
+
+def fa_bwd_f16(q, k, v, o, dout, lse, dq, dk, dv, workspace, B, H, N, d, scale, causal,
+               stream=None):
+    """fp16 attention backward (see include/fa.h)."""
+    _bwd("fa_bwd_f16", q, k, v, o, dout, lse, dq, dk, dv, workspace, B, H, N, d, scale, causal,
+         stream)
+
+
+def fa_bwd_workspace_bytes(B, H, N) -> int:
+    """Bytes of fp32 workspace fa_bwd needs (0 for invalid sizes)."""
+    return int(lib().fa_bwd_workspace_bytes(int(B), int(H), int(N)))
+
+
 def online_softmax_rows(x, y, rows, cols, stream=None):
     """Row softmax of an fp32 [rows, cols] device buffer into y (see include/fa.h)."""
     _check(lib().online_softmax_rows(_ptr(x), _ptr(y), int(rows), int(cols), _stream(stream)),
@@ -163,6 +194,31 @@ def attention(q, k, v, causal: bool = False, scale: float | None = None, out=Non
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     _attn(name, q, k, v, out, lse, B, H, N, d, scale, causal, stream)
     return out, lse
+
+
+def attention_backward(q, k, v, o, dout, lse, causal: bool = False, scale: float | None = None,
+                       stream=None):
+    """dq, dk, dv = gradients of attention for [B, H, N, d] device tensors (bf16 or fp16);
+    o and lse are what ``attention`` returned for q, k, v."""
+    import torch
+    for t in (q, k, v, o, dout):
+        if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+            raise TypeError("q, k, v, o, dout must be device tensors")
+        if not t.is_contiguous() or t.dim() != 4 or t.shape != q.shape or t.dtype != q.dtype:
+            raise ValueError("q, k, v, o, dout must be contiguous [B, H, N, d] tensors of one dtype")
+    names = {torch.bfloat16: "fa_bwd", torch.float16: "fa_bwd_f16"}
+    if q.dtype not in names:
+        raise TypeError(f"unsupported dtype {q.dtype}")
+    B, H, N, d = q.shape
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, N) or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous fp32 [B, H, N] tensor")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+    ws = torch.empty(max(1, fa_bwd_workspace_bytes(B, H, N) // 4), dtype=torch.float32,
+                     device=q.device)
+    _bwd(names[q.dtype], q, k, v, o, dout, lse, dq, dk, dv, ws, B, H, N, d, scale, causal, stream)
+    return dq, dk, dv
 
 
 def softmax(x, out=None, stream=None):

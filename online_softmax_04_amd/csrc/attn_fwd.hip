@@ -66,41 +66,10 @@
 // handed out longest first.
 #include "common.h"
 #include "kernels.h"
+#include "mfma_tile.h"
 
 namespace osm {
 namespace {
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-
-// Word 3 of a raw buffer resource on gfx9-family parts (32-bit data format,
-// no swizzle): out-of-range loads return zero and out-of-range stores are dropped.
-constexpr int kBufferWord3 = 0x00020000;
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
-  const int n = bytes <= 0 ? 0 : (bytes >= 0x7fffffff ? 0x7fffffff : (int)bytes);
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, kBufferWord3);
-}
-
-template <typename T>
-struct Mma;
-template <>
-struct Mma<__bf16> {
-  using v8 = bf16x8;
-  static __device__ __forceinline__ f32x16 run(v8 a, v8 b, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-  }
-};
-template <>
-struct Mma<_Float16> {
-  using v8 = f16x8;
-  static __device__ __forceinline__ f32x16 run(v8 a, v8 b, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
-  }
-};
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
@@ -116,11 +85,6 @@ __device__ __forceinline__ float add_pair<_Float16>(unsigned x, float acc) {
   return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, x), __builtin_bit_cast(f16x2, 0x3c003c00u), acc, false);
 }
 
-template <typename T>
-__device__ __forceinline__ unsigned pack2(float a, float b) {
-  return (unsigned)__builtin_bit_cast(unsigned short, (T)a) |
-         ((unsigned)__builtin_bit_cast(unsigned short, (T)b) << 16);
-}
 
 constexpr float kSlack = 8.f;  // how far (log2 units) the running maximum may pass m
 constexpr int kBM = 256;       // queries per workgroup
@@ -130,31 +94,6 @@ template <int D>
 constexpr int kBN = D == 64 ? 128 : 64;
 constexpr int kThreads = 512;  // 8 waves: two groups of 4, one wave of each group per SIMD
 
-// 16-byte chunk swizzles of the K and V tiles in LDS (rows of D bf16/fp16
-// values, unpadded): physical chunk = logical chunk ^ swizzle(row).  They make
-// the MFMA operand reads conflict-free on gfx950's LDS: K is read as 16-byte
-// pieces of 32 consecutive rows at one chunk position, V through transposed
-// 8-byte reads of 4 consecutive rows x 32 bytes per 16 lanes.
-template <int D>
-__device__ __forceinline__ int kswz(int row) {
-  return D == 128 ? (row & 15) : ((row >> 1) & 7);
-}
-template <int D>
-__device__ __forceinline__ int vswz(int row) {
-  return D == 128 ? 4 * (row & 3) : 4 * ((row >> 1) & 1);
-}
-
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-typedef __attribute__((address_space(3))) void lds_void;
-
-// One wave-wide buffer load straight into LDS: lane i's 16 bytes (at byte
-// offset voff of the buffer) land at lds + 16 i.  Kept out of the kernel
-// templates: used in a template body, this builtin makes the host pass drop
-// the kernel's launch stub.
-__device__ __forceinline__ void load16_to_lds(__amdgpu_buffer_rsrc_t r, unsigned char* lds, int voff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, voff, 0, 0, 0);
-}
 
 template <typename T, int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(

@@ -54,6 +54,44 @@ int attn_entry(osm::Elem elem, const void* q, const void* k, const void* v, void
   return FA_OK;
 }
 
+int bwd_entry(osm::Elem elem, const void* q, const void* k, const void* v, const void* o,
+              const void* dout, const float* lse, void* dq, void* dk, void* dv, float* workspace,
+              int B, int H, int N, int d, float scale, int causal, hipStream_t stream) {
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !workspace)
+    return FA_ERR_INVALID_ARG;
+  if (B < 1 || H < 1 || N < 1 || d < 1) return FA_ERR_INVALID_ARG;
+  if (!std::isfinite(scale) || !(scale > 0.f)) return FA_ERR_INVALID_ARG;
+  if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
+  const uint64_t bytes = tensor_bytes(B, H, N, d, 2);
+  const uint64_t row_bytes = tensor_bytes(B, H, N, 1, 4);  // lse and the workspace
+  if (bytes == 0 || row_bytes == 0) return FA_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if ((uint64_t)N * (uint64_t)d * 2 >= ((uint64_t)1 << 31)) return FA_ERR_UNSUPPORTED;
+  // the dK/dV kernel has the larger grid: one workgroup per 128 keys of a head
+  const uint64_t blocks = (uint64_t)B * (uint64_t)H * (((uint64_t)N + 127) / 128);
+  if (blocks > (uint64_t)INT_MAX) return FA_ERR_INVALID_ARG;
+  const void* in[] = {q, k, v, o, dout};
+  for (const void* p : in)
+    if (!aligned(p, 16)) return FA_ERR_ALIGNMENT;
+  if (!aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) || !aligned(workspace, 16))
+    return FA_ERR_ALIGNMENT;
+  if (!aligned(lse, 4)) return FA_ERR_ALIGNMENT;
+  // outputs (dq, dk, dv, workspace) overlap neither each other nor any input
+  const void* outs[] = {dq, dk, dv, workspace};
+  const uint64_t out_bytes[] = {bytes, bytes, bytes, row_bytes};
+  for (int a = 0; a < 4; ++a) {
+    for (int b = a + 1; b < 4; ++b)
+      if (overlaps(outs[a], out_bytes[a], outs[b], out_bytes[b])) return FA_ERR_INVALID_ARG;
+    for (const void* p : in)
+      if (overlaps(outs[a], out_bytes[a], p, bytes)) return FA_ERR_INVALID_ARG;
+    if (overlaps(outs[a], out_bytes[a], lse, row_bytes)) return FA_ERR_INVALID_ARG;
+  }
+  hipError_t e = osm::launch_attn_bwd(elem, q, k, v, o, dout, lse, dq, dk, dv, workspace, B, H, N,
+                                      d, scale, causal != 0, stream);
+  if (e != hipSuccess) return FA_ERR_HIP;
+  return FA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -71,6 +109,25 @@ int fa_fwd_f16(const void* q, const void* k, const void* v, void* o, float* lse,
 int fa_fwd_f32(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
                int N, int d, float scale, int causal, hipStream_t stream) {
   return attn_entry(osm::Elem::f32, q, k, v, o, lse, B, H, N, d, scale, causal, stream);
+}
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+           const float* lse, void* dq, void* dk, void* dv, float* workspace, int B, int H, int N,
+           int d, float scale, int causal, hipStream_t stream) {
+  return bwd_entry(osm::Elem::bf16, q, k, v, o, dout, lse, dq, dk, dv, workspace, B, H, N, d, scale,
+                   causal, stream);
+}
+
+int fa_bwd_f16(const void* q, const void* k, const void* v, const void* o, const void* dout,
+               const float* lse, void* dq, void* dk, void* dv, float* workspace, int B, int H,
+               int N, int d, float scale, int causal, hipStream_t stream) {
+  return bwd_entry(osm::Elem::f16, q, k, v, o, dout, lse, dq, dk, dv, workspace, B, H, N, d, scale,
+                   causal, stream);
+}
+
+size_t fa_bwd_workspace_bytes(int B, int H, int N) {
+  if (B < 1 || H < 1 || N < 1) return 0;
+  return (size_t)tensor_bytes(B, H, N, 1, 4);
 }
 
 int online_softmax_rows(const float* x, float* y, int rows, int cols, hipStream_t stream) {
@@ -106,6 +163,9 @@ int fa_kernel_attributes(int op, int d, int causal, fa_kernel_attrs* out) {
     if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
     const osm::Elem elem = op == 0 ? osm::Elem::bf16 : (op == 1 ? osm::Elem::f16 : osm::Elem::f32);
     e = osm::attn_fwd_attributes(elem, d, causal != 0, &attr, &threads, &blocks);
+  } else if (op == 4 || op == 5) {
+    if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+    e = osm::attn_bwd_attributes(osm::Elem::bf16, d, causal != 0, op - 4, &attr, &threads, &blocks);
   } else if (op == 3) {
     if (d < 1) return FA_ERR_INVALID_ARG;
     e = osm::softmax_attributes(d, d % 4 == 0, &attr, &threads, &blocks);

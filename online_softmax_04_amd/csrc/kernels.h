@@ -14,6 +14,16 @@ hipError_t launch_attn_fwd(Elem elem, const void* q, const void* k, const void* 
 hipError_t attn_fwd_attributes(Elem elem, int d, bool causal, hipFuncAttributes* attr,
                                int* threads, int* blocks_per_cu);
 
+// Attention backward (bf16 / fp16): dQ and D into `workspace` ([B, H, N] fp32),
+// then dK and dV; arguments already validated by the C ABI layer.
+hipError_t launch_attn_bwd(Elem elem, const void* q, const void* k, const void* v, const void* o,
+                           const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                           float* workspace, int B, int H, int N, int d, float scale, bool causal,
+                           hipStream_t stream);
+// which: 0 = the dQ kernel, 1 = the dK/dV kernel
+hipError_t attn_bwd_attributes(Elem elem, int d, bool causal, int which, hipFuncAttributes* attr,
+                               int* threads, int* blocks_per_cu);
+
 // Row softmax on `stream`; vec_ok = 16-byte aligned pointers and cols % 4 == 0.
 hipError_t launch_softmax(const float* x, float* y, int rows, int cols, bool vec_ok,
                           hipStream_t stream);

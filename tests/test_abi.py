@@ -28,8 +28,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ("fa_fwd", "fa_fwd_f16", "fa_fwd_f32", "online_softmax_rows", "fa_status_string",
-              "fa_kernel_attributes"):
+    for n in ("fa_fwd", "fa_fwd_f16", "fa_fwd_f32", "fa_bwd", "fa_bwd_f16", "fa_bwd_workspace_bytes",
+              "online_softmax_rows", "fa_status_string", "fa_kernel_attributes"):
         assert n in names
 
 
@@ -105,6 +105,62 @@ def test_attn_alignment(name, kw):
                                 dict(lse=A + 192 * MB + 16), dict(lse=A)])
 def test_attn_overlap(name, kw):
     assert call_attn(name, **kw) == fa.FA_ERR_INVALID_ARG
+
+
+# backward: ten buffers, 64 MiB apart (each [1, 2, 128, 64] 16-bit tensor is 32 KiB)
+BWD_NAMES = ["q", "k", "v", "o", "dout", "lse", "dq", "dk", "dv", "ws"]
+BWD_ENTRIES = ["fa_bwd", "fa_bwd_f16"]
+
+
+def call_bwd(name="fa_bwd", B=1, H=2, N=128, d=64, scale=0.125, causal=0, **ptrs):
+    p = {n: A + 64 * MB * i for i, n in enumerate(BWD_NAMES)}
+    p.update(ptrs)
+    fn = getattr(fa.lib(), name)
+    return fn(*(p[n] for n in BWD_NAMES), B, H, N, d, scale, causal, None)
+
+
+@pytest.mark.parametrize("name", BWD_ENTRIES)
+@pytest.mark.parametrize("which", BWD_NAMES)
+def test_bwd_null_pointer(name, which):
+    assert call_bwd(name, **{which: 0}) == fa.FA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("name", BWD_ENTRIES)
+@pytest.mark.parametrize("kw", [dict(B=0), dict(H=0), dict(N=0), dict(d=0), dict(N=-5),
+                                dict(scale=0.0), dict(scale=math.nan), dict(causal=2),
+                                dict(B=1 << 20, H=1 << 20, N=1 << 20, d=128),
+                                dict(B=1 << 16, H=1 << 16, N=256, d=64)])
+def test_bwd_bad_arguments(name, kw):
+    assert call_bwd(name, **kw) == fa.FA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("name", BWD_ENTRIES)
+@pytest.mark.parametrize("d", [32, 96, 256])
+def test_bwd_unsupported_head_dim(name, d):
+    assert call_bwd(name, d=d) == fa.FA_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("name", BWD_ENTRIES)
+@pytest.mark.parametrize("which,off", [("q", 2), ("dout", 8), ("dq", 4), ("dv", 2), ("ws", 4),
+                                       ("lse", 2)])
+def test_bwd_alignment(name, which, off):
+    base = A + 64 * MB * BWD_NAMES.index(which)
+    assert call_bwd(name, **{which: base + off}) == fa.FA_ERR_ALIGNMENT
+
+
+@pytest.mark.parametrize("name", BWD_ENTRIES)
+@pytest.mark.parametrize("kw", [dict(dq=A), dict(dk=A + 64 * MB * 4 + 1024),
+                                dict(dv=A + 64 * MB * 6), dict(ws=A + 64 * MB * 7 + 16),
+                                dict(dq=A + 64 * MB * 5 + 512), dict(ws=A + 64 * MB * 5)])
+def test_bwd_overlap(name, kw):
+    """Outputs may overlap neither an input nor each other."""
+    assert call_bwd(name, **kw) == fa.FA_ERR_INVALID_ARG
+
+
+def test_bwd_workspace_bytes():
+    assert fa.fa_bwd_workspace_bytes(2, 3, 100) == 4 * 2 * 3 * 100
+    assert fa.fa_bwd_workspace_bytes(0, 3, 100) == 0
+    assert fa.fa_bwd_workspace_bytes(1 << 30, 1 << 30, 1 << 30) == 0
 
 
 def call_softmax(x=A, y=A + 64 * MB, rows=4, cols=100):
