@@ -417,6 +417,32 @@ def main():
     print(f"[bench] timed {args.steps} steps: attention {attn_ms:.3f} ms, softmax {sm_ms * 1e3:.1f} us",
           file=sys.stderr, flush=True)
 
+    # The backward pass (fa_bwd) on the same inputs, after the timed steps: the
+    # forward's O and logsumexp, a synthetic upstream gradient.  Reported beside
+    # the step, not inside it.
+    gen = torch.Generator(device=dev).manual_seed(97700)
+    dod = torch.randn(qd.shape, device=dev, generator=gen).to(torch.bfloat16)
+    dqd, dkd, dvd = (torch.empty_like(qd) for _ in range(3))
+    wsd = torch.empty(fa.fa_bwd_workspace_bytes(w.B, w.H, w.N) // 4, dtype=torch.float32, device=dev)
+
+    def bwd():
+        fa.fa_bwd(qd, kd, vd, od, dod, lsed, dqd, dkd, dvd, wsd, w.B, w.H, w.N, w.d, w.sm_scale, 1,
+                  stream)
+
+    for _ in range(args.warmup):
+        bwd()
+    bev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        bev[i][0].record(stream)
+        bwd()
+        bev[i][1].record(stream)
+    torch.cuda.synchronize()
+    bwd_each = sorted(e[0].elapsed_time(e[1]) for e in bev)
+    bwd_ms = sum(bwd_each) / args.steps
+    bwd_flop = 2.5 * w.flops  # dV, dP, dQ, dK and the recomputed S: 5 products vs 2
+    bwd_tflops = bwd_flop / (bwd_ms * 1e-3) / 1e12
+    print(f"[bench] backward {bwd_ms:.3f} ms", file=sys.stderr, flush=True)
+
     tflops = w.flops / (attn_ms * 1e-3) / 1e12
     sm_bytes = sw.algorithmic_bytes
     sm_gbps = sm_bytes / (sm_ms * 1e-3) / 1e9
@@ -454,7 +480,19 @@ def main():
                                  "median_launch_us": round(sm_each[len(sm_each) // 2] * 1e3, 2),
                                  "min_launch_us": round(sm_each[0] * 1e3, 2)},
                     "copy_gbps": round(2 * COPY_BYTES / (copy_ms * 1e-3) / 1e9, 1)},
-        "kernel_resources": {"attention": attrs, "softmax": sm_attrs},
+        "backward": {"value": round(bwd_tflops, 2), "unit": "TFLOP/s",
+                     "flop_per_launch": bwd_flop,
+                     "mfma_flop_issued_per_launch": 3.5 * w.flops,
+                     "avg_launch_ms": round(bwd_ms, 5),
+                     "median_launch_ms": round(bwd_each[len(bwd_each) // 2], 5),
+                     "roofline": {"bound": "mfma", "achieved": round(bwd_tflops, 2),
+                                  "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                                  "frac": round(bwd_tflops / PEAK_BF16_TFLOPS, 4),
+                                  "kernels": ["attn_bwd_dq<bf16,128,causal>",
+                                              "attn_bwd_dkdv<bf16,128,causal>"]}},
+        "kernel_resources": {"attention": attrs, "softmax": sm_attrs,
+                             "backward_dq": fa.kernel_attributes(fa.OP_FA_BWD_DQ, w.d, True),
+                             "backward_dkdv": fa.kernel_attributes(fa.OP_FA_BWD_DKDV, w.d, True)},
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the fp64 oracle on the host", file=sys.stderr, flush=True)
