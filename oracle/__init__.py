@@ -49,6 +49,8 @@ class Oracle:
         lib.oracle_softmax_rows.restype = None
         lib.oracle_attention_rows.argtypes = [dp, dp, dp, L, L, D, I, lp, L, dp, dp, I]
         lib.oracle_attention_rows.restype = None
+        lib.oracle_attention_ranged.argtypes = [dp, dp, dp, L, L, D, lp, lp, lp, L, dp, dp, I]
+        lib.oracle_attention_ranged.restype = None
         lib.oracle_attention_probs.argtypes = [dp, dp, L, L, D, I, L, dp]
         lib.oracle_attention_probs.restype = None
         lib.oracle_online_normaliser.argtypes = [dp, L, dp, dp]
@@ -105,6 +107,25 @@ class Oracle:
                                        rows.ctypes.data_as(ctypes.POINTER(ctypes.c_long)),
                                        rows.size, self._p(o), self._p(lse),
                                        threads or default_threads())
+        return o, lse
+
+    def attention_ranged(self, q, k, v, scale: float, lo, hi, rows=None, dtype: str | None = None,
+                         threads: int | None = None):
+        """O and LSE of one head where query i sees keys lo[i] .. hi[i] (inclusive)."""
+        q, k, v = (self.to_f64(t, dtype) for t in (q, k, v))
+        n, d = q.shape
+        lo = np.ascontiguousarray(lo, dtype=np.int64)
+        hi = np.ascontiguousarray(hi, dtype=np.int64)
+        if lo.shape != (n,) or hi.shape != (n,) or np.any(lo < 0) or np.any(hi >= n) or np.any(lo > hi):
+            raise ValueError("need 0 <= lo[i] <= hi[i] < N for every query")
+        rows = np.arange(n, dtype=np.int64) if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
+        o = np.empty((rows.size, d), np.float64)
+        lse = np.empty(rows.size, np.float64)
+        lp = ctypes.POINTER(ctypes.c_long)
+        self.lib.oracle_attention_ranged(self._p(q), self._p(k), self._p(v), n, d, float(scale),
+                                         lo.ctypes.data_as(lp), hi.ctypes.data_as(lp),
+                                         rows.ctypes.data_as(lp), rows.size, self._p(o),
+                                         self._p(lse), threads or default_threads())
         return o, lse
 
     def attention(self, q, k, v, scale: float, causal: bool, rows_of=None,

@@ -36,6 +36,10 @@
  * The backward pass (gradients of O with respect to Q, K and V for an
  * upstream gradient dO) is the chain rule through that definition:
  *
+ *   oracle_attention_ranged   -- the same with an explicit key range per query
+ *                                (sliding windows and document boundaries of
+ *                                "Online Softmax: Tiling Across a Reduction").
+ *
  *   oracle_attention_backward -- dV = P^T dO, dP = dO V^T,
  *                                dS = P o (dP - D) with D_i = sum_j P_ij dP_ij
  *                                (= <dO_i, O_i>; optionally from a given O),
@@ -178,6 +182,52 @@ void oracle_attention_rows(const double* q, const double* k, const double* v, lo
                            double* lse, int nthreads) {
   attn_ctx c = {q, k, v, n, d, scale, causal, rows, o, lse};
   parallel_rows(attention_one_row, &c, nrows, n, nthreads);
+}
+
+/* Attention where query i sees exactly the keys lo[i] .. hi[i] (inclusive): the
+ * structured masks of "Online Softmax: Tiling Across a Reduction" (the paragraph
+ * on sliding windows, block sparsity and document masks) written as an explicit
+ * key range per query.  Same three passes as above over that range. */
+typedef struct {
+  const double *q, *k, *v;
+  long n, d;
+  double scale;
+  const long *lo, *hi, *rows;
+  double *o, *lse;
+} ranged_ctx;
+
+static void ranged_one_row(void* p, long r, double* s) {
+  ranged_ctx* c = (ranged_ctx*)p;
+  const long i = c->rows[r], j0 = c->lo[i], j1 = c->hi[i];
+  const double* qrow = c->q + i * c->d;
+  for (long j = j0; j <= j1; ++j) {
+    const double* kj = c->k + j * c->d;
+    double acc = 0.0;
+    for (long e = 0; e < c->d; ++e) acc += qrow[e] * kj[e];
+    s[j - j0] = c->scale * acc;
+  }
+  const long cnt = j1 - j0 + 1;
+  double m = -INFINITY;
+  for (long t = 0; t < cnt; ++t)              /* pass 1: the row maximum */
+    if (s[t] > m) m = s[t];
+  double l = 0.0;
+  for (long t = 0; t < cnt; ++t) l += exp(s[t] - m);   /* pass 2: the sum */
+  double* o = c->o + r * c->d;
+  for (long e = 0; e < c->d; ++e) o[e] = 0.0;
+  for (long t = 0; t < cnt; ++t) {            /* pass 3: P V */
+    const double pij = exp(s[t] - m) / l;
+    const double* vj = c->v + (j0 + t) * c->d;
+    for (long e = 0; e < c->d; ++e) o[e] += pij * vj[e];
+  }
+  c->lse[r] = log(l) + m;
+}
+
+/* lo[i] <= hi[i] must hold for every i (an empty range has no softmax) */
+void oracle_attention_ranged(const double* q, const double* k, const double* v, long n, long d,
+                             double scale, const long* lo, const long* hi, const long* rows,
+                             long nrows, double* o, double* lse, int nthreads) {
+  ranged_ctx c = {q, k, v, n, d, scale, lo, hi, rows, o, lse};
+  parallel_rows(ranged_one_row, &c, nrows, n, nthreads);
 }
 
 /* the probability row p_ij = exp(s_ij - m_i)/l_i (zero for hidden keys) */

@@ -292,6 +292,63 @@ def pin_last_tile_case(orc):
 
 
 # ---------------------------------------------------------------------------
+# key-range (structured mask) pins
+# ---------------------------------------------------------------------------
+def pin_ranged_full_ranges_are_causal_and_dense(orc):
+    """lo = 0, hi = i is the causal rule; lo = 0, hi = N - 1 is no mask."""
+    r = _rng(40)
+    n, d = 37, 6
+    q, k, v = (r.normal(size=(n, d)) for _ in range(3))
+    for causal, hi in ((True, np.arange(n)), (False, np.full(n, n - 1))):
+        o1, l1 = orc.attention_ranged(q, k, v, 0.45, np.zeros(n, np.int64), hi)
+        o2, l2 = orc.attention_head(q, k, v, 0.45, causal)
+        _close(o1, o2, 1e-14, f"full range O causal={causal}")
+        _close(l1, l2, 1e-14, f"full range LSE causal={causal}")
+
+
+def pin_ranged_window_is_a_slice(orc):
+    """A window of keys lo..hi is plain attention of q_i over the sliced K and V."""
+    r = _rng(41)
+    n, d = 40, 5
+    q, k, v = (r.normal(size=(n, d)) for _ in range(3))
+    w = 7
+    lo = np.maximum(0, np.arange(n) - w + 1)
+    hi = np.arange(n)
+    o, lse = orc.attention_ranged(q, k, v, 0.6, lo, hi)
+    for i in range(n):
+        ks, vs = k[lo[i]:hi[i] + 1], v[lo[i]:hi[i] + 1]
+        qs = np.tile(q[i], (ks.shape[0], 1))
+        oi, li = orc.attention_head(qs, ks, vs, 0.6, False, rows=[0])
+        _close(o[i], oi[0], 1e-14, f"window row {i}")
+        _close([lse[i]], li, 1e-14, f"window lse row {i}")
+
+
+def pin_ranged_documents_are_independent(orc):
+    """Packed documents under a causal mask: each document alone, causally."""
+    r = _rng(42)
+    lens = [5, 1, 12, 9]
+    n, d = sum(lens), 4
+    q, k, v = (r.normal(size=(n, d)) for _ in range(3))
+    start = np.repeat(np.cumsum([0] + lens[:-1]), lens)
+    o, lse = orc.attention_ranged(q, k, v, 0.8, start, np.arange(n))
+    for s0, ln in zip(np.cumsum([0] + lens[:-1]), lens):
+        oi, li = orc.attention_head(q[s0:s0 + ln], k[s0:s0 + ln], v[s0:s0 + ln], 0.8, True)
+        _close(o[s0:s0 + ln], oi, 1e-14, f"document at {s0}")
+        _close(lse[s0:s0 + ln], li, 1e-14, f"document lse at {s0}")
+
+
+def pin_ranged_single_key(orc):
+    """lo = hi = j: O_i = v_j and lse_i = scale <q_i, k_j>."""
+    r = _rng(43)
+    n, d = 11, 3
+    q, k, v = (r.normal(size=(n, d)) for _ in range(3))
+    j = r.integers(0, n, size=n)
+    o, lse = orc.attention_ranged(q, k, v, 0.3, j, j)
+    _close(o, v[j], 1e-15, "single key O")
+    _close(lse, 0.3 * np.sum(q * k[j], axis=1), 1e-14, "single key LSE")
+
+
+# ---------------------------------------------------------------------------
 # backward-pass pins
 # ---------------------------------------------------------------------------
 def _loss(orc, q, k, v, g, scale, causal):

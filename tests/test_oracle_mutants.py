@@ -50,6 +50,12 @@ MUTATIONS = [
     ("bwd_magnitude_signed", "mvj[e] += fabs(pij * doi[e]);", "mvj[e] += pij * doi[e];"),
     ("bwd_magnitude_wrong_operand", "mqi[e] += c->scale * fabs(ds * kj[e]);",
      "mqi[e] += c->scale * fabs(ds * c->q[i * d + e]);"),
+    ("ranged_hi_exclusive", "const long i = c->rows[r], j0 = c->lo[i], j1 = c->hi[i];",
+     "const long i = c->rows[r], j0 = c->lo[i], j1 = c->hi[i] > c->lo[i] ? c->hi[i] - 1 : c->hi[i];"),
+    ("ranged_values_unshifted", "const double* vj = c->v + (j0 + t) * c->d;", "const double* vj = c->v + t * c->d;"),
+    ("ranged_keys_from_zero", "for (long e = 0; e < c->d; ++e) acc += qrow[e] * kj[e];",
+     "for (long e = 0; e < c->d; ++e) acc += qrow[e] * c->k[(j - j0) * c->d + e];"),
+    ("ranged_query_is_key", "acc += qrow[e] * kj[e];", "acc += kj[e] * kj[e];"),
     ("partition_drops_rows", "jobs[t].end = (t + 1) * per < nrows ? (t + 1) * per : nrows;",
      "jobs[t].end = (t + 1) * per < nrows ? (t + 1) * per - 1 : nrows;"),
 ]
