@@ -443,6 +443,35 @@ def main():
     bwd_tflops = bwd_flop / (bwd_ms * 1e-3) / 1e12
     print(f"[bench] backward {bwd_ms:.3f} ms", file=sys.stderr, flush=True)
 
+    # Structured masks (sliding window over packed documents) on the same inputs;
+    # FLOP counted over the visible query-key pairs only.
+    lw = workloads.LOCAL_WORKLOAD
+    doc = workloads.packed_doc_starts(w.B, w.N, lw["doc_seed"], lw["doc_min"], lw["doc_max"])
+    pairs = 0
+    for b in range(w.B):
+        lo, hi = workloads.local_ranges(doc[b], lw["window"])
+        pairs += int(np.sum(hi - lo + 1))
+    loc_flop = 4.0 * w.d * w.H * pairs
+    docd = torch.from_numpy(doc).to(dev)
+    lod = torch.empty_like(qd)
+
+    def local():
+        fa.fa_fwd_local(qd, kd, vd, lod, lsed, docd, lw["window"], w.B, w.H, w.N, w.d, w.sm_scale,
+                        stream)
+
+    for _ in range(args.warmup):
+        local()
+    lev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        lev[i][0].record(stream)
+        local()
+        lev[i][1].record(stream)
+    torch.cuda.synchronize()
+    loc_each = sorted(e[0].elapsed_time(e[1]) for e in lev)
+    loc_ms = sum(loc_each) / args.steps
+    loc_tflops = loc_flop / (loc_ms * 1e-3) / 1e12
+    print(f"[bench] local {loc_ms:.3f} ms", file=sys.stderr, flush=True)
+
     tflops = w.flops / (attn_ms * 1e-3) / 1e12
     sm_bytes = sw.algorithmic_bytes
     sm_gbps = sm_bytes / (sm_ms * 1e-3) / 1e9
@@ -490,6 +519,14 @@ def main():
                                   "frac": round(bwd_tflops / PEAK_BF16_TFLOPS, 4),
                                   "kernels": ["attn_bwd_dq<bf16,128,causal>",
                                               "attn_bwd_dkdv<bf16,128,causal>"]}},
+        "local": {"workload": lw["name"], "value": round(loc_tflops, 2), "unit": "TFLOP/s",
+                  "visible_pairs": pairs, "flop_per_launch": loc_flop,
+                  "avg_launch_ms": round(loc_ms, 5),
+                  "median_launch_ms": round(loc_each[len(loc_each) // 2], 5),
+                  "roofline": {"bound": "mfma", "achieved": round(loc_tflops, 2),
+                               "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                               "frac": round(loc_tflops / PEAK_BF16_TFLOPS, 4),
+                               "kernel": "attn_fwd_mfma<bf16,128,causal,local>"}},
         "kernel_resources": {"attention": attrs, "softmax": sm_attrs,
                              "backward_dq": fa.kernel_attributes(fa.OP_FA_BWD_DQ, w.d, True),
                              "backward_dkdv": fa.kernel_attributes(fa.OP_FA_BWD_DKDV, w.d, True)},

@@ -86,6 +86,30 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
 int fa_fwd_f16(const void* q, const void* k, const void* v, void* o, float* lse,
                int B, int H, int N, int d, float scale, int causal, hipStream_t stream);
 
+/*
+ * Causal attention forward with structured masks as tile skips (sliding
+ * windows and document boundaries, the structured-mask paragraph of "Online
+ * Softmax: Tiling Across a Reduction"), bfloat16 operands: query i of batch b
+ * sees keys j with lo_i <= j <= i, where
+ *   lo_i = max(doc_start[b * N + i], i - window + 1)     (clamped to 0 .. i).
+ *  doc_start  [B, N] int32, 4-byte aligned, read only: the first position of the
+ *             document that position i belongs to (packed sequences), shared
+ *             by every head; NULL = one document per batch row.
+ *  window     keys per query including itself; 0 = unbounded.
+ *  Key tiles wholly before a query block's smallest lo_i or after its
+ *  diagonal are never read; tiles crossing a bound are masked element by
+ *  element.  Every other argument, layout, error and the arithmetic are those
+ *  of fa_fwd with causal = 1; lse is over the visible keys.
+ */
+int fa_fwd_local(const void* q, const void* k, const void* v, void* o, float* lse,
+                 const int* doc_start, int window, int B, int H, int N, int d, float scale,
+                 hipStream_t stream);
+
+/* Same contract with IEEE half-precision Q/K/V/O. */
+int fa_fwd_local_f16(const void* q, const void* k, const void* v, void* o, float* lse,
+                     const int* doc_start, int window, int B, int H, int N, int d, float scale,
+                     hipStream_t stream);
+
 /* Same contract with fp32 Q/K/V/O: products and sums in fp32 throughout, no
  * reduced-precision operand anywhere (the fp32 workloads' path). */
 int fa_fwd_f32(const void* q, const void* k, const void* v, void* o, float* lse,

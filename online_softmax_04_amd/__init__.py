@@ -59,6 +59,10 @@ def lib() -> ctypes.CDLL:
             fn = getattr(L, name)
             fn.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp]
             fn.restype = i
+        for name in ("fa_fwd_local", "fa_fwd_local_f16"):
+            fn = getattr(L, name)
+            fn.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, vp]
+            fn.restype = i
         for name in ("fa_bwd", "fa_bwd_f16"):
             fn = getattr(L, name)
             fn.argtypes = [vp] * 10 + [i, i, i, i, f, i, vp]
@@ -121,6 +125,22 @@ def fa_fwd_f16(q, k, v, o, lse, B, H, N, d, scale, causal, stream=None):
 def fa_fwd_f32(q, k, v, o, lse, B, H, N, d, scale, causal, stream=None):
     """fp32 attention forward (see include/fa.h)."""
     _attn("fa_fwd_f32", q, k, v, o, lse, B, H, N, d, scale, causal, stream)
+
+
+def _local(name, q, k, v, o, lse, doc_start, window, B, H, N, d, scale, stream):
+    fn = getattr(lib(), name)
+    _check(fn(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(doc_start), int(window), int(B),
+              int(H), int(N), int(d), float(scale), _stream(stream)), name)
+
+
+def fa_fwd_local(q, k, v, o, lse, doc_start, window, B, H, N, d, scale, stream=None):
+    """bf16 causal attention with a sliding window and document starts (see include/fa.h)."""
+    _local("fa_fwd_local", q, k, v, o, lse, doc_start, window, B, H, N, d, scale, stream)
+
+
+def fa_fwd_local_f16(q, k, v, o, lse, doc_start, window, B, H, N, d, scale, stream=None):
+    """fp16 causal attention with a sliding window and document starts (see include/fa.h)."""
+    _local("fa_fwd_local_f16", q, k, v, o, lse, doc_start, window, B, H, N, d, scale, stream)
 
 
 def _bwd(name, q, k, v, o, dout, lse, dq, dk, dv, workspace, B, H, N, d, scale, causal, stream):

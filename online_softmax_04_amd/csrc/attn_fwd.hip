@@ -95,11 +95,12 @@ constexpr int kBN = D == 64 ? 128 : 64;
 constexpr int kThreads = 512;  // 8 waves: two groups of 4, one wave of each group per SIMD
 
 
-template <typename T, int D, bool CAUSAL>
+template <typename T, int D, bool CAUSAL, bool LOCAL>
 __global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE, int BH,
-    int N, int n_mtiles, float c, int xcd_groups) {
+    int N, int n_mtiles, float c, int xcd_groups, int H, const int* __restrict__ doc_start,
+    int window) {
   using v8 = typename Mma<T>::v8;
   constexpr int ROW_BYTES = D * 2;
   constexpr int BN = kBN<D>;                  // keys per tile
@@ -171,6 +172,35 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(
   // per-wave tests and merge the slots into blocks it schedules with more
   // values live than fit in registers; keep the tests in place.
   asm volatile("" : "+v"(n_w));
+
+  // LOCAL (with CAUSAL): query i sees keys lo_i .. i, lo_i = max(document start,
+  // i - window + 1).  Whole tiles before a wave's smallest lo_i are skipped (tw0),
+  // the workgroup loads from the smallest over its waves (t0), and tiles reaching
+  // below a wave's largest lo_i are masked element by element.
+  int lo_i = 0, lo_max_w = 0, tw0 = 0, t0 = 0;
+  if constexpr (LOCAL) {
+    const int qc = min(qi, N - 1);
+    int lo = doc_start ? doc_start[(size_t)(bh / H) * N + qc] : 0;
+    lo = min(max(lo, 0), qc);
+    if (window > 0) lo = max(lo, qc - window + 1);
+    lo_i = lo;
+    int mn = lo, mx = lo;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      mn = min(mn, __shfl_xor(mn, off));
+      mx = max(mx, __shfl_xor(mx, off));
+    }
+    lo_max_w = mx;
+    tw0 = __builtin_amdgcn_readfirstlane(mn) / BN;
+    __shared__ int wave_first[kThreads / 64];
+    if (lane == 0) wave_first[wave] = tw0;
+    __syncthreads();
+    t0 = wave_first[0];
+#pragma unroll
+    for (int w = 1; w < kThreads / 64; ++w) t0 = min(t0, wave_first[w]);
+  }
+  // tile t holds keys this wave computes with
+  auto act = [&](int t) { return (!LOCAL || t >= tw0) && t < n_w; };
 
   // ---- loader: global -> LDS directly, no registers ------------------------------------
   // A wave-wide 16-byte-per-lane buffer load with the LDS flag writes lane i's
@@ -245,13 +275,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(
   auto sm = [&](int t) {
     const int j0 = t * BN;
     // keys past N, and keys after the query when causal (wave-uniform test)
-    if ((j0 + BN > N) || (CAUSAL && j0 + BN - 1 > qw0)) {
+    if ((j0 + BN > N) || (CAUSAL && j0 + BN - 1 > qw0) || (LOCAL && j0 < lo_max_w)) {
 #pragma unroll
       for (int kh = 0; kh < NH; ++kh) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = j0 + 32 * kh + 8 * (r >> 2) + 4 * hf + (r & 3);
-          if (key >= N || (CAUSAL && key > qi)) s[kh][r] = kNegInf;
+          if (key >= N || (CAUSAL && key > qi) || (LOCAL && key < lo_i)) s[kh][r] = kNegInf;
         }
       }
     }
@@ -338,56 +368,106 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(
   // ends X(t).  That barrier is the only one per tile: no LDS buffer changes
   // hands between Y(t) and X(t+1), and meeting once per tile keeps the two
   // groups in opposite phases.
-  load_k(0);
-  loads_landed();
-  __syncthreads();
-  // Retire the Q loads here.  Left pending, they would make the first MFMA that
-  // reads Q wait on the vector-memory counter, which then also counts the tile
-  // loads in flight.
-#pragma unroll
-  for (int kb = 0; kb < NK; ++kb) asm volatile("" ::"v"(qf[kb]));
-  // slot Y(-1): load K(1), V(0); group 0 computes S(0)
-  if (n_kt > 1) load_k(1);
-  load_v(0);
-  if (group == 0) {
-    __builtin_amdgcn_s_setprio(1);
-    qk(0);
-    __builtin_amdgcn_s_setprio(0);
-  }
-  __syncthreads();
-  for (int t = 0; t < n_kt; ++t) {
-    // ---- slot X(t)
-    if (group == 0) {
-      if (t < n_w) sm(t);
-    } else {
-      __builtin_amdgcn_s_setprio(1);
-      if (t >= 1 && t < n_w) {
-        pv_qk(t - 1, t);
-      } else {
-        if (t >= 1 && t - 1 < n_w) pv(t - 1);
-        if (t < n_w) qk(t);
-      }
-      __builtin_amdgcn_s_setprio(0);
-    }
-    loads_landed();  // K(t+1), V(t)
+  if constexpr (!LOCAL) {
+    load_k(0);
+    loads_landed();
     __syncthreads();
-    // ---- slot Y(t)
-    if (t + 2 < n_kt) load_k(t + 2);
-    if (t + 1 < n_kt) load_v(t + 1);
+    // Retire the Q loads here.  Left pending, they would make the first MFMA that
+    // reads Q wait on the vector-memory counter, which then also counts the tile
+    // loads in flight.
+  #pragma unroll
+    for (int kb = 0; kb < NK; ++kb) asm volatile("" ::"v"(qf[kb]));
+    // slot Y(-1): load K(1), V(0); group 0 computes S(0)
+    if (n_kt > 1) load_k(1);
+    load_v(0);
     if (group == 0) {
       __builtin_amdgcn_s_setprio(1);
-      if (t + 1 < n_w) {
-        pv_qk(t, t + 1);
-      } else if (t < n_w) {
-        pv(t);
-      }
+      qk(0);
       __builtin_amdgcn_s_setprio(0);
-    } else {
-      if (t < n_w) sm(t);
     }
+    __syncthreads();
+    for (int t = 0; t < n_kt; ++t) {
+      // ---- slot X(t)
+      if (group == 0) {
+        if (t < n_w) sm(t);
+      } else {
+        __builtin_amdgcn_s_setprio(1);
+        if (t >= 1 && t < n_w) {
+          pv_qk(t - 1, t);
+        } else {
+          if (t >= 1 && t - 1 < n_w) pv(t - 1);
+          if (t < n_w) qk(t);
+        }
+        __builtin_amdgcn_s_setprio(0);
+      }
+      loads_landed();  // K(t+1), V(t)
+      __syncthreads();
+      // ---- slot Y(t)
+      if (t + 2 < n_kt) load_k(t + 2);
+      if (t + 1 < n_kt) load_v(t + 1);
+      if (group == 0) {
+        __builtin_amdgcn_s_setprio(1);
+        if (t + 1 < n_w) {
+          pv_qk(t, t + 1);
+        } else if (t < n_w) {
+          pv(t);
+        }
+        __builtin_amdgcn_s_setprio(0);
+      } else {
+        if (t < n_w) sm(t);
+      }
+    }
+    // slot X(n_kt): group 1 finishes the last PV
+    if (group == 1 && n_kt - 1 < n_w) pv(n_kt - 1);
+  } else {
+    // the same schedule from tile t0, each wave computing from its own tile tw0
+    load_k(t0);
+    loads_landed();
+    __syncthreads();
+#pragma unroll
+    for (int kb = 0; kb < NK; ++kb) asm volatile("" ::"v"(qf[kb]));
+    if (t0 + 1 < n_kt) load_k(t0 + 1);
+    load_v(t0);
+    if (group == 0 && act(t0)) {
+      __builtin_amdgcn_s_setprio(1);
+      qk(t0);
+      __builtin_amdgcn_s_setprio(0);
+    }
+    __syncthreads();
+    for (int t = t0; t < n_kt; ++t) {
+      // ---- slot X(t)
+      if (group == 0) {
+        if (act(t)) sm(t);
+      } else {
+        __builtin_amdgcn_s_setprio(1);
+        if (t > t0 && act(t - 1) && act(t)) {
+          pv_qk(t - 1, t);
+        } else {
+          if (t > t0 && act(t - 1)) pv(t - 1);
+          if (act(t)) qk(t);
+        }
+        __builtin_amdgcn_s_setprio(0);
+      }
+      loads_landed();  // K(t+1), V(t)
+      __syncthreads();
+      // ---- slot Y(t)
+      if (t + 2 < n_kt) load_k(t + 2);
+      if (t + 1 < n_kt) load_v(t + 1);
+      if (group == 0) {
+        __builtin_amdgcn_s_setprio(1);
+        if (act(t) && act(t + 1)) {
+          pv_qk(t, t + 1);
+        } else {
+          if (act(t)) pv(t);
+          if (act(t + 1)) qk(t + 1);
+        }
+        __builtin_amdgcn_s_setprio(0);
+      } else {
+        if (act(t)) sm(t);
+      }
+    }
+    if (group == 1 && act(n_kt - 1)) pv(n_kt - 1);
   }
-  // slot X(n_kt): group 1 finishes the last PV
-  if (group == 1 && n_kt - 1 < n_w) pv(n_kt - 1);
 
   // ---- epilogue: O / l, logsumexp --------------------------------------------------
   const float l_tot = sum_halves(l_run);
@@ -504,11 +584,16 @@ __global__ __launch_bounds__(256) void attn_fwd_f32(const float* __restrict__ Q,
 }
 
 template <typename T, int D, bool C>
-const void* mfma_fn() {
-  return (const void*)attn_fwd_mfma<T, D, C>;
+const void* mfma_fn(bool local) {
+  if constexpr (C) {
+    if (local) return (const void*)attn_fwd_mfma<T, D, true, true>;
+  }
+  return (const void*)attn_fwd_mfma<T, D, C, false>;
 }
 
-const void* pick_attn(Elem elem, int d, bool causal, int* threads, int* rows_per_block) {
+// local = the causal sliding-window / document variant (requires causal)
+const void* pick_attn(Elem elem, int d, bool causal, int* threads, int* rows_per_block,
+                      bool local = false) {
   if (elem == Elem::f32) {
     *threads = 256;
     *rows_per_block = 4 * (64 / (d / 64));
@@ -518,11 +603,11 @@ const void* pick_attn(Elem elem, int d, bool causal, int* threads, int* rows_per
   *threads = kThreads;
   *rows_per_block = kBM;
   if (elem == Elem::bf16) {
-    if (d == 64) return causal ? mfma_fn<__bf16, 64, true>() : mfma_fn<__bf16, 64, false>();
-    return causal ? mfma_fn<__bf16, 128, true>() : mfma_fn<__bf16, 128, false>();
+    if (d == 64) return causal ? mfma_fn<__bf16, 64, true>(local) : mfma_fn<__bf16, 64, false>(false);
+    return causal ? mfma_fn<__bf16, 128, true>(local) : mfma_fn<__bf16, 128, false>(false);
   }
-  if (d == 64) return causal ? mfma_fn<_Float16, 64, true>() : mfma_fn<_Float16, 64, false>();
-  return causal ? mfma_fn<_Float16, 128, true>() : mfma_fn<_Float16, 128, false>();
+  if (d == 64) return causal ? mfma_fn<_Float16, 64, true>(local) : mfma_fn<_Float16, 64, false>(false);
+  return causal ? mfma_fn<_Float16, 128, true>(local) : mfma_fn<_Float16, 128, false>(false);
 }
 
 }  // namespace
@@ -542,8 +627,27 @@ hipError_t launch_attn_fwd(Elem elem, const void* q, const void* k, const void* 
     return hipLaunchKernel(fn, dim3(grid), dim3(threads), args, 0, stream);
   }
   int xcd_groups = (BH % 8 == 0) ? 1 : 0;
+  const int* doc_start = nullptr;
+  int window = 0;
   void* args[] = {(void*)&q, (void*)&k, (void*)&v, (void*)&o, (void*)&lse, (void*)&BH,
-                  (void*)&N, (void*)&n_mtiles, (void*)&c, (void*)&xcd_groups};
+                  (void*)&N, (void*)&n_mtiles, (void*)&c, (void*)&xcd_groups, (void*)&H,
+                  (void*)&doc_start, (void*)&window};
+  return hipLaunchKernel(fn, dim3(grid), dim3(threads), args, 0, stream);
+}
+
+hipError_t launch_attn_fwd_local(Elem elem, const void* q, const void* k, const void* v, void* o,
+                                 float* lse, const int* doc_start, int window, int B, int H, int N,
+                                 int d, float scale, hipStream_t stream) {
+  int threads, rows_per_block;
+  const void* fn = pick_attn(elem, d, true, &threads, &rows_per_block, true);
+  int BH = B * H;
+  int n_mtiles = (N + rows_per_block - 1) / rows_per_block;
+  float c = scale * kLog2e;
+  const int grid = BH * n_mtiles;
+  int xcd_groups = (BH % 8 == 0) ? 1 : 0;
+  void* args[] = {(void*)&q, (void*)&k, (void*)&v, (void*)&o, (void*)&lse, (void*)&BH,
+                  (void*)&N, (void*)&n_mtiles, (void*)&c, (void*)&xcd_groups, (void*)&H,
+                  (void*)&doc_start, (void*)&window};
   return hipLaunchKernel(fn, dim3(grid), dim3(threads), args, 0, stream);
 }
 

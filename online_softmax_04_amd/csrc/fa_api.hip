@@ -26,7 +26,8 @@ uint64_t tensor_bytes(int B, int H, int N, int d, uint64_t elem) {
 }
 
 int attn_entry(osm::Elem elem, const void* q, const void* k, const void* v, void* o, float* lse,
-               int B, int H, int N, int d, float scale, int causal, hipStream_t stream) {
+               int B, int H, int N, int d, float scale, int causal, hipStream_t stream,
+               bool local = false, const int* doc_start = nullptr, int window = 0) {
   if (!q || !k || !v || !o) return FA_ERR_INVALID_ARG;
   if (B < 1 || H < 1 || N < 1 || d < 1) return FA_ERR_INVALID_ARG;
   if (!std::isfinite(scale) || !(scale > 0.f)) return FA_ERR_INVALID_ARG;
@@ -49,6 +50,20 @@ int attn_entry(osm::Elem elem, const void* q, const void* k, const void* v, void
   if (lse && (overlaps(lse, lse_bytes, o, bytes) || overlaps(lse, lse_bytes, q, bytes) ||
               overlaps(lse, lse_bytes, k, bytes) || overlaps(lse, lse_bytes, v, bytes)))
     return FA_ERR_INVALID_ARG;
+  if (local) {
+    if (window < 0) return FA_ERR_INVALID_ARG;
+    if (doc_start) {
+      if (!aligned(doc_start, 4)) return FA_ERR_ALIGNMENT;
+      const uint64_t doc_bytes = tensor_bytes(B, N, 1, 1, 4);
+      if (doc_bytes == 0) return FA_ERR_INVALID_ARG;
+      if (overlaps(doc_start, doc_bytes, o, bytes) ||
+          (lse && overlaps(doc_start, doc_bytes, lse, lse_bytes)))
+        return FA_ERR_INVALID_ARG;
+    }
+    hipError_t e = osm::launch_attn_fwd_local(elem, q, k, v, o, lse, doc_start, window, B, H, N, d,
+                                              scale, stream);
+    return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+  }
   hipError_t e = osm::launch_attn_fwd(elem, q, k, v, o, lse, B, H, N, d, scale, causal != 0, stream);
   if (e != hipSuccess) return FA_ERR_HIP;
   return FA_OK;
@@ -109,6 +124,20 @@ int fa_fwd_f16(const void* q, const void* k, const void* v, void* o, float* lse,
 int fa_fwd_f32(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
                int N, int d, float scale, int causal, hipStream_t stream) {
   return attn_entry(osm::Elem::f32, q, k, v, o, lse, B, H, N, d, scale, causal, stream);
+}
+
+int fa_fwd_local(const void* q, const void* k, const void* v, void* o, float* lse,
+                 const int* doc_start, int window, int B, int H, int N, int d, float scale,
+                 hipStream_t stream) {
+  return attn_entry(osm::Elem::bf16, q, k, v, o, lse, B, H, N, d, scale, 1, stream, true, doc_start,
+                    window);
+}
+
+int fa_fwd_local_f16(const void* q, const void* k, const void* v, void* o, float* lse,
+                     const int* doc_start, int window, int B, int H, int N, int d, float scale,
+                     hipStream_t stream) {
+  return attn_entry(osm::Elem::f16, q, k, v, o, lse, B, H, N, d, scale, 1, stream, true, doc_start,
+                    window);
 }
 
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,

@@ -13,6 +13,11 @@ hipError_t launch_attn_fwd(Elem elem, const void* q, const void* k, const void* 
                            hipStream_t stream);
 hipError_t attn_fwd_attributes(Elem elem, int d, bool causal, hipFuncAttributes* attr,
                                int* threads, int* blocks_per_cu);
+// Causal attention where query i also skips keys before max(doc_start[b, i], i - window + 1)
+// (doc_start may be null, window 0 = unbounded); bf16 / fp16 only.
+hipError_t launch_attn_fwd_local(Elem elem, const void* q, const void* k, const void* v, void* o,
+                                 float* lse, const int* doc_start, int window, int B, int H, int N,
+                                 int d, float scale, hipStream_t stream);
 
 // Attention backward (bf16 / fp16): dQ and D into `workspace` ([B, H, N] fp32),
 // then dK and dV; arguments already validated by the C ABI layer.

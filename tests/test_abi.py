@@ -28,7 +28,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ("fa_fwd", "fa_fwd_f16", "fa_fwd_f32", "fa_bwd", "fa_bwd_f16", "fa_bwd_workspace_bytes",
+    for n in ("fa_fwd", "fa_fwd_f16", "fa_fwd_f32", "fa_fwd_local", "fa_fwd_local_f16", "fa_bwd",
+              "fa_bwd_f16", "fa_bwd_workspace_bytes",
               "online_softmax_rows", "fa_status_string", "fa_kernel_attributes"):
         assert n in names
 
@@ -105,6 +106,27 @@ def test_attn_alignment(name, kw):
                                 dict(lse=A + 192 * MB + 16), dict(lse=A)])
 def test_attn_overlap(name, kw):
     assert call_attn(name, **kw) == fa.FA_ERR_INVALID_ARG
+
+
+def call_local(name="fa_fwd_local", doc=A + 320 * MB, window=16, **kw):
+    base = dict(q=A, k=A + 64 * MB, v=A + 128 * MB, o=A + 192 * MB, lse=A + 256 * MB, B=1, H=2,
+                N=128, d=64, scale=0.125)
+    base.update(kw)
+    fn = getattr(fa.lib(), name)
+    return fn(base["q"], base["k"], base["v"], base["o"], base["lse"], doc, window, base["B"],
+              base["H"], base["N"], base["d"], base["scale"], None)
+
+
+@pytest.mark.parametrize("name", ["fa_fwd_local", "fa_fwd_local_f16"])
+@pytest.mark.parametrize("kw,status", [
+    (dict(window=-1), fa.FA_ERR_INVALID_ARG), (dict(q=0), fa.FA_ERR_INVALID_ARG),
+    (dict(N=0), fa.FA_ERR_INVALID_ARG), (dict(scale=0.0), fa.FA_ERR_INVALID_ARG),
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED), (dict(doc=A + 320 * MB + 2), fa.FA_ERR_ALIGNMENT),
+    (dict(doc=A + 192 * MB), fa.FA_ERR_INVALID_ARG), (dict(doc=A + 256 * MB + 64), fa.FA_ERR_INVALID_ARG),
+    (dict(o=A + 16), fa.FA_ERR_INVALID_ARG),
+])
+def test_local_validation(name, kw, status):
+    assert call_local(name, **kw) == status
 
 
 # backward: ten buffers, 64 MiB apart (each [1, 2, 128, 64] 16-bit tensor is 32 KiB)

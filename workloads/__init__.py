@@ -204,6 +204,38 @@ def attn_sample_rows(w: AttnWorkload, b: int, h: int, count: int | None = None) 
     return np.array(sorted(rows), dtype=np.int64)
 
 
+def packed_doc_starts(B: int, N: int, seed: int, min_len: int, max_len: int) -> np.ndarray:
+    """[B, N] int32: for each position, the first position of its document, for rows
+    packed with documents of seeded lengths uniform in [min_len, max_len] (the
+    last one cut at N)."""
+    rng = np.random.default_rng([BASE_SEED + 800, seed, B, N])
+    out = np.empty((B, N), np.int32)
+    for b in range(B):
+        p = 0
+        while p < N:
+            ln = int(rng.integers(min_len, max_len + 1))
+            out[b, p:p + ln] = p
+            p += ln
+    return out
+
+
+# sliding-window / packed-document forward: the B8 H32 N8192 d128 causal shape with
+# a 1024-key window over documents of 512 to 4096 tokens (K rows x U(0.5, 2) as the
+# dense workload)
+LOCAL_WORKLOAD = dict(name="attn_bf16_b8h32n8192_w1024_docs", base="attn_bf16_b8h32n8192_causal",
+                      window=1024, doc_min=512, doc_max=4096, doc_seed=5)
+
+
+def local_ranges(doc_start_row: np.ndarray, window: int) -> tuple[np.ndarray, np.ndarray]:
+    """(lo, hi) of every query of one batch row: keys max(doc start, i - window + 1) .. i."""
+    n = doc_start_row.shape[0]
+    i = np.arange(n, dtype=np.int64)
+    lo = doc_start_row.astype(np.int64)
+    if window > 0:
+        lo = np.maximum(lo, i - window + 1)
+    return np.clip(lo, 0, i), i
+
+
 # --------------------------------------------------------------------------
 # softmax inputs
 # --------------------------------------------------------------------------
