@@ -15,6 +15,10 @@ Prints ONE JSON line:
               it was taken on the current kernel source;
   cpu_baseline  the fp64 oracle timed on this host's cores over a bounded
               sample of query rows of the same workload.
+  After the timed steps, beside them: the backward (fa_bwd) on the same
+  inputs, the forward with a sliding window over packed documents
+  (fa_fwd_local, FLOP over visible pairs), and the split-row softmax over
+  4 rows of 2^24 columns (GB/s at 8 bytes per element; it moves 12).
 
 Other modes:
   --ingest-counters DIR_FETCH DIR_WRITE   turn two rocprofv3 --pmc runs
@@ -39,6 +43,7 @@ sys.path.insert(0, ROOT)
 METRIC = "attn fwd TFLOP/s at B=8,H=32,N=8192,d=128 bf16 + % MFMA peak; softmax GB/s"
 ATTN_WORKLOAD = "attn_bf16_b8h32n8192_causal"
 SOFTMAX_WORKLOAD = "softmax_4096x32768"
+SPLIT_WORKLOAD = "softmax_split_4x16777216"
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBPS = 8000.0         # MI355X HBM3E, published
 COPY_BYTES = 256 << 20         # probe copy kernel: 256 MiB read + 256 MiB written
@@ -472,6 +477,36 @@ def main():
     loc_tflops = loc_flop / (loc_ms * 1e-3) / 1e12
     print(f"[bench] local {loc_ms:.3f} ms", file=sys.stderr, flush=True)
 
+    # Split-row softmax on few very long rows (several workgroups per row), and
+    # the one-workgroup-per-row path on the same input for comparison.
+    spw = workloads.SOFTMAX[SPLIT_WORKLOAD]
+    spx = torch.from_numpy(workloads.softmax_input(spw, threads=4)).to(dev)
+    spy = torch.empty_like(spx)
+    sp_wsb = fa.online_softmax_split_workspace_bytes(spw.rows, spw.cols)
+    sp_ws = torch.empty(sp_wsb // 4, dtype=torch.float32, device=dev)
+
+    def split():
+        fa.online_softmax_rows_split(spx, spy, spw.rows, spw.cols, sp_ws, sp_wsb, stream)
+
+    def timed(fn, steps):
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+        for i in range(steps):
+            ev[i][0].record(stream)
+            fn()
+            ev[i][1].record(stream)
+        torch.cuda.synchronize()
+        return sorted(e[0].elapsed_time(e[1]) for e in ev)
+
+    for _ in range(args.warmup):
+        split()
+    sp_each = timed(split, args.steps)
+    sp_ms = sum(sp_each) / args.steps
+    sp_gbps = spw.algorithmic_bytes / (sp_ms * 1e-3) / 1e9
+    unsplit_each = timed(lambda: fa.online_softmax_rows(spx, spy, spw.rows, spw.cols, stream), 2)
+    unsplit_gbps = spw.algorithmic_bytes / (unsplit_each[0] * 1e-3) / 1e9
+    del spx, spy
+    print(f"[bench] split softmax {sp_ms * 1e3:.1f} us", file=sys.stderr, flush=True)
+
     tflops = w.flops / (attn_ms * 1e-3) / 1e12
     sm_bytes = sw.algorithmic_bytes
     sm_gbps = sm_bytes / (sm_ms * 1e-3) / 1e9
@@ -527,6 +562,17 @@ def main():
                                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                                "frac": round(loc_tflops / PEAK_BF16_TFLOPS, 4),
                                "kernel": "attn_fwd_mfma<bf16,128,causal,local>"}},
+        "softmax_split": {"workload": spw.name, "value": round(sp_gbps, 1), "unit": "GB/s",
+                          "bytes_per_launch": spw.algorithmic_bytes,
+                          "bytes_moved_per_launch": 12 * spw.rows * spw.cols,
+                          "avg_launch_us": round(sp_ms * 1e3, 2),
+                          "median_launch_us": round(sp_each[len(sp_each) // 2] * 1e3, 2),
+                          "one_workgroup_per_row_gbps": round(unsplit_gbps, 1),
+                          "roofline": {"bound": "hbm", "achieved": round(sp_gbps, 1),
+                                       "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                                       "frac": round(sp_gbps / PEAK_HBM_GBPS, 4),
+                                       "kernels": ["softmax_split_partials<512,true>",
+                                                   "softmax_split_normalise<512,true>"]}},
         "kernel_resources": {"attention": attrs, "softmax": sm_attrs,
                              "backward_dq": fa.kernel_attributes(fa.OP_FA_BWD_DQ, w.d, True),
                              "backward_dkdv": fa.kernel_attributes(fa.OP_FA_BWD_DKDV, w.d, True)},

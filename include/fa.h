@@ -23,7 +23,8 @@
  *    the sum of exponentials gathered in one fused pass and merged across
  *    threads by the associative (m, d) rule of the infra-guide page
  *    "5.2 CUDA Online Softmax" (sections 2.1 and 4.2), then one normalise
- *    pass.
+ *    pass.  online_softmax_rows_split spreads each row over several
+ *    workgroups for few, very long rows.
  *
  * Conventions shared by every entry point
  *  - All tensor pointers are DEVICE pointers owned by the caller; the library
@@ -162,6 +163,31 @@ size_t fa_bwd_workspace_bytes(int B, int H, int N);
  *  or unaligned rows take a two-read path.  Inputs must be finite.
  */
 int online_softmax_rows(const float* x, float* y, int rows, int cols, hipStream_t stream);
+
+/*
+ * Row softmax for few, very long rows: the same result as online_softmax_rows,
+ * with each row cut into chunks that separate workgroups reduce to a partial
+ * (maximum, sum) pair, which are then merged with the associative rescaling
+ * rule.  Follows the infra-guide page "5.2 CUDA Online Softmax": the merge of
+ * two partial results (section 4.1) and its remark that a tiny row count with
+ * huge rows needs several blocks per row in a two-phase launch (section 7.1).  Phase 1 writes one (m, l) pair per chunk to `workspace`;
+ * phase 2 merges the row's pairs in every workgroup and normalises its chunk.
+ * Each element is read twice and written once (12 bytes per element); no
+ * workgroup waits on another.
+ *
+ *  x, y       as for online_softmax_rows (y must not overlap x).
+ *  workspace  device memory of at least online_softmax_split_workspace_bytes
+ *             (rows, cols) bytes, 8-byte aligned, overlapping neither x nor
+ *             y; owned by the caller, contents on entry ignored, scratch on
+ *             exit.  Calls that share a workspace must be ordered (the same
+ *             stream does that).
+ *  workspace_bytes  its size; a smaller value returns FA_ERR_INVALID_ARG.
+ *  Chunks hold at least 4096 columns and the launch aims at about 2048
+ *  workgroups; rows * chunks must fit in a 31-bit grid.  Inputs must be finite.
+ */
+size_t online_softmax_split_workspace_bytes(int rows, int cols);
+int online_softmax_rows_split(const float* x, float* y, int rows, int cols, float* workspace,
+                              size_t workspace_bytes, hipStream_t stream);
 
 /* Static description of an fa_status value (never NULL). */
 const char* fa_status_string(int status);

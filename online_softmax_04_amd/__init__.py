@@ -15,6 +15,7 @@ import os
 
 __all__ = [
     "FaError", "lib", "fa_fwd", "fa_fwd_f16", "fa_fwd_f32", "online_softmax_rows",
+    "online_softmax_rows_split", "online_softmax_split_workspace_bytes", "softmax_split",
     "fa_status_string", "kernel_attributes", "attention", "softmax", "LIB_PATH",
     "FA_OK", "FA_ERR_INVALID_ARG", "FA_ERR_UNSUPPORTED", "FA_ERR_ALIGNMENT", "FA_ERR_HIP",
 ]
@@ -71,6 +72,10 @@ def lib() -> ctypes.CDLL:
         L.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
         L.online_softmax_rows.argtypes = [vp, vp, i, i, vp]
         L.online_softmax_rows.restype = i
+        L.online_softmax_split_workspace_bytes.argtypes = [i, i]
+        L.online_softmax_split_workspace_bytes.restype = ctypes.c_size_t
+        L.online_softmax_rows_split.argtypes = [vp, vp, i, i, vp, ctypes.c_size_t, vp]
+        L.online_softmax_rows_split.restype = i
         L.fa_status_string.argtypes = [i]
         L.fa_status_string.restype = ctypes.c_char_p
         L.fa_kernel_attributes.argtypes = [i, i, i, ctypes.POINTER(_Attrs)]
@@ -173,6 +178,18 @@ def online_softmax_rows(x, y, rows, cols, stream=None):
            "online_softmax_rows")
 
 
+def online_softmax_split_workspace_bytes(rows, cols) -> int:
+    """Bytes of workspace online_softmax_rows_split needs (0 for invalid sizes)."""
+    return int(lib().online_softmax_split_workspace_bytes(int(rows), int(cols)))
+
+
+def online_softmax_rows_split(x, y, rows, cols, workspace, workspace_bytes, stream=None):
+    """Row softmax with each row spread over several workgroups (see include/fa.h)."""
+    _check(lib().online_softmax_rows_split(_ptr(x), _ptr(y), int(rows), int(cols), _ptr(workspace),
+                                           int(workspace_bytes), _stream(stream)),
+           "online_softmax_rows_split")
+
+
 def kernel_attributes(op: int, d: int, causal: bool = False) -> dict:
     """Registers, LDS, spill bytes, block size and occupancy of the kernel an op launches."""
     a = _Attrs()
@@ -251,4 +268,20 @@ def softmax(x, out=None, stream=None):
     if out is None:
         out = torch.empty_like(x)
     online_softmax_rows(x, out, x.shape[0], x.shape[1], stream)
+    return out
+
+
+def softmax_split(x, out=None, stream=None):
+    """Row softmax of a contiguous fp32 [rows, cols] device tensor, each row spread
+    over several workgroups (for few, very long rows)."""
+    import torch
+    if not isinstance(x, torch.Tensor) or x.device.type != "cuda" or x.dtype != torch.float32:
+        raise TypeError("x must be an fp32 device tensor")
+    if x.dim() != 2 or not x.is_contiguous():
+        raise ValueError("x must be a contiguous [rows, cols] tensor")
+    if out is None:
+        out = torch.empty_like(x)
+    nbytes = online_softmax_split_workspace_bytes(x.shape[0], x.shape[1])
+    ws = torch.empty(max(1, nbytes // 4), dtype=torch.float32, device=x.device)
+    online_softmax_rows_split(x, out, x.shape[0], x.shape[1], ws, nbytes, stream)
     return out

@@ -172,6 +172,35 @@ int online_softmax_rows(const float* x, float* y, int rows, int cols, hipStream_
   return FA_OK;
 }
 
+size_t online_softmax_split_workspace_bytes(int rows, int cols) {
+  if (rows < 1 || cols < 1) return 0;
+  int chunk, nchunks;
+  osm::softmax_split_plan(rows, cols, &chunk, &nchunks);
+  return (size_t)tensor_bytes(rows, nchunks, 1, 1, 8);
+}
+
+int online_softmax_rows_split(const float* x, float* y, int rows, int cols, float* workspace,
+                              size_t workspace_bytes, hipStream_t stream) {
+  if (!x || !y || !workspace) return FA_ERR_INVALID_ARG;
+  if (rows < 1 || cols < 1) return FA_ERR_INVALID_ARG;
+  const uint64_t bytes = tensor_bytes(rows, cols, 1, 1, 4);
+  if (bytes == 0) return FA_ERR_INVALID_ARG;
+  int chunk, nchunks;
+  osm::softmax_split_plan(rows, cols, &chunk, &nchunks);
+  const uint64_t ws = tensor_bytes(rows, nchunks, 1, 1, 8);
+  // one workgroup per (row, chunk) must fit a 1-D grid
+  if (ws == 0 || (uint64_t)rows * (uint64_t)nchunks > (uint64_t)INT_MAX) return FA_ERR_INVALID_ARG;
+  if ((uint64_t)workspace_bytes < ws) return FA_ERR_INVALID_ARG;
+  if (!aligned(x, 4) || !aligned(y, 4) || !aligned(workspace, 8)) return FA_ERR_ALIGNMENT;
+  if (overlaps(x, bytes, y, bytes) || overlaps(workspace, ws, x, bytes) ||
+      overlaps(workspace, ws, y, bytes))
+    return FA_ERR_INVALID_ARG;
+  const bool vec_ok = aligned(x, 16) && aligned(y, 16) && (cols % 4 == 0);
+  hipError_t e = osm::launch_softmax_split(x, y, rows, cols, vec_ok, workspace, stream);
+  if (e != hipSuccess) return FA_ERR_HIP;
+  return FA_OK;
+}
+
 const char* fa_status_string(int status) {
   switch (status) {
     case FA_OK: return "FA_OK: success";

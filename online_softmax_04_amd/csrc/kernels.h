@@ -34,5 +34,10 @@ hipError_t launch_softmax(const float* x, float* y, int rows, int cols, bool vec
                           hipStream_t stream);
 hipError_t softmax_attributes(int cols, bool vec_ok, hipFuncAttributes* attr, int* threads,
                               int* blocks_per_cu);
+// Split path: chunk length and chunks per row; then the two passes with
+// rows * nchunks (m, l) pairs in `workspace`.
+void softmax_split_plan(int rows, int cols, int* chunk, int* nchunks);
+hipError_t launch_softmax_split(const float* x, float* y, int rows, int cols, bool vec_ok,
+                                float* workspace, hipStream_t stream);
 
 }  // namespace osm

@@ -162,6 +162,80 @@ __global__ __launch_bounds__(THREADS) void softmax_stream(const float* __restric
   }
 }
 
+// ---- split rows: several workgroups per row (few rows, very long rows) -----------
+// Pass 1: workgroup (row, chunk) reduces its chunk to (m, l) with the per-chunk
+// online recurrence.  Pass 2: each workgroup of the row merges the row's chunk
+// pairs with the associative rule, then re-reads its chunk and normalises it.
+// No workgroup waits on another inside a kernel; the kernel boundary orders the
+// passes.  12 bytes per element move (two reads, one write).
+template <int THREADS, bool VEC>
+__device__ __forceinline__ void chunk_ml(const float* __restrict__ xr, int j0, int j1, float& m,
+                                         float& l) {
+  const int t = threadIdx.x;
+  m = kNegInf;
+  l = 0.f;
+  if constexpr (VEC) {
+    const f32x4* x4 = reinterpret_cast<const f32x4*>(xr);
+    for (int idx = (j0 >> 2) + t; idx < (j1 >> 2); idx += THREADS) {
+      const f32x4 v = x4[idx];  // cached: pass 2 reads it again
+      const float mn = fmaxf(m, max4(v));
+      const f32x4 e = (v - mn) * kLog2e;
+      l = l * exp2_fast((m - mn) * kLog2e) +
+          (exp2_fast(e.x) + exp2_fast(e.y)) + (exp2_fast(e.z) + exp2_fast(e.w));
+      m = mn;
+    }
+  } else {
+    for (int j = j0 + t; j < j1; j += THREADS) {
+      const float v = xr[j];
+      const float mn = fmaxf(m, v);
+      l = l * exp2_fast((m - mn) * kLog2e) + exp2_fast((v - mn) * kLog2e);
+      m = mn;
+    }
+  }
+  block_merge<THREADS>(m, l);
+}
+
+template <int THREADS, bool VEC>
+__global__ __launch_bounds__(THREADS) void softmax_split_partials(const float* __restrict__ x,
+                                                                  float2* __restrict__ part,
+                                                                  int cols, int chunk, int nchunks) {
+  const int row = blockIdx.x / nchunks, c = blockIdx.x - row * nchunks;
+  const int j0 = c * chunk, j1 = min(cols, j0 + chunk);
+  float m, l;
+  chunk_ml<THREADS, VEC>(x + (size_t)row * cols, j0, j1, m, l);
+  if (threadIdx.x == 0) part[blockIdx.x] = make_float2(m, l);
+}
+
+template <int THREADS, bool VEC>
+__global__ __launch_bounds__(THREADS) void softmax_split_normalise(const float* __restrict__ x,
+                                                                   float* __restrict__ y,
+                                                                   const float2* __restrict__ part,
+                                                                   int cols, int chunk, int nchunks) {
+  const int row = blockIdx.x / nchunks, c = blockIdx.x - row * nchunks;
+  const int t = threadIdx.x;
+  float m = kNegInf, l = 0.f;
+  for (int i = t; i < nchunks; i += THREADS) {
+    const float2 p = part[(size_t)row * nchunks + i];
+    merge_ml(m, l, p.x, p.y);
+  }
+  block_merge<THREADS>(m, l);
+  const float inv = 1.f / l;
+  const int j0 = c * chunk, j1 = min(cols, j0 + chunk);
+  const float* xr = x + (size_t)row * cols;
+  float* yr = y + (size_t)row * cols;
+  if constexpr (VEC) {
+    const f32x4* x4 = reinterpret_cast<const f32x4*>(xr);
+    f32x4* y4 = reinterpret_cast<f32x4*>(yr);
+    for (int idx = (j0 >> 2) + t; idx < (j1 >> 2); idx += THREADS) {
+      const f32x4 e = (__builtin_nontemporal_load(x4 + idx) - m) * kLog2e;
+      const f32x4 o = f32x4{exp2_fast(e.x), exp2_fast(e.y), exp2_fast(e.z), exp2_fast(e.w)} * inv;
+      __builtin_nontemporal_store(o, y4 + idx);
+    }
+  } else {
+    for (int j = j0 + t; j < j1; j += THREADS) yr[j] = exp2_fast((xr[j] - m) * kLog2e) * inv;
+  }
+}
+
 struct CachedConfig {
   int capacity;  // columns
   const void* fn;
@@ -203,6 +277,40 @@ hipError_t launch_softmax(const float* x, float* y, int rows, int cols, bool vec
   pick_softmax(cols, vec_ok, &fn, &threads);
   void* args[] = {(void*)&x, (void*)&y, (void*)&cols};
   return hipLaunchKernel(fn, dim3(rows), dim3(threads), args, 0, stream);
+}
+
+// Chunking of the split path: enough workgroups to fill the chip (about 2048 in
+// all), chunks of at least 4096 columns (two 16-byte vectors per lane), chunk
+// lengths a multiple of 4 so that every chunk of an aligned row starts 16-byte
+// aligned.
+void softmax_split_plan(int rows, int cols, int* chunk, int* nchunks) {
+  int64_t n = (2048 + (int64_t)rows - 1) / rows;
+  const int64_t by_len = ((int64_t)cols + 4095) / 4096;
+  if (n > by_len) n = by_len;
+  if (n < 1) n = 1;
+  int64_t ch = ((int64_t)cols + n - 1) / n;
+  ch = (ch + 3) & ~(int64_t)3;
+  *chunk = (int)ch;
+  *nchunks = (int)(((int64_t)cols + ch - 1) / ch);
+}
+
+hipError_t launch_softmax_split(const float* x, float* y, int rows, int cols, bool vec_ok,
+                                float* workspace, hipStream_t stream) {
+  int chunk, nchunks;
+  softmax_split_plan(rows, cols, &chunk, &nchunks);
+  constexpr int T = 512;
+  const void* f1 = vec_ok ? (const void*)softmax_split_partials<T, true>
+                          : (const void*)softmax_split_partials<T, false>;
+  const void* f2 = vec_ok ? (const void*)softmax_split_normalise<T, true>
+                          : (const void*)softmax_split_normalise<T, false>;
+  float2* part = reinterpret_cast<float2*>(workspace);
+  const float2* cpart = part;
+  const int grid = rows * nchunks;
+  void* a1[] = {(void*)&x, (void*)&part, (void*)&cols, (void*)&chunk, (void*)&nchunks};
+  hipError_t e = hipLaunchKernel(f1, dim3(grid), dim3(T), a1, 0, stream);
+  if (e != hipSuccess) return e;
+  void* a2[] = {(void*)&x, (void*)&y, (void*)&cpart, (void*)&cols, (void*)&chunk, (void*)&nchunks};
+  return hipLaunchKernel(f2, dim3(grid), dim3(T), a2, 0, stream);
 }
 
 hipError_t softmax_attributes(int cols, bool vec_ok, hipFuncAttributes* attr, int* threads,

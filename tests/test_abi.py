@@ -30,7 +30,8 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("fa_fwd", "fa_fwd_f16", "fa_fwd_f32", "fa_fwd_local", "fa_fwd_local_f16", "fa_bwd",
               "fa_bwd_f16", "fa_bwd_workspace_bytes",
-              "online_softmax_rows", "fa_status_string", "fa_kernel_attributes"):
+              "online_softmax_rows", "online_softmax_rows_split",
+              "online_softmax_split_workspace_bytes", "fa_status_string", "fa_kernel_attributes"):
         assert n in names
 
 
@@ -199,6 +200,42 @@ def call_softmax(x=A, y=A + 64 * MB, rows=4, cols=100):
 ])
 def test_softmax_validation(kw, status):
     assert call_softmax(**kw) == status
+
+
+def test_split_workspace_bytes():
+    # 4096-column chunks at least, about 2048 workgroups in all, 8 bytes per chunk
+    assert fa.online_softmax_split_workspace_bytes(1, 1) == 8
+    assert fa.online_softmax_split_workspace_bytes(1, 4096) == 8
+    assert fa.online_softmax_split_workspace_bytes(1, 4097) == 16
+    assert fa.online_softmax_split_workspace_bytes(4, 1 << 24) == 4 * 512 * 8
+    assert fa.online_softmax_split_workspace_bytes(3000, 1 << 20) == 3000 * 8
+    assert fa.online_softmax_split_workspace_bytes(0, 100) == 0
+    assert fa.online_softmax_split_workspace_bytes(5, -1) == 0
+
+
+WS = A + 128 * MB
+
+
+def call_split(x=A, y=A + 64 * MB, rows=4, cols=100, ws=WS, wsb=None):
+    if wsb is None:
+        wsb = fa.online_softmax_split_workspace_bytes(4, 100)
+    return fa.lib().online_softmax_rows_split(x, y, rows, cols, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=0), fa.FA_ERR_INVALID_ARG), (dict(y=0), fa.FA_ERR_INVALID_ARG),
+    (dict(ws=0), fa.FA_ERR_INVALID_ARG),
+    (dict(rows=0), fa.FA_ERR_INVALID_ARG), (dict(cols=0), fa.FA_ERR_INVALID_ARG),
+    (dict(rows=1 << 30, cols=1 << 30), fa.FA_ERR_INVALID_ARG),
+    (dict(wsb=31), fa.FA_ERR_INVALID_ARG),
+    (dict(cols=5000), fa.FA_ERR_INVALID_ARG),          # needs two chunks a row: 64 bytes
+    (dict(x=A + 2), fa.FA_ERR_ALIGNMENT), (dict(y=A + 64 * MB + 1), fa.FA_ERR_ALIGNMENT),
+    (dict(ws=WS + 4), fa.FA_ERR_ALIGNMENT),
+    (dict(y=A + 1200), fa.FA_ERR_INVALID_ARG), (dict(ws=A + 1592), fa.FA_ERR_INVALID_ARG),
+    (dict(ws=A + 64 * MB + 8), fa.FA_ERR_INVALID_ARG),
+])
+def test_split_validation(kw, status):
+    assert call_split(**kw) == status
 
 
 def test_python_wrappers_raise():

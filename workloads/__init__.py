@@ -132,6 +132,9 @@ ATTN = {
 SOFTMAX = {
     w.name: w for w in [
         SoftmaxWorkload("softmax_4096x32768", 4096, 32768, BASE_SEED + 2),
+        # few very long rows (one row per sequence of a batch of 4, 16M positions
+        # each); rarer spikes so that each spike carries a visible share (~1/170)
+        SoftmaxWorkload("softmax_split_4x16777216", 4, 1 << 24, BASE_SEED + 6, spike_prob=1e-5),
     ]
 }
 
