@@ -128,6 +128,36 @@ class Oracle:
                                          self._p(lse), threads or default_threads())
         return o, lse
 
+    def attention_decode(self, q, k, v, scale: float, causal: bool, dtype: str | None = None,
+                         threads: int | None = None):
+        """O [Nq, d] and LSE [Nq] of Nq queries against Nk keys, q [Nq, d], k and v [Nk, d].
+
+        The queries are the last Nq positions of the key sequence (decode and
+        chunked prefill: query i sits at position Nk - Nq + i); causal lets it
+        see keys 0 .. Nk - Nq + i (the causal rule of "Online Softmax: Tiling
+        Across a Reduction"), otherwise every key.  Written as the key-range
+        oracle over sequences padded to n = max(Nq, Nk) rows: the queries take
+        the last Nq rows, padded keys lie outside every range.
+        """
+        q, k, v = (self.to_f64(t, dtype) for t in (q, k, v))
+        nq, d = q.shape
+        nk = k.shape[0]
+        if k.shape != (nk, d) or v.shape != (nk, d) or nq < 1 or nk < 1:
+            raise ValueError("q [Nq, d], k and v [Nk, d] with Nq, Nk >= 1")
+        if causal and nq > nk:
+            raise ValueError("causal needs Nq <= Nk")
+        n = max(nq, nk)
+        rows = np.arange(n - nq, n, dtype=np.int64)
+        qf = np.zeros((n, d))
+        qf[rows] = q
+        kf, vf = np.zeros((n, d)), np.zeros((n, d))
+        kf[:nk], vf[:nk] = k, v
+        lo = np.zeros(n, np.int64)
+        hi = np.full(n, nk - 1, np.int64)
+        if causal:
+            hi[rows] = nk - nq + np.arange(nq)
+        return self.attention_ranged(qf, kf, vf, scale, lo, hi, rows, threads=threads)
+
     def attention(self, q, k, v, scale: float, causal: bool, rows_of=None,
                   dtype: str | None = None, threads: int | None = None):
         """[B, H, N, d] inputs; ``rows_of(b, h)`` picks the checked rows (default all).

@@ -349,6 +349,64 @@ def pin_ranged_single_key(orc):
 
 
 # ---------------------------------------------------------------------------
+# decode-shaped (Nq queries at the end of Nk keys) pins
+# ---------------------------------------------------------------------------
+def pin_decode_square_is_attention(orc):
+    """Nq = Nk: the decode form is plain attention, causal or not."""
+    r = _rng(60)
+    n, d = 23, 5
+    q, k, v = (r.normal(size=(n, d)) for _ in range(3))
+    for causal in (False, True):
+        o1, l1 = orc.attention_decode(q, k, v, 0.7, causal)
+        o2, l2 = orc.attention_head(q, k, v, 0.7, causal)
+        _close(o1, o2, 1e-14, f"square decode O causal={causal}")
+        _close(l1, l2, 1e-14, f"square decode LSE causal={causal}")
+
+
+def pin_decode_query_sees_a_prefix(orc):
+    """Causal, Nq < Nk: query i is one query over the keys 0 .. Nk - Nq + i."""
+    r = _rng(61)
+    nq, nk, d = 4, 19, 6
+    q = r.normal(size=(nq, d))
+    k, v = r.normal(size=(nk, d)), r.normal(size=(nk, d))
+    o, lse = orc.attention_decode(q, k, v, 0.5, True)
+    for i in range(nq):
+        m = nk - nq + i + 1
+        oi, li = orc.attention_head(np.tile(q[i], (m, 1)), k[:m], v[:m], 0.5, False, rows=[0])
+        _close(o[i], oi[0], 1e-14, f"prefix query {i}")
+        _close([lse[i]], li, 1e-14, f"prefix lse {i}")
+    on, _ = orc.attention_decode(q, k, v, 0.5, False)
+    _close(on[-1], o[-1], 1e-14, "the last query sees every key either way")
+    assert np.max(np.abs(on[0] - o[0])) > 1e-3, "the first query must not see the last keys"
+
+
+def pin_decode_uniform_scores(orc):
+    """q = 0: every visible key weighs the same, O is the mean of the visible V
+    rows and LSE = ln(count)."""
+    r = _rng(62)
+    nq, nk, d = 3, 10, 4
+    k, v = r.normal(size=(nk, d)), r.normal(size=(nk, d))
+    o, lse = orc.attention_decode(np.zeros((nq, d)), k, v, 1.3, True)
+    for i in range(nq):
+        cnt = nk - nq + i + 1
+        _close(o[i], v[:cnt].mean(axis=0), 1e-15, f"uniform O {i}")
+        _close([lse[i]], [math.log(cnt)], 1e-15, f"uniform LSE {i}")
+
+
+def pin_decode_more_queries_than_keys(orc):
+    """Non-causal with Nq > Nk (padding rows exist): each query sees the Nk keys only."""
+    r = _rng(63)
+    nq, nk, d = 9, 3, 4
+    q = r.normal(size=(nq, d))
+    k, v = r.normal(size=(nk, d)), r.normal(size=(nk, d))
+    o, lse = orc.attention_decode(q, k, v, 0.9, False)
+    s = 0.9 * q @ k.T
+    p = np.exp(s - s.max(axis=1, keepdims=True))
+    _close(o, (p / p.sum(axis=1, keepdims=True)) @ v, 1e-14, "few keys O")
+    _close(lse, s.max(axis=1) + np.log(p.sum(axis=1)), 1e-14, "few keys LSE")
+
+
+# ---------------------------------------------------------------------------
 # backward-pass pins
 # ---------------------------------------------------------------------------
 def _loss(orc, q, k, v, g, scale, causal):
