@@ -17,8 +17,10 @@ Prints ONE JSON line:
               sample of query rows of the same workload.
   After the timed steps, beside them: the backward (fa_bwd) on the same
   inputs, the forward with a sliding window over packed documents
-  (fa_fwd_local, FLOP over visible pairs), and the split-row softmax over
-  4 rows of 2^24 columns (GB/s at 8 bytes per element; it moves 12).
+  (fa_fwd_local, FLOP over visible pairs), the split-row softmax over
+  4 rows of 2^24 columns (GB/s at 8 bytes per element; it moves 12), and the
+  split-KV decode of one query per head against 32768 cached keys (GB/s of
+  K, V, Q, O and LSE moved once).
 
 Other modes:
   --ingest-counters DIR_FETCH DIR_WRITE   turn two rocprofv3 --pmc runs
@@ -44,6 +46,7 @@ METRIC = "attn fwd TFLOP/s at B=8,H=32,N=8192,d=128 bf16 + % MFMA peak; softmax 
 ATTN_WORKLOAD = "attn_bf16_b8h32n8192_causal"
 SOFTMAX_WORKLOAD = "softmax_4096x32768"
 SPLIT_WORKLOAD = "softmax_split_4x16777216"
+DECODE_WORKLOAD = "decode_bf16_b8h32_q1_kv32768_d128"
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBPS = 8000.0         # MI355X HBM3E, published
 COPY_BYTES = 256 << 20         # probe copy kernel: 256 MiB read + 256 MiB written
@@ -507,6 +510,30 @@ def main():
     del spx, spy
     print(f"[bench] split softmax {sp_ms * 1e3:.1f} us", file=sys.stderr, flush=True)
 
+    # Split-KV decode: one query per head against a 32768-key cache (HBM-bound: K and
+    # V are read once).
+    dw = workloads.DECODE[DECODE_WORKLOAD]
+    dq_h, dk_h, dv_h = workloads.decode_full(dw, threads=16)
+    dqd, dkd, dvd = (torch.from_numpy(t.view(np.int16)).view(torch.bfloat16).to(dev)
+                     for t in (dq_h, dk_h, dv_h))
+    del dq_h, dk_h, dv_h
+    dod = torch.empty_like(dqd)
+    dlse = torch.empty((dw.B, dw.H, dw.Nq), dtype=torch.float32, device=dev)
+    dec_wsb = fa.fa_decode_workspace_bytes(dw.B, dw.H, dw.Nq, dw.Nk, dw.d)
+    dec_ws = torch.empty(dec_wsb // 4, dtype=torch.float32, device=dev)
+
+    def decode():
+        fa.fa_decode(dqd, dkd, dvd, dod, dlse, dec_ws, dec_wsb, dw.B, dw.H, dw.Nq, dw.Nk, dw.d,
+                     dw.sm_scale, int(dw.causal), stream)
+
+    for _ in range(args.warmup):
+        decode()
+    dec_each = timed(decode, args.steps)
+    dec_ms = sum(dec_each) / args.steps
+    dec_gbps = dw.algorithmic_bytes / (dec_ms * 1e-3) / 1e9
+    del dqd, dkd, dvd
+    print(f"[bench] decode {dec_ms * 1e3:.1f} us", file=sys.stderr, flush=True)
+
     tflops = w.flops / (attn_ms * 1e-3) / 1e12
     sm_bytes = sw.algorithmic_bytes
     sm_gbps = sm_bytes / (sm_ms * 1e-3) / 1e9
@@ -573,7 +600,17 @@ def main():
                                        "frac": round(sp_gbps / PEAK_HBM_GBPS, 4),
                                        "kernels": ["softmax_split_partials<512,true>",
                                                    "softmax_split_normalise<512,true>"]}},
+        "decode": {"workload": dw.name, "value": round(dec_gbps, 1), "unit": "GB/s",
+                   "bytes_per_launch": dw.algorithmic_bytes, "workspace_bytes": dec_wsb,
+                   "avg_launch_us": round(dec_ms * 1e3, 2),
+                   "median_launch_us": round(dec_each[len(dec_each) // 2] * 1e3, 2),
+                   "roofline": {"bound": "hbm", "achieved": round(dec_gbps, 1),
+                                "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                                "frac": round(dec_gbps / PEAK_HBM_GBPS, 4),
+                                "kernels": ["attn_decode_partial<bf16,128,causal>",
+                                            "attn_decode_merge<bf16,128>"]}},
         "kernel_resources": {"attention": attrs, "softmax": sm_attrs,
+                             "decode": fa.kernel_attributes(fa.OP_FA_DECODE, dw.d, dw.causal),
                              "backward_dq": fa.kernel_attributes(fa.OP_FA_BWD_DQ, w.d, True),
                              "backward_dkdv": fa.kernel_attributes(fa.OP_FA_BWD_DKDV, w.d, True)},
     }

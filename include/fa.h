@@ -117,6 +117,44 @@ int fa_fwd_f32(const void* q, const void* k, const void* v, void* o, float* lse,
                int B, int H, int N, int d, float scale, int causal, hipStream_t stream);
 
 /*
+ * Decode-shaped attention: Nq queries against Nk keys, the queries being the
+ * last Nq positions of the key sequence (one new token per head, a few
+ * speculative tokens, or a prefill chunk over a cached prefix).  The key range
+ * of each head is cut into chunks that separate waves process with the
+ * online-softmax recurrence; each leaves a partial (m, l, unnormalised O) per
+ * query in `workspace`, and a second kernel merges a query's partials with the
+ * associative rule of two partial results, each with its own maximum, rescaled
+ * to the larger one ("100 Days of GPU, Day 97", Solution).  Split-KV keeps
+ * about 2048 waves busy even when B*H*Nq is small.
+ *
+ *  q          [B, H, Nq, d] bf16, read only.
+ *  k, v       [B, H, Nk, d] bf16, read only.
+ *  o          [B, H, Nq, d] bf16, written.
+ *  lse        [B, H, Nq] fp32 natural-log logsumexp over the visible keys, or NULL.
+ *  workspace  device memory of at least fa_decode_workspace_bytes(B, H, Nq,
+ *             Nk, d) bytes, 16-byte aligned, owned by the caller; contents
+ *             on entry ignored, scratch on exit.  Calls that share it must be
+ *             ordered (the same stream does that).
+ *  workspace_bytes  its size; a smaller value returns FA_ERR_INVALID_ARG.
+ *  causal     1: query i (0-based) sees keys 0 .. Nk - Nq + i, and needs
+ *             Nq <= Nk; 0: every query sees all Nk keys (any Nq).
+ *  d in {64, 128} (else FA_ERR_UNSUPPORTED); Nk * d * 2 < 2^31.
+ *  q, k, v, o 16-byte aligned (FA_ERR_ALIGNMENT); o, lse and workspace overlap
+ *  neither each other nor an input (FA_ERR_INVALID_ARG).  Every other
+ *  convention and the arithmetic (fp32 scores, P rounded to 16 bits, the
+ *  trailing reference maximum) are those of fa_fwd.
+ */
+size_t fa_decode_workspace_bytes(int B, int H, int Nq, int Nk, int d);
+int fa_decode(const void* q, const void* k, const void* v, void* o, float* lse, float* workspace,
+              size_t workspace_bytes, int B, int H, int Nq, int Nk, int d, float scale, int causal,
+              hipStream_t stream);
+
+/* Same contract with IEEE half-precision Q/K/V/O. */
+int fa_decode_f16(const void* q, const void* k, const void* v, void* o, float* lse,
+                  float* workspace, size_t workspace_bytes, int B, int H, int Nq, int Nk, int d,
+                  float scale, int causal, hipStream_t stream);
+
+/*
  * Attention backward: the gradients dQ, dK, dV of O = softmax(scale * Q K^T) V
  * for an upstream gradient dO, bfloat16 operands, fp32 accumulation.
  *
@@ -198,7 +236,8 @@ const char* fa_status_string(int status);
  * reports them), LDS bytes per workgroup, private (spill) bytes per lane,
  * threads per workgroup and resident workgroups per compute unit.
  *  op: 0 = fa_fwd, 1 = fa_fwd_f16, 2 = fa_fwd_f32, 3 = online_softmax_rows,
- *  4 = fa_bwd's dQ kernel, 5 = fa_bwd's dK/dV kernel
+ *  4 = fa_bwd's dQ kernel, 5 = fa_bwd's dK/dV kernel, 6 = fa_decode's
+ *  chunk kernel
  *  (for op 3, `d` carries cols and `causal` is ignored).
  */
 typedef struct {

@@ -16,6 +16,7 @@ import os
 __all__ = [
     "FaError", "lib", "fa_fwd", "fa_fwd_f16", "fa_fwd_f32", "online_softmax_rows",
     "online_softmax_rows_split", "online_softmax_split_workspace_bytes", "softmax_split",
+    "fa_decode", "fa_decode_f16", "fa_decode_workspace_bytes", "attention_decode",
     "fa_status_string", "kernel_attributes", "attention", "softmax", "LIB_PATH",
     "FA_OK", "FA_ERR_INVALID_ARG", "FA_ERR_UNSUPPORTED", "FA_ERR_ALIGNMENT", "FA_ERR_HIP",
 ]
@@ -29,7 +30,7 @@ FA_ERR_ALIGNMENT = -3
 FA_ERR_HIP = -4
 
 OP_FA_FWD, OP_FA_FWD_F16, OP_FA_FWD_F32, OP_SOFTMAX = 0, 1, 2, 3
-OP_FA_BWD_DQ, OP_FA_BWD_DKDV = 4, 5
+OP_FA_BWD_DQ, OP_FA_BWD_DKDV, OP_FA_DECODE = 4, 5, 6
 
 
 class FaError(RuntimeError):
@@ -68,6 +69,12 @@ def lib() -> ctypes.CDLL:
             fn = getattr(L, name)
             fn.argtypes = [vp] * 10 + [i, i, i, i, f, i, vp]
             fn.restype = i
+        for name in ("fa_decode", "fa_decode_f16"):
+            fn = getattr(L, name)
+            fn.argtypes = [vp] * 6 + [ctypes.c_size_t, i, i, i, i, i, f, i, vp]
+            fn.restype = i
+        L.fa_decode_workspace_bytes.argtypes = [i, i, i, i, i]
+        L.fa_decode_workspace_bytes.restype = ctypes.c_size_t
         L.fa_bwd_workspace_bytes.argtypes = [i, i, i]
         L.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
         L.online_softmax_rows.argtypes = [vp, vp, i, i, vp]
@@ -167,6 +174,33 @@ def fa_bwd_f16(q, k, v, o, dout, lse, dq, dk, dv, workspace, B, H, N, d, scale, 
          stream)
 
 
+def _decode(name, q, k, v, o, lse, workspace, workspace_bytes, B, H, Nq, Nk, d, scale, causal,
+            stream):
+    fn = getattr(lib(), name)
+    _check(fn(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(workspace), int(workspace_bytes),
+              int(B), int(H), int(Nq), int(Nk), int(d), float(scale), int(causal), _stream(stream)),
+           name)
+
+
+def fa_decode(q, k, v, o, lse, workspace, workspace_bytes, B, H, Nq, Nk, d, scale, causal,
+              stream=None):
+    """bf16 split-KV attention of Nq queries at the end of Nk keys (see include/fa.h)."""
+    _decode("fa_decode", q, k, v, o, lse, workspace, workspace_bytes, B, H, Nq, Nk, d, scale, causal,
+            stream)
+
+
+def fa_decode_f16(q, k, v, o, lse, workspace, workspace_bytes, B, H, Nq, Nk, d, scale, causal,
+                  stream=None):
+    """fp16 split-KV attention of Nq queries at the end of Nk keys (see include/fa.h)."""
+    _decode("fa_decode_f16", q, k, v, o, lse, workspace, workspace_bytes, B, H, Nq, Nk, d, scale,
+            causal, stream)
+
+
+def fa_decode_workspace_bytes(B, H, Nq, Nk, d) -> int:
+    """Bytes of workspace fa_decode needs (0 for invalid sizes)."""
+    return int(lib().fa_decode_workspace_bytes(int(B), int(H), int(Nq), int(Nk), int(d)))
+
+
 def fa_bwd_workspace_bytes(B, H, N) -> int:
     """Bytes of fp32 workspace fa_bwd needs (0 for invalid sizes)."""
     return int(lib().fa_bwd_workspace_bytes(int(B), int(H), int(N)))
@@ -256,6 +290,32 @@ def attention_backward(q, k, v, o, dout, lse, causal: bool = False, scale: float
                      device=q.device)
     _bwd(names[q.dtype], q, k, v, o, dout, lse, dq, dk, dv, ws, B, H, N, d, scale, causal, stream)
     return dq, dk, dv
+
+
+def attention_decode(q, k, v, causal: bool = False, scale: float | None = None, stream=None):
+    """O, LSE of q [B, H, Nq, d] against k, v [B, H, Nk, d] (bf16 or fp16 device tensors), the
+    queries being the last Nq positions of the key sequence."""
+    import torch
+    for t in (q, k, v):
+        if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+            raise TypeError("q, k, v must be device tensors")
+        if not t.is_contiguous() or t.dim() != 4 or t.dtype != q.dtype:
+            raise ValueError("q, k, v must be contiguous 4-d tensors of one dtype")
+    names = {torch.bfloat16: "fa_decode", torch.float16: "fa_decode_f16"}
+    if q.dtype not in names:
+        raise TypeError(f"unsupported dtype {q.dtype}")
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    if tuple(k.shape) != (B, H, Nk, d) or tuple(v.shape) != (B, H, Nk, d):
+        raise ValueError("k and v must be [B, H, Nk, d] with q's B, H and d")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    out = torch.empty_like(q)
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    nbytes = fa_decode_workspace_bytes(B, H, Nq, Nk, d)
+    ws = torch.empty(max(4, nbytes // 4), dtype=torch.float32, device=q.device)
+    _decode(names[q.dtype], q, k, v, out, lse, ws, nbytes, B, H, Nq, Nk, d, scale, causal, stream)
+    return out, lse
 
 
 def softmax(x, out=None, stream=None):

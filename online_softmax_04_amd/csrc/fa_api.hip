@@ -107,9 +107,83 @@ int bwd_entry(osm::Elem elem, const void* q, const void* k, const void* v, const
   return FA_OK;
 }
 
+// Workspace of fa_decode: partial O (fp32, d per row) then (m, l) pairs, one
+// row per (batch*head, key chunk, query); 0 on invalid sizes or overflow.
+uint64_t decode_workspace(int B, int H, int Nq, int Nk, int d, int* n_chunks) {
+  if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || d < 1) return 0;
+  const uint64_t bh = (uint64_t)B * (uint64_t)H;
+  if (bh > (uint64_t)INT_MAX) return 0;
+  int nc, ct;
+  osm::decode_split_plan((int)bh, Nq, Nk, &nc, &ct);
+  if (n_chunks) *n_chunks = nc;
+  return tensor_bytes((int)bh, nc, Nq, 1, 4 * (uint64_t)d + 8);
+}
+
+int decode_entry(osm::Elem elem, const void* q, const void* k, const void* v, void* o, float* lse,
+                 float* workspace, size_t workspace_bytes, int B, int H, int Nq, int Nk, int d,
+                 float scale, int causal, hipStream_t stream) {
+  if (!q || !k || !v || !o || !workspace) return FA_ERR_INVALID_ARG;
+  if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || d < 1) return FA_ERR_INVALID_ARG;
+  if (!std::isfinite(scale) || !(scale > 0.f)) return FA_ERR_INVALID_ARG;
+  if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
+  if (causal && Nq > Nk) return FA_ERR_INVALID_ARG;  // the queries are the last Nq positions
+  const uint64_t qbytes = tensor_bytes(B, H, Nq, d, 2);
+  const uint64_t kbytes = tensor_bytes(B, H, Nk, d, 2);
+  const uint64_t lse_bytes = tensor_bytes(B, H, Nq, 1, 4);
+  if (qbytes == 0 || kbytes == 0 || lse_bytes == 0) return FA_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if ((uint64_t)Nk * (uint64_t)d * 2 >= ((uint64_t)1 << 31)) return FA_ERR_UNSUPPORTED;
+  int n_chunks = 0;
+  const uint64_t ws = decode_workspace(B, H, Nq, Nk, d, &n_chunks);
+  if (ws == 0) return FA_ERR_INVALID_ARG;
+  // grids: one wave per (batch*head, chunk, 32-query group); one merge workgroup per query
+  const uint64_t bh = (uint64_t)B * (uint64_t)H;
+  if (bh * (uint64_t)n_chunks * (((uint64_t)Nq + 31) / 32) > (uint64_t)INT_MAX ||
+      bh * (uint64_t)Nq > (uint64_t)INT_MAX)
+    return FA_ERR_INVALID_ARG;
+  if ((uint64_t)workspace_bytes < ws) return FA_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+      !aligned(workspace, 16))
+    return FA_ERR_ALIGNMENT;
+  if (lse && !aligned(lse, 4)) return FA_ERR_ALIGNMENT;
+  // outputs (o, lse, workspace) overlap neither each other nor any input
+  const void* outs[] = {o, lse, workspace};
+  const uint64_t out_bytes[] = {qbytes, lse_bytes, ws};
+  for (int a = 0; a < 3; ++a) {
+    if (!outs[a]) continue;
+    for (int b = a + 1; b < 3; ++b)
+      if (outs[b] && overlaps(outs[a], out_bytes[a], outs[b], out_bytes[b])) return FA_ERR_INVALID_ARG;
+    if (overlaps(outs[a], out_bytes[a], q, qbytes) || overlaps(outs[a], out_bytes[a], k, kbytes) ||
+        overlaps(outs[a], out_bytes[a], v, kbytes))
+      return FA_ERR_INVALID_ARG;
+  }
+  hipError_t e = osm::launch_attn_decode(elem, q, k, v, o, lse, workspace, B, H, Nq, Nk, d, scale,
+                                         causal != 0, stream);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 }  // namespace
 
 extern "C" {
+
+size_t fa_decode_workspace_bytes(int B, int H, int Nq, int Nk, int d) {
+  if (d != 64 && d != 128) return 0;
+  return (size_t)decode_workspace(B, H, Nq, Nk, d, nullptr);
+}
+
+int fa_decode(const void* q, const void* k, const void* v, void* o, float* lse, float* workspace,
+              size_t workspace_bytes, int B, int H, int Nq, int Nk, int d, float scale, int causal,
+              hipStream_t stream) {
+  return decode_entry(osm::Elem::bf16, q, k, v, o, lse, workspace, workspace_bytes, B, H, Nq, Nk, d,
+                      scale, causal, stream);
+}
+
+int fa_decode_f16(const void* q, const void* k, const void* v, void* o, float* lse,
+                  float* workspace, size_t workspace_bytes, int B, int H, int Nq, int Nk, int d,
+                  float scale, int causal, hipStream_t stream) {
+  return decode_entry(osm::Elem::f16, q, k, v, o, lse, workspace, workspace_bytes, B, H, Nq, Nk, d,
+                      scale, causal, stream);
+}
 
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
            int d, float scale, int causal, hipStream_t stream) {
@@ -224,6 +298,9 @@ int fa_kernel_attributes(int op, int d, int causal, fa_kernel_attrs* out) {
   } else if (op == 4 || op == 5) {
     if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
     e = osm::attn_bwd_attributes(osm::Elem::bf16, d, causal != 0, op - 4, &attr, &threads, &blocks);
+  } else if (op == 6) {
+    if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+    e = osm::attn_decode_attributes(d, causal != 0, &attr, &threads, &blocks);
   } else if (op == 3) {
     if (d < 1) return FA_ERR_INVALID_ARG;
     e = osm::softmax_attributes(d, d % 4 == 0, &attr, &threads, &blocks);

@@ -29,6 +29,16 @@ hipError_t launch_attn_bwd(Elem elem, const void* q, const void* k, const void* 
 hipError_t attn_bwd_attributes(Elem elem, int d, bool causal, int which, hipFuncAttributes* attr,
                                int* threads, int* blocks_per_cu);
 
+// Split-KV attention of Nq queries at the end of Nk keys (bf16 / fp16): partial
+// results per key chunk into `workspace`, then the merge; see decode_split_plan
+// for the chunking and the workspace layout in attn_decode.hip.
+void decode_split_plan(int BH, int Nq, int Nk, int* n_chunks, int* chunk_tiles);
+hipError_t launch_attn_decode(Elem elem, const void* q, const void* k, const void* v, void* o,
+                              float* lse, float* workspace, int B, int H, int Nq, int Nk, int d,
+                              float scale, bool causal, hipStream_t stream);
+hipError_t attn_decode_attributes(int d, bool causal, hipFuncAttributes* attr, int* threads,
+                                  int* blocks_per_cu);
+
 // Row softmax on `stream`; vec_ok = 16-byte aligned pointers and cols % 4 == 0.
 hipError_t launch_softmax(const float* x, float* y, int rows, int cols, bool vec_ok,
                           hipStream_t stream);

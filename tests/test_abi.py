@@ -30,6 +30,7 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("fa_fwd", "fa_fwd_f16", "fa_fwd_f32", "fa_fwd_local", "fa_fwd_local_f16", "fa_bwd",
               "fa_bwd_f16", "fa_bwd_workspace_bytes",
+              "fa_decode", "fa_decode_f16", "fa_decode_workspace_bytes",
               "online_softmax_rows", "online_softmax_rows_split",
               "online_softmax_split_workspace_bytes", "fa_status_string", "fa_kernel_attributes"):
         assert n in names
@@ -236,6 +237,45 @@ def call_split(x=A, y=A + 64 * MB, rows=4, cols=100, ws=WS, wsb=None):
 ])
 def test_split_validation(kw, status):
     assert call_split(**kw) == status
+
+
+def test_decode_workspace_bytes():
+    # (batch*head, chunk, query) rows of d fp32 + an (m, l) pair; chunks of 32 tiles of
+    # 32 keys, fewer tiles (down to 4) while the grid has under 2048 waves
+    assert fa.fa_decode_workspace_bytes(8, 32, 1, 32768, 128) == 256 * 32 * 1 * (4 * 128 + 8)
+    assert fa.fa_decode_workspace_bytes(1, 1, 1, 131072, 64) == 1024 * (4 * 64 + 8)
+    assert fa.fa_decode_workspace_bytes(1, 1, 1, 1, 64) == 4 * 64 + 8
+    assert fa.fa_decode_workspace_bytes(1, 1, 1, 100, 96) == 0
+    assert fa.fa_decode_workspace_bytes(0, 1, 1, 100, 64) == 0
+
+
+def call_decode(q=A, k=A + 64 * MB, v=A + 128 * MB, o=A + 192 * MB, lse=A + 200 * MB,
+                ws=A + 256 * MB, wsb=None, B=1, H=2, Nq=3, Nk=100, d=128, scale=0.1, causal=1):
+    if wsb is None:
+        wsb = fa.fa_decode_workspace_bytes(1, 2, 3, 100, 128)
+    return fa.lib().fa_decode(q, k, v, o, lse, ws, wsb, B, H, Nq, Nk, d, scale, causal, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=0), fa.FA_ERR_INVALID_ARG), (dict(k=0), fa.FA_ERR_INVALID_ARG),
+    (dict(v=0), fa.FA_ERR_INVALID_ARG), (dict(o=0), fa.FA_ERR_INVALID_ARG),
+    (dict(ws=0), fa.FA_ERR_INVALID_ARG),
+    (dict(Nq=0), fa.FA_ERR_INVALID_ARG), (dict(Nk=0), fa.FA_ERR_INVALID_ARG),
+    (dict(B=-1), fa.FA_ERR_INVALID_ARG), (dict(scale=0.0), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), fa.FA_ERR_INVALID_ARG), (dict(causal=2), fa.FA_ERR_INVALID_ARG),
+    (dict(Nq=101), fa.FA_ERR_INVALID_ARG),                 # causal needs Nq <= Nk
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(Nk=1 << 23), fa.FA_ERR_UNSUPPORTED),              # a head's K over 2^31 bytes
+    (dict(wsb=100), fa.FA_ERR_INVALID_ARG),
+    (dict(q=A + 8), fa.FA_ERR_ALIGNMENT), (dict(o=A + 192 * MB + 2), fa.FA_ERR_ALIGNMENT),
+    (dict(ws=A + 256 * MB + 8), fa.FA_ERR_ALIGNMENT), (dict(lse=A + 200 * MB + 2), fa.FA_ERR_ALIGNMENT),
+    (dict(o=A + 64 * MB + 512), fa.FA_ERR_INVALID_ARG),     # o inside k
+    (dict(lse=A + 192 * MB + 16), fa.FA_ERR_INVALID_ARG),   # lse inside o
+    (dict(ws=A + 192 * MB), fa.FA_ERR_INVALID_ARG),         # workspace on o
+    (dict(ws=A), fa.FA_ERR_INVALID_ARG),                    # workspace on q
+])
+def test_decode_validation(kw, status):
+    assert call_decode(**kw) == status
 
 
 def test_python_wrappers_raise():

@@ -36,7 +36,8 @@ import numpy as np
 BASE_SEED = 97000
 
 __all__ = [
-    "AttnWorkload", "SoftmaxWorkload", "ATTN", "SOFTMAX",
+    "AttnWorkload", "SoftmaxWorkload", "DecodeWorkload", "ATTN", "SOFTMAX", "DECODE",
+    "decode_head", "decode_full",
     "f32_to_bf16_bits", "bf16_bits_to_f32", "cast", "attn_head", "attn_full",
     "attn_sample_rows", "softmax_input", "random_attn", "random_rows",
 ]
@@ -237,6 +238,75 @@ def local_ranges(doc_start_row: np.ndarray, window: int) -> tuple[np.ndarray, np
     if window > 0:
         lo = np.maximum(lo, i - window + 1)
     return np.clip(lo, 0, i), i
+
+
+# --------------------------------------------------------------------------
+# decode-shaped attention: Nq queries at the end of Nk cached keys
+# --------------------------------------------------------------------------
+@dataclass(frozen=True)
+class DecodeWorkload:
+    name: str
+    B: int
+    H: int
+    Nq: int
+    Nk: int
+    d: int
+    dtype: str
+    causal: bool
+    seed: int
+    k_row_scale: tuple | None = (0.5, 2.0)
+
+    @property
+    def sm_scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+    @property
+    def kv_bytes(self) -> int:
+        """K and V read once: the algorithmic bytes that dominate (Q and O are Nq / Nk of them)."""
+        return 2 * self.B * self.H * self.Nk * self.d * 2
+
+    @property
+    def algorithmic_bytes(self) -> int:
+        """K and V read once, Q read once, O written once (16-bit), LSE written once (fp32)."""
+        return self.kv_bytes + 2 * self.B * self.H * self.Nq * self.d * 2 + 4 * self.B * self.H * self.Nq
+
+
+# one new token per sequence against a 32768-token cache: the B8 H32 d128 shape of
+# the dense workload, N(0, 1) entries with K rows x U(0.5, 2)
+DECODE = {
+    w.name: w for w in [
+        DecodeWorkload("decode_bf16_b8h32_q1_kv32768_d128", 8, 32, 1, 32768, 128, "bf16", True,
+                       BASE_SEED + 7),
+    ]
+}
+
+
+def decode_head(w: DecodeWorkload, b: int, h: int):
+    """One head's (q [Nq, d], k [Nk, d], v [Nk, d]) in the storage type."""
+    rng = np.random.default_rng([w.seed, b, h])
+    q = rng.standard_normal((w.Nq, w.d), dtype=np.float32)
+    k = rng.standard_normal((w.Nk, w.d), dtype=np.float32)
+    v = rng.standard_normal((w.Nk, w.d), dtype=np.float32)
+    if w.k_row_scale is not None:
+        lo, hi = w.k_row_scale
+        k = k * rng.uniform(lo, hi, size=(w.Nk, 1)).astype(np.float32)
+    return cast(q, w.dtype), cast(k, w.dtype), cast(v, w.dtype)
+
+
+def decode_full(w: DecodeWorkload, threads: int = 8):
+    """Full (q [B, H, Nq, d], k and v [B, H, Nk, d]) in the storage type."""
+    dt = {"f16": np.float16, "bf16": np.uint16}[w.dtype]
+    q = np.empty((w.B, w.H, w.Nq, w.d), dt)
+    k = np.empty((w.B, w.H, w.Nk, w.d), dt)
+    v = np.empty((w.B, w.H, w.Nk, w.d), dt)
+
+    def fill(bh):
+        b, h = divmod(bh, w.H)
+        q[b, h], k[b, h], v[b, h] = decode_head(w, b, h)
+
+    with ThreadPoolExecutor(max(1, threads)) as ex:
+        list(ex.map(fill, range(w.B * w.H)))
+    return q, k, v
 
 
 # --------------------------------------------------------------------------
