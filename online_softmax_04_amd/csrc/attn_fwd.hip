@@ -86,6 +86,11 @@ __device__ __forceinline__ float add_pair<_Float16>(unsigned x, float acc) {
 }
 
 
+template <int S>
+struct StageTag {
+  static constexpr int value = S;
+};
+
 constexpr float kSlack = 8.f;  // how far (log2 units) the running maximum may pass m
 constexpr int kBM = 256;       // queries per workgroup
 // keys per tile: 128 at d = 64, where the per-tile fixed costs weigh most and the
@@ -112,8 +117,19 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(
   constexpr int RPI = 1024 / ROW_BYTES;        // rows per 1 KiB wave-wide load
   constexpr int NI = TILE_BYTES / 1024 / 8;    // such loads per wave per tile
   static_assert(NI >= 1, "tile shape");
-  __shared__ __attribute__((aligned(1024))) unsigned char kbuf[2 * TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) unsigned char vbuf[2 * TILE_BYTES];
+  // One array per stage and operand, always named at compile time: the compiler
+  // tracks the pending direct loads per array, so a read of one stage does not
+  // wait for the loads into the other.  Tile t lives in stage (t - t0) & 1.
+  __shared__ __attribute__((aligned(1024))) unsigned char kb0[TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) unsigned char kb1[TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) unsigned char vb0[TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) unsigned char vb1[TILE_BYTES];
+  auto kbuf = [&](auto st) -> unsigned char* {
+    if constexpr (decltype(st)::value == 0) return kb0; else return kb1;
+  };
+  auto vbuf = [&](auto st) -> unsigned char* {
+    if constexpr (decltype(st)::value == 0) return vb0; else return vb1;
+  };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -216,17 +232,17 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(
     kgoff[j] = row * ROW_BYTES + (p ^ kswz<D>(row)) * 16;
     vgoff[j] = row * ROW_BYTES + (p ^ vswz<D>(row)) * 16;
   }
-  auto load_k = [&](int t) {
+  auto load_k = [&](int t, auto st) __attribute__((always_inline)) {
     const auto r = make_rsrc(Kh + (size_t)t * BN * D, (int64_t)(N - t * BN) * ROW_BYTES);
 #pragma unroll
     for (int j = 0; j < NI; ++j)
-      load16_to_lds(r, kbuf + (t & 1) * TILE_BYTES + (wave_s * NI + j) * 1024, kgoff[j]);
+      load16_to_lds(r, kbuf(st) + (wave_s * NI + j) * 1024, kgoff[j]);
   };
-  auto load_v = [&](int t) {
+  auto load_v = [&](int t, auto st) __attribute__((always_inline)) {
     const auto r = make_rsrc(Vh + (size_t)t * BN * D, (int64_t)(N - t * BN) * ROW_BYTES);
 #pragma unroll
     for (int j = 0; j < NI; ++j)
-      load16_to_lds(r, vbuf + (t & 1) * TILE_BYTES + (wave_s * NI + j) * 1024, vgoff[j]);
+      load16_to_lds(r, vbuf(st) + (wave_s * NI + j) * 1024, vgoff[j]);
   };
   // direct loads write LDS behind the compiler's back: wait for them explicitly
   auto loads_landed = [&]() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
@@ -255,9 +271,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(
   }
 
   // ---- the three pieces of a tile --------------------------------------------------------
-  // QK(t): S^T = K(t) Q^T, one accumulator per 32-key block, from K buffer t % 2.
-  auto qk = [&](int t) {
-    const unsigned char* Kt = kbuf + (t & 1) * TILE_BYTES;
+  // QK: S^T = K Q^T, one accumulator per 32-key block, from K stage st.
+  auto qk = [&](auto st) __attribute__((always_inline)) {
+    const unsigned char* Kt = kbuf(st);
 #pragma unroll
     for (int kh = 0; kh < NH; ++kh) s[kh] = f32x16{};
 #pragma unroll
@@ -272,7 +288,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(
   };
   // SM(t): online softmax of S(t): m, l and O rescaled by 2^(m_old - m_new),
   // P = 2^(c S - m_new) packed to 16 bits, with m the trailing reference.
-  auto sm = [&](int t) {
+  auto sm = [&](int t) __attribute__((always_inline)) {
     const int j0 = t * BN;
     // keys past N, and keys after the query when causal (wave-uniform test)
     if ((j0 + BN > N) || (CAUSAL && j0 + BN - 1 > qw0) || (LOCAL && j0 < lo_max_w)) {
@@ -319,9 +335,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(
       for (int db = 0; db < ND; ++db) o[db] *= alpha;
     }
   };
-  // PV(t): O^T += V^T(t) P^T(t), from V buffer t % 2.
-  auto pv = [&](int t) {
-    const unsigned char* Vt = vbuf + (t & 1) * TILE_BYTES;
+  // PV: O^T += V^T P^T, from V stage st.
+  auto pv = [&](auto st) __attribute__((always_inline)) {
+    const unsigned char* Vt = vbuf(st);
 #pragma unroll
     for (int kh = 0; kh < NH; ++kh) {
 #pragma unroll
@@ -341,9 +357,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(
   // PV(tp) then QK(tq) in one block, with the LDS operand reads running a fixed
   // distance ahead of the MFMAs that consume them: enough reads in flight to
   // cover LDS latency, few enough registers to avoid spilling.
-  auto pv_qk = [&](int tp, int tq) {
-    pv(tp);
-    qk(tq);
+  auto pv_qk = [&](auto stp, auto stq) __attribute__((always_inline)) {
+    pv(stp);
+    qk(stq);
     // PV MFMAs take two transposed reads each, QK MFMAs one read
     constexpr int kAhead = 4;               // MFMAs whose operands are read ahead
     constexpr int kPv = 2 * NH * ND, kQk = NH * NK;
@@ -357,116 +373,81 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(
     }
   };
 
+  // One tile t in stage S = (t - t0) & 1: slot X(t), the barrier, slot Y(t).
+  // For the dense kernel t0 = 0 and act(t) is t < n_w.
+  auto tile = [&](int t, auto st) __attribute__((always_inline)) {
+    constexpr int S = decltype(st)::value;
+    const StageTag<S> cur;
+    const StageTag<S ^ 1> other;
+    // ---- slot X(t)
+    if (group == 0) {
+      if (act(t)) sm(t);
+    } else {
+      __builtin_amdgcn_s_setprio(1);
+      if (t > t0 && act(t - 1) && act(t)) {
+        pv_qk(other, cur);
+      } else {
+        if (t > t0 && act(t - 1)) pv(other);
+        if (act(t)) qk(cur);
+      }
+      __builtin_amdgcn_s_setprio(0);
+    }
+    loads_landed();  // K(t+1), V(t)
+    __syncthreads();
+    // ---- slot Y(t)
+    if (t + 2 < n_kt) load_k(t + 2, cur);
+    if (t + 1 < n_kt) load_v(t + 1, other);
+    if (group == 0) {
+      __builtin_amdgcn_s_setprio(1);
+      if (act(t) && act(t + 1)) {
+        pv_qk(cur, other);
+      } else {
+        if (act(t)) pv(cur);
+        if (act(t + 1)) qk(other);
+      }
+      __builtin_amdgcn_s_setprio(0);
+    } else {
+      if (act(t)) sm(t);
+    }
+  };
+
   // ---- slot schedule ----------------------------------------------------------------
   // Each tile t takes two slots:
   //   slot X(t): group 0 runs SM(t)          group 1 runs PV(t-1), QK(t)
   //   slot Y(t): group 0 runs PV(t), QK(t+1) group 1 runs SM(t)
   // so on every SIMD one wave keeps the matrix unit busy while the other runs
   // the vector-ALU softmax.  K(t+1) and V(t) are read from Y(t) to X(t+1); they
-  // are loaded into LDS during Y(t-1) and X(t) (into the buffers of K(t-1) and
+  // are loaded into LDS during Y(t-1) and X(t) (into the stages of K(t-1) and
   // V(t-1), last read in X(t-1)) and published by the workgroup barrier that
-  // ends X(t).  That barrier is the only one per tile: no LDS buffer changes
+  // ends X(t).  That barrier is the only one per tile: no LDS stage changes
   // hands between Y(t) and X(t+1), and meeting once per tile keeps the two
-  // groups in opposite phases.
-  if constexpr (!LOCAL) {
-    load_k(0);
-    loads_landed();
-    __syncthreads();
-    // Retire the Q loads here.  Left pending, they would make the first MFMA that
-    // reads Q wait on the vector-memory counter, which then also counts the tile
-    // loads in flight.
-  #pragma unroll
-    for (int kb = 0; kb < NK; ++kb) asm volatile("" ::"v"(qf[kb]));
-    // slot Y(-1): load K(1), V(0); group 0 computes S(0)
-    if (n_kt > 1) load_k(1);
-    load_v(0);
-    if (group == 0) {
-      __builtin_amdgcn_s_setprio(1);
-      qk(0);
-      __builtin_amdgcn_s_setprio(0);
-    }
-    __syncthreads();
-    for (int t = 0; t < n_kt; ++t) {
-      // ---- slot X(t)
-      if (group == 0) {
-        if (t < n_w) sm(t);
-      } else {
-        __builtin_amdgcn_s_setprio(1);
-        if (t >= 1 && t < n_w) {
-          pv_qk(t - 1, t);
-        } else {
-          if (t >= 1 && t - 1 < n_w) pv(t - 1);
-          if (t < n_w) qk(t);
-        }
-        __builtin_amdgcn_s_setprio(0);
-      }
-      loads_landed();  // K(t+1), V(t)
-      __syncthreads();
-      // ---- slot Y(t)
-      if (t + 2 < n_kt) load_k(t + 2);
-      if (t + 1 < n_kt) load_v(t + 1);
-      if (group == 0) {
-        __builtin_amdgcn_s_setprio(1);
-        if (t + 1 < n_w) {
-          pv_qk(t, t + 1);
-        } else if (t < n_w) {
-          pv(t);
-        }
-        __builtin_amdgcn_s_setprio(0);
-      } else {
-        if (t < n_w) sm(t);
-      }
-    }
-    // slot X(n_kt): group 1 finishes the last PV
-    if (group == 1 && n_kt - 1 < n_w) pv(n_kt - 1);
-  } else {
-    // the same schedule from tile t0, each wave computing from its own tile tw0
-    load_k(t0);
-    loads_landed();
-    __syncthreads();
+  // groups in opposite phases.  The dense kernel starts at tile t0 = 0; the
+  // LOCAL one at the workgroup's first visible tile, each wave computing from
+  // its own first tile tw0.
+  load_k(t0, StageTag<0>{});
+  loads_landed();
+  __syncthreads();
+  // Retire the Q loads here.  Left pending, they would make the first MFMA that
+  // reads Q wait on the vector-memory counter, which then also counts the tile
+  // loads in flight.
 #pragma unroll
-    for (int kb = 0; kb < NK; ++kb) asm volatile("" ::"v"(qf[kb]));
-    if (t0 + 1 < n_kt) load_k(t0 + 1);
-    load_v(t0);
-    if (group == 0 && act(t0)) {
-      __builtin_amdgcn_s_setprio(1);
-      qk(t0);
-      __builtin_amdgcn_s_setprio(0);
-    }
-    __syncthreads();
-    for (int t = t0; t < n_kt; ++t) {
-      // ---- slot X(t)
-      if (group == 0) {
-        if (act(t)) sm(t);
-      } else {
-        __builtin_amdgcn_s_setprio(1);
-        if (t > t0 && act(t - 1) && act(t)) {
-          pv_qk(t - 1, t);
-        } else {
-          if (t > t0 && act(t - 1)) pv(t - 1);
-          if (act(t)) qk(t);
-        }
-        __builtin_amdgcn_s_setprio(0);
-      }
-      loads_landed();  // K(t+1), V(t)
-      __syncthreads();
-      // ---- slot Y(t)
-      if (t + 2 < n_kt) load_k(t + 2);
-      if (t + 1 < n_kt) load_v(t + 1);
-      if (group == 0) {
-        __builtin_amdgcn_s_setprio(1);
-        if (act(t) && act(t + 1)) {
-          pv_qk(t, t + 1);
-        } else {
-          if (act(t)) pv(t);
-          if (act(t + 1)) qk(t + 1);
-        }
-        __builtin_amdgcn_s_setprio(0);
-      } else {
-        if (act(t)) sm(t);
-      }
-    }
-    if (group == 1 && act(n_kt - 1)) pv(n_kt - 1);
+  for (int kb = 0; kb < NK; ++kb) asm volatile("" ::"v"(qf[kb]));
+  // slot Y(t0 - 1): load K(t0+1), V(t0); group 0 computes S(t0)
+  if (t0 + 1 < n_kt) load_k(t0 + 1, StageTag<1>{});
+  load_v(t0, StageTag<0>{});
+  if (group == 0 && act(t0)) {
+    __builtin_amdgcn_s_setprio(1);
+    qk(StageTag<0>{});
+    __builtin_amdgcn_s_setprio(0);
+  }
+  __syncthreads();
+  for (int t = t0; t < n_kt; t += 2) {
+    tile(t, StageTag<0>{});
+    if (t + 1 < n_kt) tile(t + 1, StageTag<1>{});
+  }
+  // slot X(n_kt): group 1 finishes the last PV
+  if (group == 1 && act(n_kt - 1)) {
+    if (((n_kt - 1 - t0) & 1) == 0) pv(StageTag<0>{}); else pv(StageTag<1>{});
   }
 
   // ---- epilogue: O / l, logsumexp --------------------------------------------------
