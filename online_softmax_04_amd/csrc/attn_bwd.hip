@@ -159,8 +159,17 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dq(
   constexpr int ROW_BYTES = D * 2;
   constexpr int TILE_BYTES = kKT * ROW_BYTES;
   constexpr int ND = D / 32, NK = D / 16;
-  __shared__ __attribute__((aligned(1024))) unsigned char kbuf[2 * TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) unsigned char vbuf[2 * TILE_BYTES];
+  // K and V tiles, two stages each, one array per stage (StageTag)
+  __shared__ __attribute__((aligned(1024))) unsigned char kb0[TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) unsigned char kb1[TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) unsigned char vb0[TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) unsigned char vb1[TILE_BYTES];
+  auto kbuf = [&](auto st) -> unsigned char* {
+    if constexpr (decltype(st)::value == 0) return kb0; else return kb1;
+  };
+  auto vbuf = [&](auto st) -> unsigned char* {
+    if constexpr (decltype(st)::value == 0) return vb0; else return vb1;
+  };
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hf = lane >> 5;
@@ -212,20 +221,19 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dq(
   const TrOffsets<D> tro(lane);
   const uint16_t* Kh = K + base;
   const uint16_t* Vh = V + base;
-  auto load_kv = [&](int t) {
+  auto load_kv = [&](int t, auto st) __attribute__((always_inline)) {
     const int64_t bytes = (int64_t)(N - t * kKT) * ROW_BYTES;
-    load_tile<D, kKT>(make_rsrc(Kh + (size_t)t * kKT * D, bytes), kbuf + (t & 1) * TILE_BYTES, wave_s, lane);
-    load_tile<D, kKT>(make_rsrc(Vh + (size_t)t * kKT * D, bytes), vbuf + (t & 1) * TILE_BYTES, wave_s, lane);
+    load_tile<D, kKT>(make_rsrc(Kh + (size_t)t * kKT * D, bytes), kbuf(st), wave_s, lane);
+    load_tile<D, kKT>(make_rsrc(Vh + (size_t)t * kKT * D, bytes), vbuf(st), wave_s, lane);
   };
 
-  load_kv(0);
-  vmem_landed();
-  __syncthreads();
-  for (int t = 0; t < n_kt; ++t) {
-    if (t + 1 < n_kt) load_kv(t + 1);  // into the buffers read in tile t - 1
+  // key tile t from stage st; the next tile loads into the other stage, whose
+  // reads (tile t - 1) ended at the previous barrier
+  auto tile = [&](int t, auto st) __attribute__((always_inline)) {
+    if (t + 1 < n_kt) load_kv(t + 1, StageTag<decltype(st)::value ^ 1>{});
     if (t < n_w) {
-      const unsigned char* Kt = kbuf + (t & 1) * TILE_BYTES;
-      const unsigned char* Vt = vbuf + (t & 1) * TILE_BYTES;
+      const unsigned char* Kt = kbuf(st);
+      const unsigned char* Vt = vbuf(st);
       const int j0 = t * kKT;
       const bool masked = (j0 + kKT > N) || (CAUSAL && j0 + kKT - 1 > qw0);
 #pragma unroll
@@ -259,6 +267,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dq(
     }
     vmem_landed();  // tile t + 1
     __syncthreads();
+  };
+
+  load_kv(0, StageTag<0>{});
+  vmem_landed();
+  __syncthreads();
+  for (int t = 0; t < n_kt; t += 2) {
+    tile(t, StageTag<0>{});
+    if (t + 1 < n_kt) tile(t + 1, StageTag<1>{});
   }
   store_rows<T, D>(dq, make_rsrc(dQ + base + (size_t)qw0_s * D, (int64_t)(N - qw0_s) * ROW_BYTES), lane, scale);
 }
@@ -278,14 +294,34 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dkdv(
   constexpr int BLK_BYTES = kKB * ROW_BYTES;   // the workgroup's K (or V) rows
   constexpr int TILE_BYTES = kQT * ROW_BYTES;  // one Q (or dO) tile
   constexpr int STAT_BYTES = kQT * 4;          // one tile of lse (or D)
-  // kblk | vblk | q[2] | do[2] | lse[2] | D[2]; after the loop the first
-  // 128 KiB (d = 128) hold the partial sums of the second wave of each pair
-  constexpr int OFF_V = BLK_BYTES, OFF_Q = 2 * BLK_BYTES, OFF_DO = OFF_Q + 2 * TILE_BYTES;
-  constexpr int OFF_L = OFF_DO + 2 * TILE_BYTES, OFF_D = OFF_L + 2 * STAT_BYTES;
-  constexpr int LDS_BYTES = OFF_D + 2 * STAT_BYTES;
-  constexpr int RED_BYTES = 4 * 64 * 2 * ND * 16 * 4;
-  static_assert(RED_BYTES <= LDS_BYTES, "reduction space");
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[LDS_BYTES];
+  // kvblk = the workgroup's K rows then its V rows, loaded once; after the loop
+  // it holds the partial sums of the second wave of each pair, dK then dV.  The
+  // per-tile Q, dO, lse and D have two stages each, one array per stage
+  // (StageTag).
+  constexpr int OFF_V = BLK_BYTES;
+  constexpr int RED_BYTES = 4 * 64 * ND * 16 * 4;  // one of dK, dV for the four pairs
+  static_assert(RED_BYTES <= 2 * BLK_BYTES, "reduction space");
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * BLK_BYTES];
+  __shared__ __attribute__((aligned(1024))) unsigned char qb0[TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) unsigned char qb1[TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) unsigned char db0[TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) unsigned char db1[TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) unsigned char lb0[STAT_BYTES];
+  __shared__ __attribute__((aligned(16))) unsigned char lb1[STAT_BYTES];
+  __shared__ __attribute__((aligned(16))) unsigned char eb0[STAT_BYTES];
+  __shared__ __attribute__((aligned(16))) unsigned char eb1[STAT_BYTES];
+  auto qbuf = [&](auto st) -> unsigned char* {
+    if constexpr (decltype(st)::value == 0) return qb0; else return qb1;
+  };
+  auto dobuf = [&](auto st) -> unsigned char* {
+    if constexpr (decltype(st)::value == 0) return db0; else return db1;
+  };
+  auto lbuf = [&](auto st) -> unsigned char* {
+    if constexpr (decltype(st)::value == 0) return lb0; else return lb1;
+  };
+  auto dbuf = [&](auto st) -> unsigned char* {
+    if constexpr (decltype(st)::value == 0) return eb0; else return eb1;
+  };
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hf = lane >> 5;
@@ -320,29 +356,26 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dkdv(
     kboff[kb] = (32 * kg + l32) * ROW_BYTES + ((2 * kb + hf) ^ kswz<D>(l32)) * 16;
   }
   const TrOffsets<D> tro(lane);
-  auto load_qtile = [&](int t) {
-    const int st = t & 1;
+  auto load_qtile = [&](int t, auto st) __attribute__((always_inline)) {
     const int64_t bytes = (int64_t)(N - t * kQT) * ROW_BYTES;
-    load_tile<D, kQT>(make_rsrc(Q + base + (size_t)t * kQT * D, bytes), smem + OFF_Q + st * TILE_BYTES, wave_s, lane);
-    load_tile<D, kQT>(make_rsrc(dO + base + (size_t)t * kQT * D, bytes), smem + OFF_DO + st * TILE_BYTES, wave_s, lane);
+    load_tile<D, kQT>(make_rsrc(Q + base + (size_t)t * kQT * D, bytes), qbuf(st), wave_s, lane);
+    load_tile<D, kQT>(make_rsrc(dO + base + (size_t)t * kQT * D, bytes), dobuf(st), wave_s, lane);
     const int64_t sbytes = (int64_t)(N - t * kQT) * 4;
-    if (wave_s == 0) load4_to_lds(make_rsrc(LSE + (size_t)bh * N + (size_t)t * kQT, sbytes), smem + OFF_L + st * STAT_BYTES, lane * 4);
-    if (wave_s == 1) load4_to_lds(make_rsrc(Dws + (size_t)bh * N + (size_t)t * kQT, sbytes), smem + OFF_D + st * STAT_BYTES, lane * 4);
+    if (wave_s == 0) load4_to_lds(make_rsrc(LSE + (size_t)bh * N + (size_t)t * kQT, sbytes), lbuf(st), lane * 4);
+    if (wave_s == 1) load4_to_lds(make_rsrc(Dws + (size_t)bh * N + (size_t)t * kQT, sbytes), dbuf(st), lane * 4);
   };
 
-  if (qt_first < n_qt) load_qtile(qt_first);
-  vmem_landed();
-  __syncthreads();
-  for (int t = qt_first; t < n_qt; ++t) {
-    if (t + 1 < n_qt) load_qtile(t + 1);  // into the buffers read in tile t - 1
+  // query tile t from stage st; the next tile loads into the other stage, whose
+  // reads (tile t - 1) ended at the previous barrier
+  auto tile = [&](int t, auto st) __attribute__((always_inline)) {
+    if (t + 1 < n_qt) load_qtile(t + 1, StageTag<decltype(st)::value ^ 1>{});
     const int qa0 = t * kQT + 32 * qh;    // first query of this wave's half
     // skip when every query of the half is before every key of the wave
     if (!CAUSAL || qa0 + 31 >= kw0) {
-      const int st = t & 1;
-      const unsigned char* Qt = smem + OFF_Q + st * TILE_BYTES;
-      const unsigned char* dOt = smem + OFF_DO + st * TILE_BYTES;
-      const float* Lt = reinterpret_cast<const float*>(smem + OFF_L + st * STAT_BYTES);
-      const float* Dt = reinterpret_cast<const float*>(smem + OFF_D + st * STAT_BYTES);
+      const unsigned char* Qt = qbuf(st);
+      const unsigned char* dOt = dobuf(st);
+      const float* Lt = reinterpret_cast<const float*>(lbuf(st));
+      const float* Dt = reinterpret_cast<const float*>(dbuf(st));
       f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
       for (int kb = 0; kb < NK; ++kb) {
@@ -384,24 +417,37 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dkdv(
     }
     vmem_landed();  // tile t + 1
     __syncthreads();
+  };
+
+  if (qt_first < n_qt) load_qtile(qt_first, StageTag<0>{});
+  vmem_landed();
+  __syncthreads();
+  for (int t = qt_first; t < n_qt; t += 2) {
+    tile(t, StageTag<0>{});
+    if (t + 1 < n_qt) tile(t + 1, StageTag<1>{});
   }
 
-  // the two waves of a pair (qh = 0, 1) hold partial sums over different queries
+  // the two waves of a pair (qh = 0, 1) hold partial sums over different
+  // queries: dK through the K/V block first, then dV
   f32x16* red = reinterpret_cast<f32x16*>(smem);
   if (qh == 1) {
 #pragma unroll
-    for (int db = 0; db < ND; ++db) {
-      red[((kg * 2 * ND + db) * 64) + lane] = dk[db];
-      red[((kg * 2 * ND + ND + db) * 64) + lane] = dv[db];
-    }
+    for (int db = 0; db < ND; ++db) red[((kg * ND + db) * 64) + lane] = dk[db];
   }
   __syncthreads();
   if (qh == 0) {
 #pragma unroll
-    for (int db = 0; db < ND; ++db) {
-      dk[db] += red[((kg * 2 * ND + db) * 64) + lane];
-      dv[db] += red[((kg * 2 * ND + ND + db) * 64) + lane];
-    }
+    for (int db = 0; db < ND; ++db) dk[db] += red[((kg * ND + db) * 64) + lane];
+  }
+  __syncthreads();
+  if (qh == 1) {
+#pragma unroll
+    for (int db = 0; db < ND; ++db) red[((kg * ND + db) * 64) + lane] = dv[db];
+  }
+  __syncthreads();
+  if (qh == 0) {
+#pragma unroll
+    for (int db = 0; db < ND; ++db) dv[db] += red[((kg * ND + db) * 64) + lane];
     const int kw0_s = __builtin_amdgcn_readfirstlane(kw0);
     const int64_t bytes = (int64_t)(N - kw0_s) * ROW_BYTES;
     store_rows<T, D>(dk, make_rsrc(dK + base + (size_t)kw0_s * D, bytes), lane, scale);

@@ -54,11 +54,6 @@ __device__ __forceinline__ float add_pair16<_Float16>(unsigned x, float acc) {
 
 typedef float f32x4v __attribute__((ext_vector_type(4)));
 
-template <int S>
-struct StageTag {
-  static constexpr int value = S;
-};
-
 constexpr float kSlack = 8.f;   // how far (log2 units) the running maximum may pass m
 constexpr int kTileKeys = 32;   // keys per tile
 

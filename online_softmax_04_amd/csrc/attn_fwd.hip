@@ -86,11 +86,6 @@ __device__ __forceinline__ float add_pair<_Float16>(unsigned x, float acc) {
 }
 
 
-template <int S>
-struct StageTag {
-  static constexpr int value = S;
-};
-
 constexpr float kSlack = 8.f;  // how far (log2 units) the running maximum may pass m
 constexpr int kBM = 256;       // queries per workgroup
 // keys per tile: 128 at d = 64, where the per-tile fixed costs weigh most and the

@@ -77,6 +77,15 @@ __device__ __forceinline__ void load4_to_lds(__amdgpu_buffer_rsrc_t r, unsigned 
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 4, voff, 0, 0, 0);
 }
 
+// A compile-time stage index for double-buffered LDS tiles.  Kernels keep one
+// __shared__ array per stage and name it through this tag: the compiler tracks
+// pending direct-to-LDS loads per array, so with the stage known at compile time
+// a read of one stage does not wait for the loads into the other.
+template <int S>
+struct StageTag {
+  static constexpr int value = S;
+};
+
 // Direct loads write LDS behind the compiler's back: wait for all of this
 // wave's vector-memory operations explicitly before publishing.
 __device__ __forceinline__ void vmem_landed() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
