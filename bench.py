@@ -57,7 +57,10 @@ KERNEL_SOURCES = {
 }
 # kernel-name fragments of the three dispatches the counters are read for; the
 # probe copy is torch's elementwise multiply by 1 (reads and writes 256 MiB)
-KERNEL_NAME_PART = {"attn": "attn_fwd_mfma", "softmax": "softmax_cached", "copy": "MulFunctor"}
+# name parts that pick each kernel out of a profile of this script (the attention entry is
+# the mangled dense causal bf16 d=128 instance, not the sliding-window one)
+KERNEL_NAME_PART = {"attn": "attn_fwd_mfmaIDF16bLi128ELb1ELb0E", "softmax": "softmax_cached",
+                    "copy": "MulFunctor"}
 
 
 def source_hash(kind: str) -> str:
