@@ -66,8 +66,21 @@ class Oracle:
     # -- decoding of the storage types -------------------------------------
     @staticmethod
     def to_f64(x: np.ndarray, dtype: str | None = None) -> np.ndarray:
-        """Exact widening to float64.  ``dtype='bf16'`` marks uint16 bit patterns."""
+        """Exact widening to float64.  ``dtype='bf16'`` marks uint16 bit patterns,
+        ``dtype='fp8'`` uint8 codes of the OCP fp8 E4M3 format (sign, 4-bit exponent
+        with bias 7, 3-bit mantissa; exponent 0 is subnormal, m/8 * 2^-6; codes
+        0x7F and 0xFF are NaN; no infinities)."""
         x = np.asarray(x)
+        if dtype == "fp8":
+            if x.dtype != np.uint8:
+                raise TypeError("fp8 data must be np.uint8 codes")
+            u = x.astype(np.int64)
+            sign = np.where(u & 0x80, -1.0, 1.0)
+            e, m = (u >> 3) & 0xF, u & 0x7
+            mag = np.where(e == 0, np.ldexp(m.astype(np.float64), -9),
+                           np.ldexp((8 + m).astype(np.float64), (e - 10).astype(np.int64)))
+            mag = np.where((e == 15) & (m == 7), np.nan, mag)
+            return np.ascontiguousarray(sign * mag, dtype=np.float64)
         if dtype == "bf16" or (dtype is None and x.dtype == np.uint16):
             if x.dtype != np.uint16:
                 raise TypeError("bf16 data must be np.uint16 bit patterns")

@@ -349,6 +349,37 @@ def pin_ranged_single_key(orc):
 
 
 # ---------------------------------------------------------------------------
+# fp8 E4M3 decoding (the storage type of the fp8 forward)
+# ---------------------------------------------------------------------------
+def pin_fp8_decoder_known_codes(orc):
+    """Codes whose values the OCP E4M3 definition fixes: 1, 2, -1, the largest
+    finite value 448, the smallest normal 2^-6, the subnormals m * 2^-9, 256, zero,
+    negative zero and the NaN codes."""
+    table = {0x38: 1.0, 0x40: 2.0, 0xB8: -1.0, 0x7E: 448.0, 0xFE: -448.0, 0x08: 2.0 ** -6,
+             0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9, 0x0F: 1.875 * 2.0 ** -6, 0x78: 256.0,
+             0x2B: 0.34375, 0x00: 0.0, 0x80: -0.0, 0x3F: 1.875, 0x30: 0.5}
+    codes = np.array(sorted(table), dtype=np.uint8)
+    got = orc.to_f64(codes, "fp8")
+    for c, g in zip(codes, got):
+        assert g == table[int(c)], f"code {int(c):#04x}: {g} != {table[int(c)]}"
+    assert np.isnan(orc.to_f64(np.array([0x7F, 0xFF], np.uint8), "fp8")).all()
+
+
+def pin_fp8_decoder_order(orc):
+    """Codes 0x00 .. 0x7E increase strictly, each binade holds 8 evenly spaced
+    values, and the sign bit mirrors them."""
+    pos = orc.to_f64(np.arange(0x7F, dtype=np.uint8), "fp8")
+    assert np.all(np.diff(pos) > 0)
+    for e in range(1, 16):
+        seg = pos[8 * e: 8 * e + 8]
+        steps = np.diff(seg)
+        assert np.allclose(steps, steps[0], rtol=0, atol=0), f"binade {e} not evenly spaced"
+        assert seg[0] == 2.0 ** (e - 7)
+    neg = orc.to_f64(np.arange(0x80, 0xFF, dtype=np.uint8), "fp8")
+    assert np.array_equal(neg, -pos)
+
+
+# ---------------------------------------------------------------------------
 # decode-shaped (Nq queries at the end of Nk keys) pins
 # ---------------------------------------------------------------------------
 def pin_decode_square_is_attention(orc):

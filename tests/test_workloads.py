@@ -56,3 +56,31 @@ def test_softmax_input_recipe():
     assert np.all(spikes >= 1) and np.all(np.abs(spikes - 327.68) < 80)
     assert np.array_equal(x, workloads.softmax_input(w, rows=slice(10, 14)))
     assert np.array_equal(x[1], workloads.softmax_input(w, rows=slice(11, 12))[0])
+
+
+def test_e4m3_encoder_round_trips_every_code():
+    """The input encoder inverts the oracle's own decoder on every finite code and
+    rounds to the nearest code, ties to the even one."""
+    import oracle
+    orc = oracle.load()
+    codes = np.arange(256, dtype=np.uint8)
+    vals = orc.to_f64(codes, "fp8")
+    finite = ~np.isnan(vals) & (codes != 0x80)
+    assert np.array_equal(workloads.f32_to_e4m3(vals[finite].astype(np.float32)), codes[finite])
+    # midpoints go to the even code; just above a midpoint goes up
+    pos = vals[:0x7F]
+    mid = (pos[:-1] + pos[1:]) / 2
+    got = workloads.f32_to_e4m3(mid.astype(np.float32)).astype(np.int64)
+    lo = np.arange(0x7E)
+    assert np.array_equal(got, np.where(lo % 2 == 0, lo, lo + 1))
+    assert workloads.f32_to_e4m3(np.array([1e6, -1e6], np.float32)).tolist() == [0x7E, 0xFE]
+
+
+def test_fp8_workload_stays_in_range():
+    """The fp8 recipe's descales keep every draw of a head inside +-448 (no saturation)."""
+    w = workloads.ATTN["attn_fp8_b8h32n8192_causal"]
+    q, k, v = workloads._head_f32(w, 3, 17)
+    sq, sk, sv = w.descales
+    assert np.abs(q).max() / sq < 448 and np.abs(k).max() / sk < 448 and np.abs(v).max() / sv < 448
+    q8, k8, v8 = workloads.attn_head(w, 3, 17)
+    assert q8.dtype == np.uint8 and q8.shape == (w.N, w.d)
