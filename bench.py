@@ -20,7 +20,8 @@ Prints ONE JSON line:
   (fa_fwd_local, FLOP over visible pairs), the split-row softmax over
   4 rows of 2^24 columns (GB/s at 8 bytes per element; it moves 12), and the
   split-KV decode of one query per head against 32768 cached keys (GB/s of
-  K, V, Q, O and LSE moved once).
+  K, V, Q, O and LSE moved once), and the fp8 forward on the B8 H32 N8192 d128
+  causal shape (TFLOP/s against the dense fp8 peak).
 
 Other modes:
   --ingest-counters DIR_FETCH DIR_WRITE   turn two rocprofv3 --pmc runs
@@ -47,8 +48,10 @@ ATTN_WORKLOAD = "attn_bf16_b8h32n8192_causal"
 SOFTMAX_WORKLOAD = "softmax_4096x32768"
 SPLIT_WORKLOAD = "softmax_split_4x16777216"
 DECODE_WORKLOAD = "decode_bf16_b8h32_q1_kv32768_d128"
+FP8_WORKLOAD = "attn_fp8_b8h32n8192_causal"
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBPS = 8000.0         # MI355X HBM3E, published
+PEAK_FP8_TFLOPS = 5000.0       # MI355X dense fp8 MFMA, published
 COPY_BYTES = 256 << 20         # probe copy kernel: 256 MiB read + 256 MiB written
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.md")
 KERNEL_SOURCES = {
@@ -513,6 +516,26 @@ def main():
     del spx, spy
     print(f"[bench] split softmax {sp_ms * 1e3:.1f} us", file=sys.stderr, flush=True)
 
+    # fp8 forward on the same shape (E4M3 Q/K/V with per-tensor descales, bf16 O)
+    fw = workloads.ATTN[FP8_WORKLOAD]
+    f8 = workloads.attn_full(fw, threads=16)
+    f8q, f8k, f8v = (torch.from_numpy(t).to(dev) for t in f8)
+    del f8
+    f8o = torch.empty(f8q.shape, dtype=torch.bfloat16, device=dev)
+    f8l = torch.empty((fw.B, fw.H, fw.N), dtype=torch.float32, device=dev)
+
+    def fp8():
+        fa.fa_fwd_fp8(f8q, f8k, f8v, f8o, f8l, fw.B, fw.H, fw.N, fw.d, fw.sm_scale, *fw.descales,
+                      int(fw.causal), stream)
+
+    for _ in range(args.warmup):
+        fp8()
+    f8_each = timed(fp8, args.steps)
+    f8_ms = sum(f8_each) / args.steps
+    f8_tflops = fw.flops / (f8_ms * 1e-3) / 1e12
+    del f8q, f8k, f8v, f8o
+    print(f"[bench] fp8 forward {f8_ms:.3f} ms", file=sys.stderr, flush=True)
+
     # Split-KV decode: one query per head against a 32768-key cache (HBM-bound: K and
     # V are read once).
     dw = workloads.DECODE[DECODE_WORKLOAD]
@@ -603,6 +626,13 @@ def main():
                                        "frac": round(sp_gbps / PEAK_HBM_GBPS, 4),
                                        "kernels": ["softmax_split_partials<512,true>",
                                                    "softmax_split_normalise<512,true>"]}},
+        "fp8": {"workload": fw.name, "value": round(f8_tflops, 2), "unit": "TFLOP/s",
+                "flop_per_launch": fw.flops, "avg_launch_ms": round(f8_ms, 5),
+                "median_launch_ms": round(f8_each[len(f8_each) // 2], 5),
+                "roofline": {"bound": "mfma", "achieved": round(f8_tflops, 2),
+                             "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                             "frac": round(f8_tflops / PEAK_FP8_TFLOPS, 4),
+                             "kernel": "attn_fwd_fp8<causal>"}},
         "decode": {"workload": dw.name, "value": round(dec_gbps, 1), "unit": "GB/s",
                    "bytes_per_launch": dw.algorithmic_bytes, "workspace_bytes": dec_wsb,
                    "avg_launch_us": round(dec_ms * 1e3, 2),

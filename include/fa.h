@@ -111,6 +111,29 @@ int fa_fwd_local_f16(const void* q, const void* k, const void* v, void* o, float
                      const int* doc_start, int window, int B, int H, int N, int d, float scale,
                      hipStream_t stream);
 
+/*
+ * Attention forward with fp8 operands: Q, K, V hold OCP fp8 E4M3 codes (1 byte;
+ * sign, 4-bit exponent with bias 7, 3-bit mantissa, largest finite 448, no
+ * infinities), and the value of an element is its tensor's descale times the
+ * code's value.  O = softmax(scale * Qv Kv^T) Vv is written in bf16 and the
+ * logsumexp of the scaled scores in fp32, as for fa_fwd.  Both products run on
+ * the fp8 MFMA with fp32 accumulation; P is rounded to E4M3 (as 2^7 P, with a
+ * reference maximum that trails the row maximum by at most 1.5 in log2 units,
+ * so every stored weight stays below 448) and the row sum is taken over the
+ * rounded values.  fp8 as the next precision step
+ * is the one the "100 Days of GPU, Day 97" page names for its follow-up.
+ *
+ *  q, k, v    [B, H, N, d] E4M3 codes, 16-byte aligned, read only.
+ *  o          [B, H, N, d] bf16, 16-byte aligned, written.
+ *  lse        [B, H, N] fp32 or NULL.
+ *  q_descale, k_descale, v_descale  finite, > 0 (else FA_ERR_INVALID_ARG).
+ *  d = 128 only (else FA_ERR_UNSUPPORTED).  Every other argument, layout and
+ *  error is that of fa_fwd.
+ */
+int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+               int N, int d, float scale, float q_descale, float k_descale, float v_descale,
+               int causal, hipStream_t stream);
+
 /* Same contract with fp32 Q/K/V/O: products and sums in fp32 throughout, no
  * reduced-precision operand anywhere (the fp32 workloads' path). */
 int fa_fwd_f32(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -237,7 +260,7 @@ const char* fa_status_string(int status);
  * threads per workgroup and resident workgroups per compute unit.
  *  op: 0 = fa_fwd, 1 = fa_fwd_f16, 2 = fa_fwd_f32, 3 = online_softmax_rows,
  *  4 = fa_bwd's dQ kernel, 5 = fa_bwd's dK/dV kernel, 6 = fa_decode's
- *  chunk kernel
+ *  chunk kernel, 7 = fa_fwd_fp8
  *  (for op 3, `d` carries cols and `causal` is ignored).
  */
 typedef struct {

@@ -16,7 +16,7 @@ import os
 __all__ = [
     "FaError", "lib", "fa_fwd", "fa_fwd_f16", "fa_fwd_f32", "online_softmax_rows",
     "online_softmax_rows_split", "online_softmax_split_workspace_bytes", "softmax_split",
-    "fa_decode", "fa_decode_f16", "fa_decode_workspace_bytes", "attention_decode",
+    "fa_decode", "fa_decode_f16", "fa_decode_workspace_bytes", "attention_decode", "fa_fwd_fp8",
     "fa_status_string", "kernel_attributes", "attention", "softmax", "LIB_PATH",
     "FA_OK", "FA_ERR_INVALID_ARG", "FA_ERR_UNSUPPORTED", "FA_ERR_ALIGNMENT", "FA_ERR_HIP",
 ]
@@ -30,7 +30,7 @@ FA_ERR_ALIGNMENT = -3
 FA_ERR_HIP = -4
 
 OP_FA_FWD, OP_FA_FWD_F16, OP_FA_FWD_F32, OP_SOFTMAX = 0, 1, 2, 3
-OP_FA_BWD_DQ, OP_FA_BWD_DKDV, OP_FA_DECODE = 4, 5, 6
+OP_FA_BWD_DQ, OP_FA_BWD_DKDV, OP_FA_DECODE, OP_FA_FWD_FP8 = 4, 5, 6, 7
 
 
 class FaError(RuntimeError):
@@ -69,6 +69,8 @@ def lib() -> ctypes.CDLL:
             fn = getattr(L, name)
             fn.argtypes = [vp] * 10 + [i, i, i, i, f, i, vp]
             fn.restype = i
+        L.fa_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, f, f, f, i, vp]
+        L.fa_fwd_fp8.restype = i
         for name in ("fa_decode", "fa_decode_f16"):
             fn = getattr(L, name)
             fn.argtypes = [vp] * 6 + [ctypes.c_size_t, i, i, i, i, i, f, i, vp]
@@ -172,6 +174,15 @@ def fa_bwd_f16(q, k, v, o, dout, lse, dq, dk, dv, workspace, B, H, N, d, scale, 
     """fp16 attention backward (see include/fa.h)."""
     _bwd("fa_bwd_f16", q, k, v, o, dout, lse, dq, dk, dv, workspace, B, H, N, d, scale, causal,
          stream)
+
+
+def fa_fwd_fp8(q, k, v, o, lse, B, H, N, d, scale, q_descale, k_descale, v_descale, causal,
+               stream=None):
+    """Attention forward with fp8 E4M3 Q/K/V (value = descale * code) and bf16 O
+    (see include/fa.h)."""
+    _check(lib().fa_fwd_fp8(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), int(B), int(H), int(N),
+                            int(d), float(scale), float(q_descale), float(k_descale),
+                            float(v_descale), int(causal), _stream(stream)), "fa_fwd_fp8")
 
 
 def _decode(name, q, k, v, o, lse, workspace, workspace_bytes, B, H, Nq, Nk, d, scale, causal,

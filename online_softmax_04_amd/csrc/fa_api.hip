@@ -69,6 +69,36 @@ int attn_entry(osm::Elem elem, const void* q, const void* k, const void* v, void
   return FA_OK;
 }
 
+int fp8_entry(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+              int N, int d, float scale, float q_descale, float k_descale, float v_descale,
+              int causal, hipStream_t stream) {
+  if (!q || !k || !v || !o) return FA_ERR_INVALID_ARG;
+  if (B < 1 || H < 1 || N < 1 || d < 1) return FA_ERR_INVALID_ARG;
+  const float f[] = {scale, q_descale, k_descale, v_descale};
+  for (float x : f)
+    if (!std::isfinite(x) || !(x > 0.f)) return FA_ERR_INVALID_ARG;
+  if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
+  const uint64_t in_bytes = tensor_bytes(B, H, N, d, 1);
+  const uint64_t out_bytes = tensor_bytes(B, H, N, d, 2);
+  const uint64_t lse_bytes = tensor_bytes(B, H, N, 1, 4);
+  if (in_bytes == 0 || out_bytes == 0 || lse_bytes == 0) return FA_ERR_INVALID_ARG;
+  if (d != 128) return FA_ERR_UNSUPPORTED;
+  if ((uint64_t)N * (uint64_t)d * 2 >= ((uint64_t)1 << 31)) return FA_ERR_UNSUPPORTED;
+  const uint64_t blocks = (uint64_t)B * (uint64_t)H * (((uint64_t)N + 255) / 256);
+  if (blocks > (uint64_t)INT_MAX) return FA_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16)) return FA_ERR_ALIGNMENT;
+  if (lse && !aligned(lse, 4)) return FA_ERR_ALIGNMENT;
+  if (overlaps(o, out_bytes, q, in_bytes) || overlaps(o, out_bytes, k, in_bytes) ||
+      overlaps(o, out_bytes, v, in_bytes))
+    return FA_ERR_INVALID_ARG;
+  if (lse && (overlaps(lse, lse_bytes, o, out_bytes) || overlaps(lse, lse_bytes, q, in_bytes) ||
+              overlaps(lse, lse_bytes, k, in_bytes) || overlaps(lse, lse_bytes, v, in_bytes)))
+    return FA_ERR_INVALID_ARG;
+  hipError_t e = osm::launch_attn_fwd_fp8(q, k, v, o, lse, B, H, N, d, scale, q_descale, k_descale,
+                                          v_descale, causal != 0, stream);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 int bwd_entry(osm::Elem elem, const void* q, const void* k, const void* v, const void* o,
               const void* dout, const float* lse, void* dq, void* dk, void* dv, float* workspace,
               int B, int H, int N, int d, float scale, int causal, hipStream_t stream) {
@@ -200,6 +230,13 @@ int fa_fwd_f32(const void* q, const void* k, const void* v, void* o, float* lse,
   return attn_entry(osm::Elem::f32, q, k, v, o, lse, B, H, N, d, scale, causal, stream);
 }
 
+int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+               int N, int d, float scale, float q_descale, float k_descale, float v_descale,
+               int causal, hipStream_t stream) {
+  return fp8_entry(q, k, v, o, lse, B, H, N, d, scale, q_descale, k_descale, v_descale, causal,
+                   stream);
+}
+
 int fa_fwd_local(const void* q, const void* k, const void* v, void* o, float* lse,
                  const int* doc_start, int window, int B, int H, int N, int d, float scale,
                  hipStream_t stream) {
@@ -298,6 +335,9 @@ int fa_kernel_attributes(int op, int d, int causal, fa_kernel_attrs* out) {
   } else if (op == 4 || op == 5) {
     if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
     e = osm::attn_bwd_attributes(osm::Elem::bf16, d, causal != 0, op - 4, &attr, &threads, &blocks);
+  } else if (op == 7) {
+    if (d != 128) return FA_ERR_UNSUPPORTED;
+    e = osm::attn_fwd_fp8_attributes(causal != 0, &attr, &threads, &blocks);
   } else if (op == 6) {
     if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
     e = osm::attn_decode_attributes(d, causal != 0, &attr, &threads, &blocks);

@@ -19,6 +19,13 @@ hipError_t launch_attn_fwd_local(Elem elem, const void* q, const void* k, const 
                                  float* lse, const int* doc_start, int window, int B, int H, int N,
                                  int d, float scale, hipStream_t stream);
 
+// Attention forward with fp8 E4M3 Q/K/V (value = descale * code), bf16 O; d = 128.
+hipError_t launch_attn_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
+                               int B, int H, int N, int d, float scale, float q_descale,
+                               float k_descale, float v_descale, bool causal, hipStream_t stream);
+hipError_t attn_fwd_fp8_attributes(bool causal, hipFuncAttributes* attr, int* threads,
+                                   int* blocks_per_cu);
+
 // Attention backward (bf16 / fp16): dQ and D into `workspace` ([B, H, N] fp32),
 // then dK and dV; arguments already validated by the C ABI layer.
 hipError_t launch_attn_bwd(Elem elem, const void* q, const void* k, const void* v, const void* o,

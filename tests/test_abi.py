@@ -30,7 +30,7 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("fa_fwd", "fa_fwd_f16", "fa_fwd_f32", "fa_fwd_local", "fa_fwd_local_f16", "fa_bwd",
               "fa_bwd_f16", "fa_bwd_workspace_bytes",
-              "fa_decode", "fa_decode_f16", "fa_decode_workspace_bytes",
+              "fa_decode", "fa_decode_f16", "fa_decode_workspace_bytes", "fa_fwd_fp8",
               "online_softmax_rows", "online_softmax_rows_split",
               "online_softmax_split_workspace_bytes", "fa_status_string", "fa_kernel_attributes"):
         assert n in names
@@ -276,6 +276,26 @@ def call_decode(q=A, k=A + 64 * MB, v=A + 128 * MB, o=A + 192 * MB, lse=A + 200 
 ])
 def test_decode_validation(kw, status):
     assert call_decode(**kw) == status
+
+
+def call_fp8(q=A, k=A + 64 * MB, v=A + 128 * MB, o=A + 192 * MB, lse=A + 256 * MB, B=1, H=2,
+             N=100, d=128, scale=0.1, qs=0.5, ks=0.5, vs=0.5, causal=1):
+    return fa.lib().fa_fwd_fp8(q, k, v, o, lse, B, H, N, d, scale, qs, ks, vs, causal, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=0), fa.FA_ERR_INVALID_ARG), (dict(o=0), fa.FA_ERR_INVALID_ARG),
+    (dict(N=0), fa.FA_ERR_INVALID_ARG), (dict(scale=-1.0), fa.FA_ERR_INVALID_ARG),
+    (dict(qs=0.0), fa.FA_ERR_INVALID_ARG), (dict(ks=float("inf")), fa.FA_ERR_INVALID_ARG),
+    (dict(vs=float("nan")), fa.FA_ERR_INVALID_ARG), (dict(causal=3), fa.FA_ERR_INVALID_ARG),
+    (dict(d=64), fa.FA_ERR_UNSUPPORTED), (dict(N=1 << 23), fa.FA_ERR_UNSUPPORTED),
+    (dict(q=A + 8), fa.FA_ERR_ALIGNMENT), (dict(o=A + 192 * MB + 4), fa.FA_ERR_ALIGNMENT),
+    (dict(lse=A + 256 * MB + 1), fa.FA_ERR_ALIGNMENT),
+    (dict(o=A + 128 * MB + 16), fa.FA_ERR_INVALID_ARG),    # o over v
+    (dict(lse=A + 192 * MB + 64), fa.FA_ERR_INVALID_ARG),  # lse inside o
+])
+def test_fp8_validation(kw, status):
+    assert call_fp8(**kw) == status
 
 
 def test_python_wrappers_raise():
