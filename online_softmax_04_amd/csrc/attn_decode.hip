@@ -143,10 +143,10 @@ __global__ __launch_bounds__(64) void attn_decode_partial(
     const int64_t rest = real ? (int64_t)(Nk - t * kTileKeys) * ROW_BYTES : 0;
     const auto rk = make_rsrc(Kh + (size_t)t * kTileKeys * D, rest);
 #pragma unroll
-    for (int j = 0; j < NI; ++j) load16_to_lds(rk, kdst + j * 1024, kgoff[j]);
+    for (int j = 0; j < NI; ++j) load16_to_lds_nt(rk, kdst + j * 1024, kgoff[j]);
     const auto rv = make_rsrc(Vh + (size_t)t * kTileKeys * D, rest);
 #pragma unroll
-    for (int j = 0; j < NI; ++j) load16_to_lds(rv, vdst + j * 1024, vgoff[j]);
+    for (int j = 0; j < NI; ++j) load16_to_lds_nt(rv, vdst + j * 1024, vgoff[j]);
   };
 
   // operand read offsets, as in the forward kernel (K: row l32, logical chunk

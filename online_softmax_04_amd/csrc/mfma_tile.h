@@ -72,6 +72,12 @@ __device__ __forceinline__ void load16_to_lds(__amdgpu_buffer_rsrc_t r, unsigned
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, voff, 0, 0, 0);
 }
 
+// The same with the non-temporal cache policy (gfx940-family NT bit), for data
+// read exactly once: it streams past the caches instead of displacing reused lines.
+__device__ __forceinline__ void load16_to_lds_nt(__amdgpu_buffer_rsrc_t r, unsigned char* lds, int voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, voff, 0, 0, 2);
+}
+
 // The same for 4 bytes per lane: lane i's word lands at lds + 4 i.
 __device__ __forceinline__ void load4_to_lds(__amdgpu_buffer_rsrc_t r, unsigned char* lds, int voff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 4, voff, 0, 0, 0);
