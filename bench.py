@@ -336,8 +336,18 @@ def cpu_baseline(w, q, k, v, target_s: float = 15.0):
     while secs < target_s * 2 / 3 and rows < 2048:
         rows = int(min(2048, rows * min(8.0, max(1.5, target_s / max(secs, 1e-3)))))
         flops, secs = run(rows)
+    # the single-thread rate on a small sample of the same rows (a few seconds)
+    t1_flops, t1 = 0.0, time.perf_counter()
+    for b, h in heads[:: max(1, len(heads) // 16)]:
+        r1 = workloads.attn_sample_rows(w, b, h, count=16)
+        orc.attention_head(q[b, h], k[b, h], v[b, h], w.sm_scale, w.causal, r1, dtype=w.dtype,
+                           threads=1)
+        vis = (r1 + 1) if w.causal else np.full(r1.shape, w.N)
+        t1_flops += float(np.sum(4.0 * vis * w.d))
+    t1 = time.perf_counter() - t1
     return {
         "value": flops / secs / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+        "one_thread_value": t1_flops / t1 / 1e12,
         "sample": f"{rows} seeded query rows in each of the {len(heads)} heads "
                   f"({flops:.3g} FLOP counted as 4*visible_keys*d per row) in {secs:.1f} s; "
                   "fp64 three-pass definition, one materialised score row at a time",
