@@ -51,6 +51,8 @@ class Oracle:
         lib.oracle_attention_rows.restype = None
         lib.oracle_attention_ranged.argtypes = [dp, dp, dp, L, L, D, lp, lp, lp, L, dp, dp, I]
         lib.oracle_attention_ranged.restype = None
+        lib.oracle_attention_keyset.argtypes = [dp, dp, dp, L, D, lp, lp, lp, L, L, dp, dp, I]
+        lib.oracle_attention_keyset.restype = None
         lib.oracle_attention_probs.argtypes = [dp, dp, L, L, D, I, L, dp]
         lib.oracle_attention_probs.restype = None
         lib.oracle_online_normaliser.argtypes = [dp, L, dp, dp]
@@ -140,6 +142,54 @@ class Oracle:
                                          rows.ctypes.data_as(lp), rows.size, self._p(o),
                                          self._p(lse), threads or default_threads())
         return o, lse
+
+    def attention_keyset(self, q, k, v, scale: float, keysets, rows=None,
+                         dtype: str | None = None, threads: int | None = None):
+        """O [len(rows), d] and LSE of one head where query rows[r] sees exactly the keys
+        keysets[r] (an index array; empty: O = 0, LSE = -inf)."""
+        q, k, v = (self.to_f64(t, dtype) for t in (q, k, v))
+        n, d = q.shape
+        rows = np.arange(n, dtype=np.int64) if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
+        if len(keysets) != rows.size:
+            raise ValueError("one key set per row")
+        sizes = np.array([len(ks) for ks in keysets], dtype=np.int64)
+        ptr = np.zeros(rows.size + 1, np.int64)
+        np.cumsum(sizes, out=ptr[1:])
+        keys = (np.concatenate([np.asarray(ks, np.int64) for ks in keysets]) if rows.size
+                else np.zeros(0, np.int64))
+        if keys.size and (keys.min() < 0 or keys.max() >= k.shape[0]):
+            raise ValueError("key index out of range")
+        keys = np.ascontiguousarray(keys if keys.size else np.zeros(1, np.int64))
+        o = np.empty((rows.size, d), np.float64)
+        lse = np.empty(rows.size, np.float64)
+        lp = ctypes.POINTER(ctypes.c_long)
+        self.lib.oracle_attention_keyset(self._p(q), self._p(k), self._p(v), d, float(scale),
+                                         ptr.ctypes.data_as(lp), keys.ctypes.data_as(lp),
+                                         rows.ctypes.data_as(lp), rows.size,
+                                         int(sizes.max()) if sizes.size else 1,
+                                         self._p(o), self._p(lse), threads or default_threads())
+        return o, lse
+
+    @staticmethod
+    def block_sparse_keys(n, i, blk_ptr, blk_idx, qblock, kblock, causal):
+        """The keys query i sees under a block-sparse pattern: every key of the key
+        blocks listed for its query block (i // qblock) in CSR form (blk_ptr, blk_idx),
+        cut at n, and only keys j <= i when causal."""
+        qb = i // qblock
+        blocks = np.asarray(blk_idx[blk_ptr[qb]:blk_ptr[qb + 1]], np.int64)
+        keys = [np.arange(b * kblock, min(n, (b + 1) * kblock)) for b in blocks]
+        keys = np.concatenate(keys) if keys else np.zeros(0, np.int64)
+        return keys[keys <= i] if causal else keys
+
+    def attention_blocksparse(self, q, k, v, scale: float, causal: bool, blk_ptr, blk_idx,
+                              qblock: int, kblock: int, rows=None, dtype: str | None = None,
+                              threads: int | None = None):
+        """O and LSE of one head under a block-sparse pattern (see block_sparse_keys)."""
+        n = q.shape[0]
+        rows = np.arange(n, dtype=np.int64) if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
+        sets = [self.block_sparse_keys(n, int(i), blk_ptr, blk_idx, qblock, kblock, causal)
+                for i in rows]
+        return self.attention_keyset(q, k, v, scale, sets, rows, dtype=dtype, threads=threads)
 
     def attention_decode(self, q, k, v, scale: float, causal: bool, dtype: str | None = None,
                          threads: int | None = None):

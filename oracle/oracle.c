@@ -40,6 +40,9 @@
  *                                (sliding windows and document boundaries of
  *                                "Online Softmax: Tiling Across a Reduction").
  *
+ *   oracle_attention_keyset   -- the same with an explicit key list per query
+ *                                (block-sparse masks, same paragraph).
+ *
  *   oracle_attention_backward -- dV = P^T dO, dP = dO V^T,
  *                                dS = P o (dP - D) with D_i = sum_j P_ij dP_ij
  *                                (= <dO_i, O_i>; optionally from a given O),
@@ -228,6 +231,56 @@ void oracle_attention_ranged(const double* q, const double* k, const double* v, 
                              long nrows, double* o, double* lse, int nthreads) {
   ranged_ctx c = {q, k, v, n, d, scale, lo, hi, rows, o, lse};
   parallel_rows(ranged_one_row, &c, nrows, n, nthreads);
+}
+
+/* Attention where query rows[r] sees exactly the keys keys[ptr[r]] .. keys[ptr[r+1] - 1]
+ * (any set, in any order): the block-sparse masks of "Online Softmax: Tiling Across a
+ * Reduction" (the paragraph on sliding windows, block sparsity and document masks)
+ * written as an explicit key list per query.  The same three passes over that list.
+ * A query whose list is empty has no softmax: its output row is zero and its
+ * logsumexp is -inf. */
+typedef struct {
+  const double *q, *k, *v;
+  long d;
+  double scale;
+  const long *ptr, *keys, *rows;
+  double *o, *lse;
+} keyset_ctx;
+
+static void keyset_one_row(void* p, long r, double* sc) {
+  keyset_ctx* c = (keyset_ctx*)p;
+  const long b0 = c->ptr[r], cnt = c->ptr[r + 1] - c->ptr[r];
+  const double* qv = c->q + c->rows[r] * c->d;
+  double* out = c->o + r * c->d;
+  for (long e = 0; e < c->d; ++e) out[e] = 0.0;
+  if (cnt == 0) {
+    c->lse[r] = -INFINITY;
+    return;
+  }
+  double mx = -INFINITY;
+  for (long t = 0; t < cnt; ++t) {            /* scores; pass 1: their maximum */
+    const double* kk = c->k + c->keys[b0 + t] * c->d;
+    double dot = 0.0;
+    for (long e = 0; e < c->d; ++e) dot += kk[e] * qv[e];
+    sc[t] = dot * c->scale;
+    if (sc[t] > mx) mx = sc[t];
+  }
+  double den = 0.0;
+  for (long t = 0; t < cnt; ++t) den += exp(sc[t] - mx);   /* pass 2: the sum */
+  for (long t = 0; t < cnt; ++t) {                          /* pass 3: P V */
+    const double w = exp(sc[t] - mx) / den;
+    const double* vv = c->v + c->keys[b0 + t] * c->d;
+    for (long e = 0; e < c->d; ++e) out[e] += w * vv[e];
+  }
+  c->lse[r] = mx + log(den);
+}
+
+/* max_keys bounds ptr[r+1] - ptr[r] (the score scratch of one row) */
+void oracle_attention_keyset(const double* q, const double* k, const double* v, long d, double scale,
+                             const long* ptr, const long* keys, const long* rows, long nrows,
+                             long max_keys, double* o, double* lse, int nthreads) {
+  keyset_ctx c = {q, k, v, d, scale, ptr, keys, rows, o, lse};
+  parallel_rows(keyset_one_row, &c, nrows, max_keys > 0 ? max_keys : 1, nthreads);
 }
 
 /* the probability row p_ij = exp(s_ij - m_i)/l_i (zero for hidden keys) */

@@ -349,6 +349,83 @@ def pin_ranged_single_key(orc):
 
 
 # ---------------------------------------------------------------------------
+# key-set (block-sparse) pins
+# ---------------------------------------------------------------------------
+def pin_keyset_full_and_prefix_sets_are_attention(orc):
+    """Every key, or keys 0..i, is dense or causal attention."""
+    r = _rng(70)
+    n, d = 29, 5
+    q, k, v = (r.normal(size=(n, d)) for _ in range(3))
+    o1, l1 = orc.attention_keyset(q, k, v, 0.6, [np.arange(n)] * n)
+    o2, l2 = orc.attention_head(q, k, v, 0.6, False)
+    _close(o1, o2, 1e-14, "full key sets")
+    _close(l1, l2, 1e-14, "full key sets LSE")
+    o1, l1 = orc.attention_keyset(q, k, v, 0.6, [np.arange(i + 1) for i in range(n)])
+    o2, l2 = orc.attention_head(q, k, v, 0.6, True)
+    _close(o1, o2, 1e-14, "prefix key sets")
+    _close(l1, l2, 1e-14, "prefix key sets LSE")
+
+
+def pin_keyset_gaps_are_a_slice(orc):
+    """A set with gaps is plain attention of q_i over the listed rows of K and V,
+    whatever their order."""
+    r = _rng(71)
+    n, d = 40, 4
+    q, k, v = (r.normal(size=(n, d)) for _ in range(3))
+    sets = [np.sort(r.choice(n, size=int(r.integers(1, n)), replace=False)) for _ in range(n)]
+    o, lse = orc.attention_keyset(q, k, v, 0.7, sets)
+    shuffled = [r.permutation(ks) for ks in sets]
+    o2, l2 = orc.attention_keyset(q, k, v, 0.7, shuffled)
+    _close(o, o2, 1e-14, "key order")
+    _close(lse, l2, 1e-13, "key order LSE")
+    for i in (0, 7, 39):
+        ks = sets[i]
+        oi, li = orc.attention_head(np.tile(q[i], (ks.size, 1)), k[ks], v[ks], 0.7, False, rows=[0])
+        _close(o[i], oi[0], 1e-14, f"gapped set row {i}")
+        _close([lse[i]], li, 1e-14, f"gapped set LSE row {i}")
+
+
+def pin_keyset_single_and_empty(orc):
+    """One key j: O_i = v_j and LSE_i = scale <q_i, k_j>.  No key: O_i = 0, LSE_i = -inf."""
+    r = _rng(72)
+    n, d = 9, 3
+    q, k, v = (r.normal(size=(n, d)) for _ in range(3))
+    j = r.integers(0, n, size=n)
+    sets = [np.array([jj]) for jj in j]
+    sets[4] = np.zeros(0, np.int64)
+    o, lse = orc.attention_keyset(q, k, v, 0.3, sets)
+    for i in range(n):
+        if i == 4:
+            assert np.all(o[i] == 0.0) and lse[i] == -np.inf
+        else:
+            _close(o[i], v[j[i]], 1e-15, f"single key {i}")
+            _close([lse[i]], [0.3 * float(q[i] @ k[j[i]])], 1e-14, f"single key LSE {i}")
+
+
+def pin_block_sparse_keys(orc):
+    """The block-sparse key rule: listed key blocks of the query's block, cut at N
+    and at the diagonal when causal; a full pattern is dense attention."""
+    n, qb, kb = 300, 128, 64
+    n_qb, n_kb = -(-n // qb), -(-n // kb)
+    blk_ptr = np.arange(n_qb + 1) * n_kb
+    blk_idx = np.tile(np.arange(n_kb), n_qb)
+    assert np.array_equal(orc.block_sparse_keys(n, 299, blk_ptr, blk_idx, qb, kb, False), np.arange(n))
+    assert np.array_equal(orc.block_sparse_keys(n, 130, blk_ptr, blk_idx, qb, kb, True), np.arange(131))
+    ptr2 = np.array([0, 2, 2, 3])
+    idx2 = np.array([1, 3, 4])
+    assert np.array_equal(orc.block_sparse_keys(n, 5, ptr2, idx2, qb, kb, False),
+                          np.r_[np.arange(64, 128), np.arange(192, 256)])
+    assert orc.block_sparse_keys(n, 200, ptr2, idx2, qb, kb, False).size == 0
+    assert np.array_equal(orc.block_sparse_keys(n, 290, ptr2, idx2, qb, kb, True), np.arange(256, 291))
+    r = _rng(73)
+    q, k, v = (r.normal(size=(n, 4)) for _ in range(3))
+    o1, l1 = orc.attention_blocksparse(q, k, v, 0.5, True, blk_ptr, blk_idx, qb, kb, rows=[0, 64, 299])
+    o2, l2 = orc.attention_head(q, k, v, 0.5, True, rows=[0, 64, 299])
+    _close(o1, o2, 1e-14, "full block pattern")
+    _close(l1, l2, 1e-14, "full block pattern LSE")
+
+
+# ---------------------------------------------------------------------------
 # fp8 E4M3 decoding (the storage type of the fp8 forward)
 # ---------------------------------------------------------------------------
 def pin_fp8_decoder_known_codes(orc):

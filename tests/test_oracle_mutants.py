@@ -56,6 +56,12 @@ MUTATIONS = [
     ("ranged_keys_from_zero", "for (long e = 0; e < c->d; ++e) acc += qrow[e] * kj[e];",
      "for (long e = 0; e < c->d; ++e) acc += qrow[e] * c->k[(j - j0) * c->d + e];"),
     ("ranged_query_is_key", "acc += qrow[e] * kj[e];", "acc += kj[e] * kj[e];"),
+    ("keyset_ignores_list", "const double* kk = c->k + c->keys[b0 + t] * c->d;",
+     "const double* kk = c->k + t * c->d;"),
+    ("keyset_values_misplaced", "const double* vv = c->v + c->keys[b0 + t] * c->d;",
+     "const double* vv = c->v + c->keys[b0] * c->d;"),
+    ("keyset_sum_unshifted", "den += exp(sc[t] - mx);", "den += exp(sc[t]);"),
+    ("keyset_empty_is_nan", "    c->lse[r] = -INFINITY;\n    return;", "    c->lse[r] = NAN;\n    return;"),
     ("partition_drops_rows", "jobs[t].end = (t + 1) * per < nrows ? (t + 1) * per : nrows;",
      "jobs[t].end = (t + 1) * per < nrows ? (t + 1) * per - 1 : nrows;"),
 ]
