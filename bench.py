@@ -17,7 +17,8 @@ Prints ONE JSON line:
               sample of query rows of the same workload.
   After the timed steps, beside them: the backward (fa_bwd) on the same
   inputs, the forward with a sliding window over packed documents
-  (fa_fwd_local, FLOP over visible pairs), the split-row softmax over
+  (fa_fwd_local, FLOP over visible pairs), the forward under a block-sparse
+  pattern (fa_fwd_blocksparse, FLOP over visible pairs), the split-row softmax over
   4 rows of 2^24 columns (GB/s at 8 bytes per element; it moves 12), and the
   split-KV decode of one query per head against 32768 cached keys (GB/s of
   K, V, Q, O and LSE moved once), and the fp8 forward on the B8 H32 N8192 d128
@@ -62,7 +63,7 @@ KERNEL_SOURCES = {
 # probe copy is torch's elementwise multiply by 1 (reads and writes 256 MiB)
 # name parts that pick each kernel out of a profile of this script (the attention entry is
 # the mangled dense causal bf16 d=128 instance, not the sliding-window one)
-KERNEL_NAME_PART = {"attn": "attn_fwd_mfmaIDF16bLi128ELb1ELb0E", "softmax": "softmax_cached",
+KERNEL_NAME_PART = {"attn": "attn_fwd_mfmaIDF16bLi128ELb1ELi0E", "softmax": "softmax_cached",
                     "copy": "MulFunctor"}
 
 
@@ -441,6 +442,15 @@ def main():
     print(f"[bench] timed {args.steps} steps: attention {attn_ms:.3f} ms, softmax {sm_ms * 1e3:.1f} us",
           file=sys.stderr, flush=True)
 
+    def timed(fn, steps):
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+        for i in range(steps):
+            ev[i][0].record(stream)
+            fn()
+            ev[i][1].record(stream)
+        torch.cuda.synchronize()
+        return sorted(e[0].elapsed_time(e[1]) for e in ev)
+
     # The backward pass (fa_bwd) on the same inputs, after the timed steps: the
     # forward's O and logsumexp, a synthetic upstream gradient.  Reported beside
     # the step, not inside it.
@@ -496,6 +506,28 @@ def main():
     loc_tflops = loc_flop / (loc_ms * 1e-3) / 1e12
     print(f"[bench] local {loc_ms:.3f} ms", file=sys.stderr, flush=True)
 
+    # Block-sparse pattern (sink block, diagonal band, 10 % random blocks) on the
+    # same inputs; FLOP counted over the visible query-key pairs only.
+    bw = workloads.BLOCKSPARSE_WORKLOAD
+    bs_ptr, bs_idx = workloads.block_sparse_pattern(w.N, bw["pattern_seed"], band=bw["band"],
+                                                    sinks=bw["sinks"], p_random=bw["p_random"],
+                                                    causal=w.causal)
+    bs_pairs = workloads.block_sparse_pairs(w.N, bs_ptr, bs_idx, w.causal)
+    bs_flop = 4.0 * w.d * w.B * w.H * bs_pairs
+    bs_ptr_d = torch.from_numpy(bs_ptr).to(dev)
+    bs_idx_d = torch.from_numpy(bs_idx).to(dev)
+
+    def blocksparse():
+        fa.fa_fwd_blocksparse(qd, kd, vd, lod, lsed, bs_ptr_d, bs_idx_d, bs_idx.size, w.B, w.H,
+                              w.N, w.d, w.sm_scale, int(w.causal), stream)
+
+    for _ in range(args.warmup):
+        blocksparse()
+    bs_each = timed(blocksparse, args.steps)
+    bs_ms = sum(bs_each) / args.steps
+    bs_tflops = bs_flop / (bs_ms * 1e-3) / 1e12
+    print(f"[bench] blocksparse {bs_ms:.3f} ms", file=sys.stderr, flush=True)
+
     # Split-row softmax on few very long rows (several workgroups per row), and
     # the one-workgroup-per-row path on the same input for comparison.
     spw = workloads.SOFTMAX[SPLIT_WORKLOAD]
@@ -506,15 +538,6 @@ def main():
 
     def split():
         fa.online_softmax_rows_split(spx, spy, spw.rows, spw.cols, sp_ws, sp_wsb, stream)
-
-    def timed(fn, steps):
-        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
-        for i in range(steps):
-            ev[i][0].record(stream)
-            fn()
-            ev[i][1].record(stream)
-        torch.cuda.synchronize()
-        return sorted(e[0].elapsed_time(e[1]) for e in ev)
 
     for _ in range(args.warmup):
         split()
@@ -625,6 +648,14 @@ def main():
                                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                                "frac": round(loc_tflops / PEAK_BF16_TFLOPS, 4),
                                "kernel": "attn_fwd_mfma<bf16,128,causal,local>"}},
+        "blocksparse": {"workload": bw["name"], "value": round(bs_tflops, 2), "unit": "TFLOP/s",
+                        "visible_pairs_per_head": bs_pairs, "listed_blocks": int(bs_idx.size),
+                        "flop_per_launch": bs_flop, "avg_launch_ms": round(bs_ms, 5),
+                        "median_launch_ms": round(bs_each[len(bs_each) // 2], 5),
+                        "roofline": {"bound": "mfma", "achieved": round(bs_tflops, 2),
+                                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                                     "frac": round(bs_tflops / PEAK_BF16_TFLOPS, 4),
+                                     "kernel": "attn_fwd_mfma<bf16,128,causal,blocksparse>"}},
         "softmax_split": {"workload": spw.name, "value": round(sp_gbps, 1), "unit": "GB/s",
                           "bytes_per_launch": spw.algorithmic_bytes,
                           "bytes_moved_per_launch": 12 * spw.rows * spw.cols,

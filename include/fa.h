@@ -112,6 +112,37 @@ int fa_fwd_local_f16(const void* q, const void* k, const void* v, void* o, float
                      hipStream_t stream);
 
 /*
+ * Attention forward under a block-sparse pattern, the block-level skip of the
+ * structured-sparsity paragraph of "Online Softmax: Tiling Across a Reduction",
+ * bfloat16 operands.  Queries are grouped in blocks of 256 rows (query block qb
+ * = rows 256 qb .. 256 qb + 255) and keys in blocks of 128; query i of every
+ * batch and head sees the keys of the key blocks listed for its query block,
+ *   blk_idx[blk_ptr[qb]] .. blk_idx[blk_ptr[qb + 1] - 1],   qb = i / 256,
+ * keys j < N only, and with causal = 1 only keys j <= i.
+ *  blk_ptr  int32[ceil(N / 256) + 1], device, 4-byte aligned, read only:
+ *           CSR row offsets, blk_ptr[0] = 0, non-decreasing, last = nnz.
+ *  blk_idx  int32[nnz], device, 4-byte aligned, read only: key-block indices
+ *           in 0 .. ceil(N / 128) - 1, ascending and distinct within a query
+ *           block (may be NULL when nnz = 0).
+ *  nnz      number of listed (query block, key block) pairs, >= 0.
+ *  Only listed key blocks are read from memory.  A query that sees no key
+ *  (an empty list, or causal with every listed key after it) gets O = 0 and
+ *  lse = -inf.  Row offsets are clamped to 0 .. nnz, and a block index outside
+ *  0 .. ceil(N / 128) - 1 contributes no keys, so no pattern makes the kernel
+ *  read or write outside its buffers; a block listed twice is counted twice.
+ *  Every other argument, layout, error and the arithmetic are those of fa_fwd;
+ *  blk_ptr and blk_idx may not overlap o or lse (FA_ERR_INVALID_ARG).
+ */
+int fa_fwd_blocksparse(const void* q, const void* k, const void* v, void* o, float* lse,
+                       const int* blk_ptr, const int* blk_idx, int nnz, int B, int H, int N,
+                       int d, float scale, int causal, hipStream_t stream);
+
+/* Same contract with IEEE half-precision Q/K/V/O. */
+int fa_fwd_blocksparse_f16(const void* q, const void* k, const void* v, void* o, float* lse,
+                           const int* blk_ptr, const int* blk_idx, int nnz, int B, int H, int N,
+                           int d, float scale, int causal, hipStream_t stream);
+
+/*
  * Attention forward with fp8 operands: Q, K, V hold OCP fp8 E4M3 codes (1 byte;
  * sign, 4-bit exponent with bias 7, 3-bit mantissa, largest finite 448, no
  * infinities), and the value of an element is its tensor's descale times the
@@ -260,7 +291,8 @@ const char* fa_status_string(int status);
  * threads per workgroup and resident workgroups per compute unit.
  *  op: 0 = fa_fwd, 1 = fa_fwd_f16, 2 = fa_fwd_f32, 3 = online_softmax_rows,
  *  4 = fa_bwd's dQ kernel, 5 = fa_bwd's dK/dV kernel, 6 = fa_decode's
- *  chunk kernel, 7 = fa_fwd_fp8
+ *  chunk kernel, 7 = fa_fwd_fp8, 8 = fa_fwd_blocksparse, 9 = fa_fwd_local
+ *  (causal = 1 only)
  *  (for op 3, `d` carries cols and `causal` is ignored).
  */
 typedef struct {

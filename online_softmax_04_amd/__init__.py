@@ -17,6 +17,8 @@ __all__ = [
     "FaError", "lib", "fa_fwd", "fa_fwd_f16", "fa_fwd_f32", "online_softmax_rows",
     "online_softmax_rows_split", "online_softmax_split_workspace_bytes", "softmax_split",
     "fa_decode", "fa_decode_f16", "fa_decode_workspace_bytes", "attention_decode", "fa_fwd_fp8",
+    "fa_fwd_local", "fa_fwd_local_f16", "fa_fwd_blocksparse", "fa_fwd_blocksparse_f16",
+    "attention_blocksparse", "SPARSE_QBLOCK", "SPARSE_KBLOCK",
     "fa_status_string", "kernel_attributes", "attention", "softmax", "LIB_PATH",
     "FA_OK", "FA_ERR_INVALID_ARG", "FA_ERR_UNSUPPORTED", "FA_ERR_ALIGNMENT", "FA_ERR_HIP",
 ]
@@ -31,6 +33,10 @@ FA_ERR_HIP = -4
 
 OP_FA_FWD, OP_FA_FWD_F16, OP_FA_FWD_F32, OP_SOFTMAX = 0, 1, 2, 3
 OP_FA_BWD_DQ, OP_FA_BWD_DKDV, OP_FA_DECODE, OP_FA_FWD_FP8 = 4, 5, 6, 7
+OP_FA_FWD_BLOCKSPARSE, OP_FA_FWD_LOCAL = 8, 9
+
+# block sizes of a block-sparse pattern: query rows and keys per block
+SPARSE_QBLOCK, SPARSE_KBLOCK = 256, 128
 
 
 class FaError(RuntimeError):
@@ -64,6 +70,10 @@ def lib() -> ctypes.CDLL:
         for name in ("fa_fwd_local", "fa_fwd_local_f16"):
             fn = getattr(L, name)
             fn.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, vp]
+            fn.restype = i
+        for name in ("fa_fwd_blocksparse", "fa_fwd_blocksparse_f16"):
+            fn = getattr(L, name)
+            fn.argtypes = [vp] * 7 + [i, i, i, i, i, f, i, vp]
             fn.restype = i
         for name in ("fa_bwd", "fa_bwd_f16"):
             fn = getattr(L, name)
@@ -155,6 +165,28 @@ def fa_fwd_local(q, k, v, o, lse, doc_start, window, B, H, N, d, scale, stream=N
 def fa_fwd_local_f16(q, k, v, o, lse, doc_start, window, B, H, N, d, scale, stream=None):
     """fp16 causal attention with a sliding window and document starts (see include/fa.h)."""
     _local("fa_fwd_local_f16", q, k, v, o, lse, doc_start, window, B, H, N, d, scale, stream)
+
+
+def _blocksparse(name, q, k, v, o, lse, blk_ptr, blk_idx, nnz, B, H, N, d, scale, causal,
+                 stream):
+    fn = getattr(lib(), name)
+    _check(fn(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(blk_ptr), _ptr(blk_idx),
+              int(nnz), int(B), int(H), int(N), int(d), float(scale), int(causal),
+              _stream(stream)), name)
+
+
+def fa_fwd_blocksparse(q, k, v, o, lse, blk_ptr, blk_idx, nnz, B, H, N, d, scale, causal,
+                       stream=None):
+    """bf16 attention under a block-sparse pattern in CSR form (see include/fa.h)."""
+    _blocksparse("fa_fwd_blocksparse", q, k, v, o, lse, blk_ptr, blk_idx, nnz, B, H, N, d, scale,
+                 causal, stream)
+
+
+def fa_fwd_blocksparse_f16(q, k, v, o, lse, blk_ptr, blk_idx, nnz, B, H, N, d, scale, causal,
+                           stream=None):
+    """fp16 attention under a block-sparse pattern in CSR form (see include/fa.h)."""
+    _blocksparse("fa_fwd_blocksparse_f16", q, k, v, o, lse, blk_ptr, blk_idx, nnz, B, H, N, d,
+                 scale, causal, stream)
 
 
 def _bwd(name, q, k, v, o, dout, lse, dq, dk, dv, workspace, B, H, N, d, scale, causal, stream):
@@ -275,6 +307,39 @@ def attention(q, k, v, causal: bool = False, scale: float | None = None, out=Non
     if lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     _attn(name, q, k, v, out, lse, B, H, N, d, scale, causal, stream)
+    return out, lse
+
+
+def attention_blocksparse(q, k, v, blk_ptr, blk_idx, causal: bool = False,
+                          scale: float | None = None, out=None, lse=None, stream=None):
+    """O, LSE of [B, H, N, d] bf16 or fp16 device tensors under a block-sparse pattern:
+    blk_ptr (int32, ceil(N / SPARSE_QBLOCK) + 1) and blk_idx (int32, nnz) on the device
+    list, per query block, the key blocks of SPARSE_KBLOCK keys it sees."""
+    import torch
+    for t in (q, k, v):
+        if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+            raise TypeError("q, k, v must be device tensors")
+        if not t.is_contiguous() or t.dim() != 4 or t.shape != q.shape or t.dtype != q.dtype:
+            raise ValueError("q, k, v must be contiguous [B, H, N, d] tensors of one dtype")
+    names = {torch.bfloat16: "fa_fwd_blocksparse", torch.float16: "fa_fwd_blocksparse_f16"}
+    if q.dtype not in names:
+        raise TypeError(f"unsupported dtype {q.dtype}")
+    B, H, N, d = q.shape
+    n_qb = (N + SPARSE_QBLOCK - 1) // SPARSE_QBLOCK
+    for t, n in ((blk_ptr, n_qb + 1), (blk_idx, None)):
+        if (not isinstance(t, torch.Tensor) or t.device != q.device or t.dtype != torch.int32
+                or t.dim() != 1 or not t.is_contiguous() or (n is not None and t.numel() != n)):
+            raise ValueError("blk_ptr (ceil(N / 256) + 1) and blk_idx must be contiguous int32 "
+                             "device vectors")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    _blocksparse(names[q.dtype], q, k, v, out, lse, blk_ptr,
+                 blk_idx if blk_idx.numel() else None, blk_idx.numel(), B, H, N, d, scale,
+                 causal, stream)
     return out, lse
 
 

@@ -95,12 +95,15 @@ constexpr int kBN = D == 64 ? 128 : 64;
 constexpr int kThreads = 512;  // 8 waves: two groups of 4, one wave of each group per SIMD
 
 
-template <typename T, int D, bool CAUSAL, bool LOCAL>
+// MASK: kMaskNone, kMaskLocal or kMaskSparse (kernels.h)
+template <typename T, int D, bool CAUSAL, int MASK>
 __global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE, int BH,
     int N, int n_mtiles, float c, int xcd_groups, int H, const int* __restrict__ doc_start,
-    int window) {
+    int window, const int* __restrict__ blk_ptr, const int* __restrict__ blk_idx, int nnz) {
+  constexpr bool LOCAL = MASK == kMaskLocal;
+  constexpr bool SPARSE = MASK == kMaskSparse;
   using v8 = typename Mma<T>::v8;
   constexpr int ROW_BYTES = D * 2;
   constexpr int BN = kBN<D>;                  // keys per tile
@@ -114,7 +117,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(
   static_assert(NI >= 1, "tile shape");
   // One array per stage and operand, always named at compile time: the compiler
   // tracks the pending direct loads per array, so a read of one stage does not
-  // wait for the loads into the other.  Tile t lives in stage (t - t0) & 1.
+  // wait for the loads into the other.  The tile at list position i (below)
+  // lives in stage i & 1.
   __shared__ __attribute__((aligned(1024))) unsigned char kb0[TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) unsigned char kb1[TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) unsigned char vb0[TILE_BYTES];
@@ -212,6 +216,38 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(
   }
   // tile t holds keys this wave computes with
   auto act = [&](int t) { return (!LOCAL || t >= tw0) && t < n_w; };
+
+  // The workgroup walks a list of key tiles: position i holds tile t0 + i for the
+  // dense and sliding-window kernels; for block-sparse, the tiles of the key
+  // blocks listed for this query block (ascending, as the pattern lists them).
+  // Causal masking and the key count N apply on top.
+  constexpr int kTilesPerBlock = kSparseKBlock / BN;
+  const int nkb = (N + kSparseKBlock - 1) / kSparseKBlock;  // key blocks
+  int n_list = n_kt - t0, p0 = 0;
+  if constexpr (SPARSE) {
+    static_assert(kBM == kSparseQBlock && kSparseKBlock % BN == 0, "pattern blocks");
+    // the row's range, clamped into [0, nnz]
+    p0 = min(max(blk_ptr[mt], 0), nnz);
+    n_list = (min(max(blk_ptr[mt + 1], p0), nnz) - p0) * kTilesPerBlock;
+  }
+  auto tile_of = [&](int i) -> int {
+    if constexpr (SPARSE) {
+      // a block index outside [0, nkb) maps past the last key: no load, no compute
+      const unsigned b = (unsigned)blk_idx[p0 + i / kTilesPerBlock];
+      return (int)min(b, (unsigned)nkb) * kTilesPerBlock + i % kTilesPerBlock;
+    } else {
+      return t0 + i;
+    }
+  };
+  // list position i holds keys this wave computes with
+  auto act_at = [&](int i) {
+    if constexpr (SPARSE) {
+      const int j0 = tile_of(i) * BN;
+      return j0 < N && (!CAUSAL || j0 <= qw0 + 31);
+    } else {
+      return act(t0 + i);
+    }
+  };
 
   // ---- loader: global -> LDS directly, no registers ------------------------------------
   // A wave-wide 16-byte-per-lane buffer load with the LDS flag writes lane i's
@@ -368,41 +404,43 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(
     }
   };
 
-  // One tile t in stage S = (t - t0) & 1: slot X(t), the barrier, slot Y(t).
-  // For the dense kernel t0 = 0 and act(t) is t < n_w.
-  auto tile = [&](int t, auto st) __attribute__((always_inline)) {
+  // The tile at list position i, in stage S = i & 1: slot X, the barrier, slot Y.
+  auto tile = [&](int i, auto st) __attribute__((always_inline)) {
     constexpr int S = decltype(st)::value;
     const StageTag<S> cur;
     const StageTag<S ^ 1> other;
-    // ---- slot X(t)
+    const bool a_cur = act_at(i);
+    // ---- slot X
     if (group == 0) {
-      if (act(t)) sm(t);
+      if (a_cur) sm(tile_of(i));
     } else {
       __builtin_amdgcn_s_setprio(1);
-      if (t > t0 && act(t - 1) && act(t)) {
+      const bool a_prev = i > 0 && act_at(i - 1);
+      if (a_prev && a_cur) {
         pv_qk(other, cur);
       } else {
-        if (t > t0 && act(t - 1)) pv(other);
-        if (act(t)) qk(cur);
+        if (a_prev) pv(other);
+        if (a_cur) qk(cur);
       }
       __builtin_amdgcn_s_setprio(0);
     }
-    loads_landed();  // K(t+1), V(t)
+    loads_landed();  // K of position i + 1, V of position i
     __syncthreads();
-    // ---- slot Y(t)
-    if (t + 2 < n_kt) load_k(t + 2, cur);
-    if (t + 1 < n_kt) load_v(t + 1, other);
+    // ---- slot Y
+    if (i + 2 < n_list) load_k(tile_of(i + 2), cur);
+    if (i + 1 < n_list) load_v(tile_of(i + 1), other);
     if (group == 0) {
       __builtin_amdgcn_s_setprio(1);
-      if (act(t) && act(t + 1)) {
+      const bool a_next = i + 1 < n_list && act_at(i + 1);
+      if (a_cur && a_next) {
         pv_qk(cur, other);
       } else {
-        if (act(t)) pv(cur);
-        if (act(t + 1)) qk(other);
+        if (a_cur) pv(cur);
+        if (a_next) qk(other);
       }
       __builtin_amdgcn_s_setprio(0);
     } else {
-      if (act(t)) sm(t);
+      if (a_cur) sm(tile_of(i));
     }
   };
 
@@ -419,7 +457,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(
   // groups in opposite phases.  The dense kernel starts at tile t0 = 0; the
   // LOCAL one at the workgroup's first visible tile, each wave computing from
   // its own first tile tw0.
-  load_k(t0, StageTag<0>{});
+  if (n_list > 0) load_k(tile_of(0), StageTag<0>{});
   loads_landed();
   __syncthreads();
   // Retire the Q loads here.  Left pending, they would make the first MFMA that
@@ -428,26 +466,27 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(
 #pragma unroll
   for (int kb = 0; kb < NK; ++kb) asm volatile("" ::"v"(qf[kb]));
   // slot Y(t0 - 1): load K(t0+1), V(t0); group 0 computes S(t0)
-  if (t0 + 1 < n_kt) load_k(t0 + 1, StageTag<1>{});
-  load_v(t0, StageTag<0>{});
-  if (group == 0 && act(t0)) {
+  if (1 < n_list) load_k(tile_of(1), StageTag<1>{});
+  if (n_list > 0) load_v(tile_of(0), StageTag<0>{});
+  if (group == 0 && n_list > 0 && act_at(0)) {
     __builtin_amdgcn_s_setprio(1);
     qk(StageTag<0>{});
     __builtin_amdgcn_s_setprio(0);
   }
   __syncthreads();
-  for (int t = t0; t < n_kt; t += 2) {
-    tile(t, StageTag<0>{});
-    if (t + 1 < n_kt) tile(t + 1, StageTag<1>{});
+  for (int i = 0; i < n_list; i += 2) {
+    tile(i, StageTag<0>{});
+    if (i + 1 < n_list) tile(i + 1, StageTag<1>{});
   }
-  // slot X(n_kt): group 1 finishes the last PV
-  if (group == 1 && act(n_kt - 1)) {
-    if (((n_kt - 1 - t0) & 1) == 0) pv(StageTag<0>{}); else pv(StageTag<1>{});
+  // slot X after the last tile: group 1 finishes the last PV
+  if (group == 1 && n_list > 0 && act_at(n_list - 1)) {
+    if (((n_list - 1) & 1) == 0) pv(StageTag<0>{}); else pv(StageTag<1>{});
   }
 
   // ---- epilogue: O / l, logsumexp --------------------------------------------------
   const float l_tot = sum_halves(l_run);
-  const float inv = 1.f / l_tot;
+  // a block-sparse row can see no key at all: O = 0 and logsumexp -inf there
+  const float inv = (SPARSE && l_tot == 0.f) ? 0.f : 1.f / l_tot;
   {
     // rows past N fall outside the buffer and are dropped
     const auto ro = make_rsrc(O + base + (size_t)qw0_s * D, (int64_t)(N - qw0_s) * ROW_BYTES);
@@ -463,7 +502,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(
     }
   }
   if (LSE != nullptr && hf == 0 && qi < N)
-    LSE[(size_t)bh * N + qi] = (m_run + log2f(l_tot)) * kLn2;
+    LSE[(size_t)bh * N + qi] = (SPARSE && l_tot == 0.f) ? kNegInf : (m_run + log2f(l_tot)) * kLn2;
 }
 
 // ------------------------------------------------------------------------------------
@@ -560,16 +599,18 @@ __global__ __launch_bounds__(256) void attn_fwd_f32(const float* __restrict__ Q,
 }
 
 template <typename T, int D, bool C>
-const void* mfma_fn(bool local) {
+const void* mfma_fn(int mask) {
+  if (mask == kMaskSparse) return (const void*)attn_fwd_mfma<T, D, C, kMaskSparse>;
   if constexpr (C) {
-    if (local) return (const void*)attn_fwd_mfma<T, D, true, true>;
+    if (mask == kMaskLocal) return (const void*)attn_fwd_mfma<T, D, true, kMaskLocal>;
   }
-  return (const void*)attn_fwd_mfma<T, D, C, false>;
+  return (const void*)attn_fwd_mfma<T, D, C, kMaskNone>;
 }
 
-// local = the causal sliding-window / document variant (requires causal)
+// mask: kMaskNone, kMaskLocal (requires causal) or kMaskSparse; 16-bit operands
+// only for the last two
 const void* pick_attn(Elem elem, int d, bool causal, int* threads, int* rows_per_block,
-                      bool local = false) {
+                      int mask = kMaskNone) {
   if (elem == Elem::f32) {
     *threads = 256;
     *rows_per_block = 4 * (64 / (d / 64));
@@ -579,11 +620,11 @@ const void* pick_attn(Elem elem, int d, bool causal, int* threads, int* rows_per
   *threads = kThreads;
   *rows_per_block = kBM;
   if (elem == Elem::bf16) {
-    if (d == 64) return causal ? mfma_fn<__bf16, 64, true>(local) : mfma_fn<__bf16, 64, false>(false);
-    return causal ? mfma_fn<__bf16, 128, true>(local) : mfma_fn<__bf16, 128, false>(false);
+    if (d == 64) return causal ? mfma_fn<__bf16, 64, true>(mask) : mfma_fn<__bf16, 64, false>(mask);
+    return causal ? mfma_fn<__bf16, 128, true>(mask) : mfma_fn<__bf16, 128, false>(mask);
   }
-  if (d == 64) return causal ? mfma_fn<_Float16, 64, true>(local) : mfma_fn<_Float16, 64, false>(false);
-  return causal ? mfma_fn<_Float16, 128, true>(local) : mfma_fn<_Float16, 128, false>(false);
+  if (d == 64) return causal ? mfma_fn<_Float16, 64, true>(mask) : mfma_fn<_Float16, 64, false>(mask);
+  return causal ? mfma_fn<_Float16, 128, true>(mask) : mfma_fn<_Float16, 128, false>(mask);
 }
 
 }  // namespace
@@ -605,9 +646,13 @@ hipError_t launch_attn_fwd(Elem elem, const void* q, const void* k, const void* 
   int xcd_groups = (BH % 8 == 0) ? 1 : 0;
   const int* doc_start = nullptr;
   int window = 0;
+  const int* blk_ptr = nullptr;
+  const int* blk_idx = nullptr;
+  int nnz = 0;
   void* args[] = {(void*)&q, (void*)&k, (void*)&v, (void*)&o, (void*)&lse, (void*)&BH,
                   (void*)&N, (void*)&n_mtiles, (void*)&c, (void*)&xcd_groups, (void*)&H,
-                  (void*)&doc_start, (void*)&window};
+                  (void*)&doc_start, (void*)&window, (void*)&blk_ptr, (void*)&blk_idx,
+                  (void*)&nnz};
   return hipLaunchKernel(fn, dim3(grid), dim3(threads), args, 0, stream);
 }
 
@@ -615,22 +660,46 @@ hipError_t launch_attn_fwd_local(Elem elem, const void* q, const void* k, const 
                                  float* lse, const int* doc_start, int window, int B, int H, int N,
                                  int d, float scale, hipStream_t stream) {
   int threads, rows_per_block;
-  const void* fn = pick_attn(elem, d, true, &threads, &rows_per_block, true);
+  const void* fn = pick_attn(elem, d, true, &threads, &rows_per_block, kMaskLocal);
   int BH = B * H;
   int n_mtiles = (N + rows_per_block - 1) / rows_per_block;
   float c = scale * kLog2e;
   const int grid = BH * n_mtiles;
   int xcd_groups = (BH % 8 == 0) ? 1 : 0;
+  const int* blk_ptr = nullptr;
+  const int* blk_idx = nullptr;
+  int nnz = 0;
   void* args[] = {(void*)&q, (void*)&k, (void*)&v, (void*)&o, (void*)&lse, (void*)&BH,
                   (void*)&N, (void*)&n_mtiles, (void*)&c, (void*)&xcd_groups, (void*)&H,
-                  (void*)&doc_start, (void*)&window};
+                  (void*)&doc_start, (void*)&window, (void*)&blk_ptr, (void*)&blk_idx,
+                  (void*)&nnz};
+  return hipLaunchKernel(fn, dim3(grid), dim3(threads), args, 0, stream);
+}
+
+hipError_t launch_attn_fwd_blocksparse(Elem elem, const void* q, const void* k, const void* v,
+                                       void* o, float* lse, const int* blk_ptr,
+                                       const int* blk_idx, int nnz, int B, int H, int N, int d,
+                                       float scale, bool causal, hipStream_t stream) {
+  int threads, rows_per_block;
+  const void* fn = pick_attn(elem, d, causal, &threads, &rows_per_block, kMaskSparse);
+  int BH = B * H;
+  int n_mtiles = (N + rows_per_block - 1) / rows_per_block;
+  float c = scale * kLog2e;
+  const int grid = BH * n_mtiles;
+  int xcd_groups = (BH % 8 == 0) ? 1 : 0;
+  const int* doc_start = nullptr;
+  int window = 0;
+  void* args[] = {(void*)&q, (void*)&k, (void*)&v, (void*)&o, (void*)&lse, (void*)&BH,
+                  (void*)&N, (void*)&n_mtiles, (void*)&c, (void*)&xcd_groups, (void*)&H,
+                  (void*)&doc_start, (void*)&window, (void*)&blk_ptr, (void*)&blk_idx,
+                  (void*)&nnz};
   return hipLaunchKernel(fn, dim3(grid), dim3(threads), args, 0, stream);
 }
 
 hipError_t attn_fwd_attributes(Elem elem, int d, bool causal, hipFuncAttributes* attr,
-                               int* threads, int* blocks_per_cu) {
+                               int* threads, int* blocks_per_cu, int mask) {
   int rows_per_block;
-  const void* fn = pick_attn(elem, d, causal, threads, &rows_per_block);
+  const void* fn = pick_attn(elem, d, causal, threads, &rows_per_block, mask);
   hipError_t e = hipFuncGetAttributes(attr, fn);
   if (e != hipSuccess) return e;
   return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, fn, *threads, 0);

@@ -25,9 +25,12 @@ uint64_t tensor_bytes(int B, int H, int N, int d, uint64_t elem) {
   return (uint64_t)n;
 }
 
+// mask: osm::kMaskNone, kMaskLocal (doc_start, window) or kMaskSparse (blk_ptr,
+// blk_idx, nnz); the masked kernels take 16-bit operands only.
 int attn_entry(osm::Elem elem, const void* q, const void* k, const void* v, void* o, float* lse,
                int B, int H, int N, int d, float scale, int causal, hipStream_t stream,
-               bool local = false, const int* doc_start = nullptr, int window = 0) {
+               int mask = osm::kMaskNone, const int* doc_start = nullptr, int window = 0,
+               const int* blk_ptr = nullptr, const int* blk_idx = nullptr, int nnz = 0) {
   if (!q || !k || !v || !o) return FA_ERR_INVALID_ARG;
   if (B < 1 || H < 1 || N < 1 || d < 1) return FA_ERR_INVALID_ARG;
   if (!std::isfinite(scale) || !(scale > 0.f)) return FA_ERR_INVALID_ARG;
@@ -50,7 +53,23 @@ int attn_entry(osm::Elem elem, const void* q, const void* k, const void* v, void
   if (lse && (overlaps(lse, lse_bytes, o, bytes) || overlaps(lse, lse_bytes, q, bytes) ||
               overlaps(lse, lse_bytes, k, bytes) || overlaps(lse, lse_bytes, v, bytes)))
     return FA_ERR_INVALID_ARG;
-  if (local) {
+  if (mask == osm::kMaskSparse) {
+    // CSR over the query blocks: n_qb + 1 row offsets, nnz key-block indices
+    const uint64_t n_qb = ((uint64_t)N + osm::kSparseQBlock - 1) / osm::kSparseQBlock;
+    if (!blk_ptr || nnz < 0 || (nnz > 0 && !blk_idx)) return FA_ERR_INVALID_ARG;
+    if (!aligned(blk_ptr, 4) || (blk_idx && !aligned(blk_idx, 4))) return FA_ERR_ALIGNMENT;
+    const uint64_t ptr_bytes = (n_qb + 1) * 4, idx_bytes = (uint64_t)nnz * 4;
+    if (overlaps(blk_ptr, ptr_bytes, o, bytes) || (lse && overlaps(blk_ptr, ptr_bytes, lse, lse_bytes)))
+      return FA_ERR_INVALID_ARG;
+    if (nnz > 0 && (overlaps(blk_idx, idx_bytes, o, bytes) ||
+                    (lse && overlaps(blk_idx, idx_bytes, lse, lse_bytes))))
+      return FA_ERR_INVALID_ARG;
+    hipError_t e = osm::launch_attn_fwd_blocksparse(elem, q, k, v, o, lse, blk_ptr,
+                                                    nnz > 0 ? blk_idx : blk_ptr, nnz, B, H, N, d,
+                                                    scale, causal != 0, stream);
+    return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+  }
+  if (mask == osm::kMaskLocal) {
     if (window < 0) return FA_ERR_INVALID_ARG;
     if (doc_start) {
       if (!aligned(doc_start, 4)) return FA_ERR_ALIGNMENT;
@@ -240,15 +259,29 @@ int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
 int fa_fwd_local(const void* q, const void* k, const void* v, void* o, float* lse,
                  const int* doc_start, int window, int B, int H, int N, int d, float scale,
                  hipStream_t stream) {
-  return attn_entry(osm::Elem::bf16, q, k, v, o, lse, B, H, N, d, scale, 1, stream, true, doc_start,
-                    window);
+  return attn_entry(osm::Elem::bf16, q, k, v, o, lse, B, H, N, d, scale, 1, stream, osm::kMaskLocal,
+                    doc_start, window);
 }
 
 int fa_fwd_local_f16(const void* q, const void* k, const void* v, void* o, float* lse,
                      const int* doc_start, int window, int B, int H, int N, int d, float scale,
                      hipStream_t stream) {
-  return attn_entry(osm::Elem::f16, q, k, v, o, lse, B, H, N, d, scale, 1, stream, true, doc_start,
-                    window);
+  return attn_entry(osm::Elem::f16, q, k, v, o, lse, B, H, N, d, scale, 1, stream, osm::kMaskLocal,
+                    doc_start, window);
+}
+
+int fa_fwd_blocksparse(const void* q, const void* k, const void* v, void* o, float* lse,
+                       const int* blk_ptr, const int* blk_idx, int nnz, int B, int H, int N,
+                       int d, float scale, int causal, hipStream_t stream) {
+  return attn_entry(osm::Elem::bf16, q, k, v, o, lse, B, H, N, d, scale, causal, stream,
+                    osm::kMaskSparse, nullptr, 0, blk_ptr, blk_idx, nnz);
+}
+
+int fa_fwd_blocksparse_f16(const void* q, const void* k, const void* v, void* o, float* lse,
+                           const int* blk_ptr, const int* blk_idx, int nnz, int B, int H, int N,
+                           int d, float scale, int causal, hipStream_t stream) {
+  return attn_entry(osm::Elem::f16, q, k, v, o, lse, B, H, N, d, scale, causal, stream,
+                    osm::kMaskSparse, nullptr, 0, blk_ptr, blk_idx, nnz);
 }
 
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
@@ -335,6 +368,11 @@ int fa_kernel_attributes(int op, int d, int causal, fa_kernel_attrs* out) {
   } else if (op == 4 || op == 5) {
     if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
     e = osm::attn_bwd_attributes(osm::Elem::bf16, d, causal != 0, op - 4, &attr, &threads, &blocks);
+  } else if (op == 8 || op == 9) {
+    if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+    if (op == 9 && causal == 0) return FA_ERR_INVALID_ARG;  // the window kernel is causal
+    e = osm::attn_fwd_attributes(osm::Elem::bf16, d, causal != 0, &attr, &threads, &blocks,
+                                 op == 8 ? osm::kMaskSparse : osm::kMaskLocal);
   } else if (op == 7) {
     if (d != 128) return FA_ERR_UNSUPPORTED;
     e = osm::attn_fwd_fp8_attributes(causal != 0, &attr, &threads, &blocks);

@@ -7,17 +7,31 @@ namespace osm {
 
 enum class Elem { bf16, f16, f32 };
 
+// Key masks of the 16-bit attention forward: none (dense, or causal alone), the
+// causal sliding window over packed documents, and block-sparse (per block of
+// kSparseQBlock queries, a list of kSparseKBlock-key blocks).
+constexpr int kMaskNone = 0, kMaskLocal = 1, kMaskSparse = 2;
+constexpr int kSparseQBlock = 256;
+constexpr int kSparseKBlock = 128;
+
 // Attention forward on `stream`; arguments already validated by the C ABI layer.
 hipError_t launch_attn_fwd(Elem elem, const void* q, const void* k, const void* v, void* o,
                            float* lse, int B, int H, int N, int d, float scale, bool causal,
                            hipStream_t stream);
 hipError_t attn_fwd_attributes(Elem elem, int d, bool causal, hipFuncAttributes* attr,
-                               int* threads, int* blocks_per_cu);
+                               int* threads, int* blocks_per_cu, int mask = kMaskNone);
 // Causal attention where query i also skips keys before max(doc_start[b, i], i - window + 1)
 // (doc_start may be null, window 0 = unbounded); bf16 / fp16 only.
 hipError_t launch_attn_fwd_local(Elem elem, const void* q, const void* k, const void* v, void* o,
                                  float* lse, const int* doc_start, int window, int B, int H, int N,
                                  int d, float scale, hipStream_t stream);
+// Block-sparse attention: query block qb (rows 256 qb ..) sees the 128-key blocks
+// blk_idx[blk_ptr[qb] .. blk_ptr[qb + 1]) (CSR over ceil(N / 256) query blocks,
+// nnz entries, shared by all batches and heads), with causal masking on top.
+hipError_t launch_attn_fwd_blocksparse(Elem elem, const void* q, const void* k, const void* v,
+                                       void* o, float* lse, const int* blk_ptr,
+                                       const int* blk_idx, int nnz, int B, int H, int N, int d,
+                                       float scale, bool causal, hipStream_t stream);
 
 // Attention forward with fp8 E4M3 Q/K/V (value = descale * code), bf16 O; d = 128.
 hipError_t launch_attn_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,

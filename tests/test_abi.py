@@ -28,7 +28,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ("fa_fwd", "fa_fwd_f16", "fa_fwd_f32", "fa_fwd_local", "fa_fwd_local_f16", "fa_bwd",
+    for n in ("fa_fwd", "fa_fwd_f16", "fa_fwd_f32", "fa_fwd_local", "fa_fwd_local_f16",
+              "fa_fwd_blocksparse", "fa_fwd_blocksparse_f16", "fa_bwd",
               "fa_bwd_f16", "fa_bwd_workspace_bytes",
               "fa_decode", "fa_decode_f16", "fa_decode_workspace_bytes", "fa_fwd_fp8",
               "online_softmax_rows", "online_softmax_rows_split",
@@ -129,6 +130,32 @@ def call_local(name="fa_fwd_local", doc=A + 320 * MB, window=16, **kw):
 ])
 def test_local_validation(name, kw, status):
     assert call_local(name, **kw) == status
+
+
+def call_sparse(name="fa_fwd_blocksparse", ptr=A + 320 * MB, idx=A + 384 * MB, nnz=4, **kw):
+    base = dict(q=A, k=A + 64 * MB, v=A + 128 * MB, o=A + 192 * MB, lse=A + 256 * MB, B=1, H=2,
+                N=128, d=64, scale=0.125, causal=0)
+    base.update(kw)
+    fn = getattr(fa.lib(), name)
+    return fn(base["q"], base["k"], base["v"], base["o"], base["lse"], ptr, idx, nnz, base["B"],
+              base["H"], base["N"], base["d"], base["scale"], base["causal"], None)
+
+
+# every case fails validation before a launch (the addresses are not device memory)
+@pytest.mark.parametrize("name", ["fa_fwd_blocksparse", "fa_fwd_blocksparse_f16"])
+@pytest.mark.parametrize("kw,status", [
+    (dict(ptr=0), fa.FA_ERR_INVALID_ARG), (dict(nnz=-1), fa.FA_ERR_INVALID_ARG),
+    (dict(idx=0), fa.FA_ERR_INVALID_ARG), (dict(q=0), fa.FA_ERR_INVALID_ARG),
+    (dict(N=0), fa.FA_ERR_INVALID_ARG), (dict(scale=float("nan")), fa.FA_ERR_INVALID_ARG),
+    (dict(causal=2), fa.FA_ERR_INVALID_ARG), (dict(d=32), fa.FA_ERR_UNSUPPORTED),
+    (dict(ptr=A + 320 * MB + 2), fa.FA_ERR_ALIGNMENT), (dict(idx=A + 384 * MB + 1), fa.FA_ERR_ALIGNMENT),
+    (dict(ptr=A + 192 * MB + 8), fa.FA_ERR_INVALID_ARG),  # inside o
+    (dict(idx=A + 256 * MB), fa.FA_ERR_INVALID_ARG),      # on lse
+    (dict(ptr=A + 256 * MB - 4), fa.FA_ERR_INVALID_ARG),  # reaches into lse
+    (dict(o=A + 64 * MB + 16), fa.FA_ERR_INVALID_ARG),    # o over k
+])
+def test_blocksparse_validation(name, kw, status):
+    assert call_sparse(name, **kw) == status
 
 
 # backward: ten buffers, 64 MiB apart (each [1, 2, 128, 64] 16-bit tensor is 32 KiB)

@@ -1,0 +1,160 @@
+"""Block-sparse attention (fa_fwd_blocksparse) on the GPU, through the C ABI,
+against the fp64 oracle's explicit key lists: query i sees every key of the
+128-key blocks listed for its 256-row query block, cut at N, and with causal
+only keys j <= i.  Gates are the stated ones (bf16 / fp16: max-abs 1e-2,
+relative L2 5e-3; the logsumexp scaled by max(1, |lse|)); rows that see no key
+must hold O = 0 and lse = -inf exactly."""
+import numpy as np
+import pytest
+import torch
+
+import online_softmax_04_amd as fa
+import oracle
+import workloads
+from gpu_util import gate, say, to_device, to_f64
+
+pytestmark = pytest.mark.gpu
+
+ENTRY = {"bf16": fa.fa_fwd_blocksparse, "f16": fa.fa_fwd_blocksparse_f16}
+QB, KB = fa.SPARSE_QBLOCK, fa.SPARSE_KBLOCK
+
+
+@pytest.fixture(scope="module")
+def orc():
+    return oracle.load()
+
+
+def csr(lists):
+    """(blk_ptr, blk_idx) int32 from one key-block list per query block."""
+    ptr = np.zeros(len(lists) + 1, np.int32)
+    ptr[1:] = np.cumsum([len(x) for x in lists])
+    idx = np.asarray([b for x in lists for b in x], np.int32)
+    return ptr, idx
+
+
+def run_sparse(q, k, v, ptr, idx, causal, dtype, scale):
+    B, H, N, d = q.shape
+    qd, kd, vd = (to_device(t, dtype) for t in (q, k, v))
+    o = torch.empty_like(qd)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    ptr_d = torch.from_numpy(np.ascontiguousarray(ptr, np.int32)).cuda()
+    idx_d = torch.from_numpy(np.ascontiguousarray(idx, np.int32)).cuda() if len(idx) else None
+    ENTRY[dtype](qd, kd, vd, o, lse, ptr_d, idx_d, len(idx), B, H, N, d, scale, int(causal))
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def check(orc, name, q, k, v, ptr, idx, causal, dtype, scale, o, lse, rows_of=None, heads=None,
+          oracle_ptr=None, oracle_idx=None):
+    """Compare every (or the sampled) rows of the given heads with the oracle; the
+    oracle may be handed another (equivalent) pattern than the kernel."""
+    B, H, N, d = q.shape
+    optr = ptr if oracle_ptr is None else oracle_ptr
+    oidx = idx if oracle_idx is None else oracle_idx
+    go, ro, gl, rl = [], [], [], []
+    for b, h in heads or [(b, h) for b in range(B) for h in range(H)]:
+        rows = np.arange(N) if rows_of is None else rows_of(b, h)
+        oo, ll = orc.attention_blocksparse(q[b, h], k[b, h], v[b, h], scale, causal, optr, oidx,
+                                           QB, KB, rows=rows, dtype=dtype)
+        rt = torch.from_numpy(rows).cuda()
+        go.append(to_f64(o[b, h].index_select(0, rt)))
+        gl.append(to_f64(lse[b, h].index_select(0, rt)))
+        ro.append(oo)
+        rl.append(ll)
+    go, ro, gl, rl = (np.concatenate(x) for x in (go, ro, gl, rl))
+    empty = np.isneginf(rl)
+    say(f"  {name}: {int(empty.sum())} of {rl.size} checked rows see no key")
+    if empty.any():
+        assert np.all(np.isneginf(gl[empty])), f"{name}: lse of a row without keys is not -inf"
+        assert np.all(go[empty] == 0.0), f"{name}: O of a row without keys is not 0"
+    if (~empty).any():
+        gate(f"{name} O", go[~empty], ro[~empty], dtype)
+        gate(f"{name} LSE", gl[~empty][:, None], rl[~empty][:, None], dtype, scaled=True)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("N,causal,p", [
+    (1, False, 0.0), (1, True, 0.0), (200, False, 0.5), (300, True, 0.3), (777, False, 0.2),
+    (1000, True, 0.2), (1500, True, 0.0), (2100, False, 0.1),
+])
+def test_blocksparse_shapes(orc, dtype, d, N, causal, p):
+    B, H = 2, 2
+    say(f"[attention blocksparse] dtype={dtype} d={d} N={N} causal={causal} p={p}")
+    q, k, v = workloads.random_attn(B, H, N, d, dtype, seed=N + d + int(causal) + 7)
+    ptr, idx = workloads.block_sparse_pattern(N, seed=N + int(causal), p_random=p, causal=causal)
+    scale = 1.0 / np.sqrt(d)
+    o, lse = run_sparse(q, k, v, ptr, idx, causal, dtype, scale)
+    check(orc, f"blocksparse {dtype} d{d} N{N} c{int(causal)} p{p}", q, k, v, ptr, idx, causal,
+          dtype, scale, o, lse)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_irregular_lists(orc, d):
+    """Hand-made lists: empty query blocks, a single far block, a block past the
+    diagonal (causal hides it), the ragged last key block, every block."""
+    N = 1400  # 6 query blocks, 11 key blocks (the last one 120 keys)
+    lists = [[], [10], [0, 5, 9], list(range(11)), [3, 4], [1, 10]]
+    ptr, idx = csr(lists)
+    q, k, v = workloads.random_attn(1, 3, N, d, "bf16", seed=d + 3)
+    for causal in (False, True):
+        say(f"[attention blocksparse] irregular d={d} causal={causal}")
+        o, lse = run_sparse(q, k, v, ptr, idx, causal, "bf16", 0.09)
+        check(orc, f"irregular d{d} c{int(causal)}", q, k, v, ptr, idx, causal, "bf16", 0.09, o,
+              lse)
+
+
+def test_empty_pattern():
+    """nnz = 0: every row sees no key, O = 0 and lse = -inf."""
+    N = 600
+    q, k, v = workloads.random_attn(1, 2, N, 128, "bf16", seed=5)
+    ptr = np.zeros((N + QB - 1) // QB + 1, np.int32)
+    o, lse = run_sparse(q, k, v, ptr, np.zeros(0, np.int32), True, "bf16", 0.1)
+    assert torch.all(o.float() == 0) and torch.all(torch.isneginf(lse))
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_full_pattern_equals_dense(d, causal):
+    """Every key block listed for every query block: the same tiles in the same
+    order as fa_fwd, so the same bits."""
+    B, H, N = 1, 3, 1000
+    q, k, v = workloads.random_attn(B, H, N, d, "bf16", seed=17 + d)
+    nqb, nkb = (N + QB - 1) // QB, (N + KB - 1) // KB
+    ptr, idx = csr([list(range(nkb))] * nqb)
+    o1, l1 = run_sparse(q, k, v, ptr, idx, causal, "bf16", 0.1)
+    qd, kd, vd = (to_device(t, "bf16") for t in (q, k, v))
+    o2 = torch.empty_like(qd)
+    l2 = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    fa.fa_fwd(qd, kd, vd, o2, l2, B, H, N, d, 0.1, int(causal))
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
+
+
+def test_out_of_range_blocks_read_nothing(orc):
+    """Block indices outside 0 .. ceil(N / 128) - 1 contribute no keys, and row
+    offsets are clamped to 0 .. nnz: the result is that of the valid blocks."""
+    N = 700  # 3 query blocks, 6 key blocks
+    lists = [[0, 6, 2147483647], [-1, 1, 2], [3, 4, 5, 100]]
+    ptr, idx = csr(lists)
+    valid_ptr, valid_idx = csr([[b for b in x if 0 <= b < 6] for x in lists])
+    q, k, v = workloads.random_attn(1, 2, N, 64, "bf16", seed=23)
+    o, lse = run_sparse(q, k, v, ptr, idx, False, "bf16", 0.125)
+    check(orc, "out-of-range blocks", q, k, v, ptr, idx, False, "bf16", 0.125, o, lse,
+          oracle_ptr=valid_ptr, oracle_idx=valid_idx)
+
+
+def test_blocksparse_headline_shape(orc):
+    """B8 H32 N8192 d128 causal under the seeded sink + band + random pattern, in its
+    full launch; 256 seeded rows per head of four heads checked."""
+    bw = workloads.BLOCKSPARSE_WORKLOAD
+    w = workloads.ATTN[bw["base"]]
+    say(f"[attention blocksparse] {bw['name']}")
+    q, k, v = workloads.attn_full(w, threads=16)
+    ptr, idx = workloads.block_sparse_pattern(w.N, bw["pattern_seed"], band=bw["band"],
+                                              sinks=bw["sinks"], p_random=bw["p_random"],
+                                              causal=w.causal)
+    o, lse = run_sparse(q, k, v, ptr, idx, w.causal, "bf16", w.sm_scale)
+    check(orc, bw["name"], q, k, v, ptr, idx, w.causal, "bf16", w.sm_scale, o, lse,
+          rows_of=lambda b, h: workloads.attn_sample_rows(w, b, h),
+          heads=[(0, 0), (3, 17), (5, 2), (7, 31)])

@@ -1,5 +1,6 @@
 """The seeded input generators: determinism, rounding and the recipes' structure."""
 import numpy as np
+import pytest
 import torch
 
 import workloads
@@ -84,3 +85,34 @@ def test_fp8_workload_stays_in_range():
     assert np.abs(q).max() / sq < 448 and np.abs(k).max() / sk < 448 and np.abs(v).max() / sv < 448
     q8, k8, v8 = workloads.attn_head(w, 3, 17)
     assert q8.dtype == np.uint8 and q8.shape == (w.N, w.d)
+
+
+@pytest.mark.parametrize("N,causal,p", [(1, True, 0.0), (300, False, 0.3), (1400, True, 0.2),
+                                        (8192, True, 0.1)])
+def test_block_sparse_pattern_is_valid_csr(N, causal, p):
+    """Offsets start at 0 and grow to nnz; each list ascending, distinct, in range,
+    holding the sink block and the diagonal block of its query block; causal lists
+    hold no block that starts after the query block's last row."""
+    ptr, idx = workloads.block_sparse_pattern(N, seed=3, p_random=p, causal=causal)
+    nqb, nkb = (N + 255) // 256, (N + 127) // 128
+    assert ptr.dtype == np.int32 and idx.dtype == np.int32 and ptr.shape == (nqb + 1,)
+    assert ptr[0] == 0 and ptr[-1] == idx.size and np.all(np.diff(ptr) >= 0)
+    for qb in range(nqb):
+        lst = idx[ptr[qb]:ptr[qb + 1]]
+        last_row = min(N, 256 * (qb + 1)) - 1
+        assert np.all(np.diff(lst) > 0) and lst.min() >= 0 and lst.max() < nkb
+        assert 0 in lst and last_row // 128 in lst
+        if causal:
+            assert np.all(lst * 128 <= last_row)
+    assert np.array_equal(ptr, workloads.block_sparse_pattern(N, seed=3, p_random=p, causal=causal)[0])
+
+
+@pytest.mark.parametrize("N,causal", [(300, False), (700, True), (1400, True)])
+def test_block_sparse_pairs_counts_the_oracle_key_lists(N, causal):
+    """The pair count the benchmark prices equals the sum of the oracle's key-list
+    lengths over all queries."""
+    import oracle
+    ptr, idx = workloads.block_sparse_pattern(N, seed=11, p_random=0.3, causal=causal)
+    total = sum(len(oracle.Oracle.block_sparse_keys(N, i, ptr, idx, 256, 128, causal))
+                for i in range(N))
+    assert workloads.block_sparse_pairs(N, ptr, idx, causal) == total

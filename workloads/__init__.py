@@ -280,6 +280,61 @@ def local_ranges(doc_start_row: np.ndarray, window: int) -> tuple[np.ndarray, np
     return np.clip(lo, 0, i), i
 
 
+def block_sparse_pattern(N: int, seed: int, qblock: int = 256, kblock: int = 128,
+                         band: int = 2, sinks: int = 1, p_random: float = 0.1,
+                         causal: bool = True) -> tuple[np.ndarray, np.ndarray]:
+    """(blk_ptr, blk_idx) int32 CSR over ceil(N / qblock) query blocks: for each
+    query block, ascending distinct key-block indices of the first `sinks` key
+    blocks, the `band` key blocks ending at the block holding the query block's
+    last row together with every key block overlapping the query block, and each
+    other key block with probability p_random; with causal, only key blocks that
+    start at or before the query block's last row are drawn."""
+    rng = np.random.default_rng([BASE_SEED + 900, seed, N, qblock, kblock])
+    nqb = (N + qblock - 1) // qblock
+    nkb = (N + kblock - 1) // kblock
+    ptr = [0]
+    idx: list[int] = []
+    for qb in range(nqb):
+        first_row = qb * qblock
+        last_row = min(N, first_row + qblock) - 1
+        top = last_row // kblock if causal else nkb - 1   # last key block drawn from
+        chosen = set(range(min(sinks, top + 1)))
+        diag_hi = last_row // kblock
+        chosen.update(range(max(0, min(first_row // kblock, diag_hi - band + 1)), diag_hi + 1))
+        if not causal:
+            chosen.update(range(first_row // kblock, diag_hi + 1))
+        draws = rng.random(nkb) < p_random
+        chosen.update(int(b) for b in np.nonzero(draws[:top + 1])[0])
+        blocks = sorted(b for b in chosen if 0 <= b < nkb and b <= top)
+        idx.extend(blocks)
+        ptr.append(len(idx))
+    return np.asarray(ptr, np.int32), np.asarray(idx, np.int32)
+
+
+def block_sparse_pairs(N: int, blk_ptr: np.ndarray, blk_idx: np.ndarray, causal: bool,
+                       qblock: int = 256, kblock: int = 128) -> int:
+    """Number of (query, key) pairs a pattern lets through (per head), counting
+    keys j < N and, with causal, j <= i."""
+    total = 0
+    for qb in range(len(blk_ptr) - 1):
+        r0, r1 = qb * qblock, min(N, (qb + 1) * qblock)
+        for b in blk_idx[blk_ptr[qb]:blk_ptr[qb + 1]]:
+            j0, j1 = int(b) * kblock, min(N, (int(b) + 1) * kblock)
+            if not causal:
+                total += (r1 - r0) * (j1 - j0)
+                continue
+            for i in range(r0, r1):
+                total += max(0, min(j1, i + 1) - j0)
+    return total
+
+
+# block-sparse forward: the B8 H32 N8192 d128 causal shape under a pattern of one
+# sink block, a two-block band at the diagonal and 10 % random blocks (K rows x
+# U(0.5, 2) as the dense workload)
+BLOCKSPARSE_WORKLOAD = dict(name="attn_bf16_b8h32n8192_blocksparse", base="attn_bf16_b8h32n8192_causal",
+                            band=2, sinks=1, p_random=0.1, pattern_seed=7)
+
+
 # --------------------------------------------------------------------------
 # decode-shaped attention: Nq queries at the end of Nk cached keys
 # --------------------------------------------------------------------------
