@@ -239,11 +239,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(
       return t0 + i;
     }
   };
+  // last key a tile may start at and still hold a key this wave computes with;
+  // opaque to the compiler for the reason n_w is
+  int j0_max = CAUSAL ? min(qw0 + 31, N - 1) : N - 1;
+  if constexpr (SPARSE) asm volatile("" : "+v"(j0_max));
   // list position i holds keys this wave computes with
   auto act_at = [&](int i) {
     if constexpr (SPARSE) {
-      const int j0 = tile_of(i) * BN;
-      return j0 < N && (!CAUSAL || j0 <= qw0 + 31);
+      return tile_of(i) * BN <= j0_max;
     } else {
       return act(t0 + i);
     }
