@@ -28,7 +28,11 @@
 // own 256 queries of one (batch, head) in two groups that run half a tile apart
 // (one issues MFMAs while the other runs the softmax), 64-key tiles, one
 // barrier per tile, direct buffer loads into LDS with one array per stage
-// (StageTag).  Rows are 128 bytes (d = 128 fp8).
+// (StageTag).  Rows are 128 bytes (d = 128 fp8).  Unlike the bf16 kernel, only
+// group 0 issues the tile loads, in slot Y where it runs the products: the fp8
+// products take about a third of the softmax's time, so that wave has room for
+// the load instructions, whose issue would otherwise lengthen the softmax wave
+// that bounds the slot.
 //  * S^T = K Q^T: A = K rows from LDS (lane = key, 32 bytes of head dims per
 //    lane half), B = Q^T in VGPRs (lane = query).  Two MFMAs per 32 keys.
 //  * O^T += V^T P^T: A = V^T through ds_read_b64_tr_b8 (in each 16-lane group
@@ -90,7 +94,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8(
   constexpr int NH = kBN / 32;                 // 32-key blocks of a tile
   constexpr int CPR = ROW_BYTES / 16;          // 16-byte chunks per row
   constexpr int RPI = 1024 / ROW_BYTES;        // rows per 1 KiB wave-wide load
-  constexpr int NI = TILE_BYTES / 1024 / 8;    // such loads per wave per tile
+  constexpr int NI = TILE_BYTES / 1024 / 4;    // such loads per group-0 wave per tile
   static_assert(NI >= 1 && NH == 2, "tile shape");
   __shared__ __attribute__((aligned(1024))) unsigned char kb0[TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) unsigned char kb1[TILE_BYTES];
@@ -159,12 +163,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8(
   asm volatile("" : "+v"(n_w));
   auto act = [&](int t) { return t < n_w; };
 
-  // ---- loader: global -> LDS directly
+  // ---- loader: global -> LDS directly, by the four group-0 waves (2 KiB each per tile)
   const int wave_s = __builtin_amdgcn_readfirstlane(wave);
   int kgoff[NI], vgoff[NI];
 #pragma unroll
   for (int j = 0; j < NI; ++j) {
-    const int row = (wave * NI + j) * RPI + lane / CPR;
+    const int row = ((wave & 3) * NI + j) * RPI + lane / CPR;
     const int p = lane % CPR;
     kgoff[j] = row * ROW_BYTES + (p ^ kswz8(row)) * 16;
     vgoff[j] = row * ROW_BYTES + (p ^ vswz8(row)) * 16;
@@ -172,12 +176,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8(
   auto load_k = [&](int t, auto st) __attribute__((always_inline)) {
     const auto r = make_rsrc(Kh + (size_t)t * kBN * kD, (int64_t)(N - t * kBN) * ROW_BYTES);
 #pragma unroll
-    for (int j = 0; j < NI; ++j) load16_to_lds(r, kbuf(st) + (wave_s * NI + j) * 1024, kgoff[j]);
+    for (int j = 0; j < NI; ++j) load16_to_lds(r, kbuf(st) + ((wave_s & 3) * NI + j) * 1024, kgoff[j]);
   };
   auto load_v = [&](int t, auto st) __attribute__((always_inline)) {
     const auto r = make_rsrc(Vh + (size_t)t * kBN * kD, (int64_t)(N - t * kBN) * ROW_BYTES);
 #pragma unroll
-    for (int j = 0; j < NI; ++j) load16_to_lds(r, vbuf(st) + (wave_s * NI + j) * 1024, vgoff[j]);
+    for (int j = 0; j < NI; ++j) load16_to_lds(r, vbuf(st) + ((wave_s & 3) * NI + j) * 1024, vgoff[j]);
   };
   auto loads_landed = [&]() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
 
@@ -327,9 +331,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8(
     }
     loads_landed();
     __syncthreads();
-    if (t + 2 < n_kt) load_k(t + 2, cur);
-    if (t + 1 < n_kt) load_v(t + 1, other);
     if (group == 0) {
+      if (t + 2 < n_kt) load_k(t + 2, cur);
+      if (t + 1 < n_kt) load_v(t + 1, other);
       __builtin_amdgcn_s_setprio(1);
       if (act(t) && act(t + 1)) {
         pv_qk(cur, other);
@@ -343,13 +347,15 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8(
     }
   };
 
-  load_k(0, StageTag<0>{});
+  if (group == 0) load_k(0, StageTag<0>{});
   loads_landed();
   __syncthreads();
 #pragma unroll
   for (int kb = 0; kb < NK; ++kb) asm volatile("" ::"v"(qf[kb]));
-  if (1 < n_kt) load_k(1, StageTag<1>{});
-  load_v(0, StageTag<0>{});
+  if (group == 0) {
+    if (1 < n_kt) load_k(1, StageTag<1>{});
+    load_v(0, StageTag<0>{});
+  }
   if (group == 0 && act(0)) {
     __builtin_amdgcn_s_setprio(1);
     qk(StageTag<0>{});
