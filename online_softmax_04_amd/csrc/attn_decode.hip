@@ -57,14 +57,6 @@ typedef float f32x4v __attribute__((ext_vector_type(4)));
 constexpr float kSlack = 8.f;   // how far (log2 units) the running maximum may pass m
 constexpr int kTileKeys = 32;   // keys per tile
 
-// s_waitcnt with only the vector-memory count set (gfx9 encoding: vmcnt in
-// bits 3:0 and 15:14, expcnt and lgkmcnt left at their maxima).
-template <int N>
-__device__ __forceinline__ void wait_vmem() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
-}
-
 // Phase 1.  Workgroup = one wave = (batch*head, chunk, 32-query group).
 // Writes, for each of its valid queries q: part_o[(bh, chunk, q), :] = O (not
 // normalised, against reference m) and part_ml[(bh, chunk, q)] = (m, l), m in

@@ -72,6 +72,16 @@ __device__ __forceinline__ void load16_to_lds(__amdgpu_buffer_rsrc_t r, unsigned
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, voff, 0, 0, 0);
 }
 
+// s_waitcnt with only the vector-memory count set (gfx9 encoding: vmcnt in
+// bits 3:0 and 15:14, expcnt and lgkmcnt left at their maxima).  Unlike the
+// same instruction in inline assembly, the compiler sees it and knows which
+// direct-to-LDS loads it retires.
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+
 // The same with the non-temporal cache policy (gfx940-family NT bit), for data
 // read exactly once: it streams past the caches instead of displacing reused lines.
 __device__ __forceinline__ void load16_to_lds_nt(__amdgpu_buffer_rsrc_t r, unsigned char* lds, int voff) {
