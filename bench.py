@@ -18,7 +18,8 @@ Prints ONE JSON line:
   After the timed steps, beside them: the backward (fa_bwd) on the same
   inputs, the forward with a sliding window over packed documents
   (fa_fwd_local, FLOP over visible pairs), the forward under a block-sparse
-  pattern (fa_fwd_blocksparse, FLOP over visible pairs), the split-row softmax over
+  pattern (fa_fwd_blocksparse, FLOP over visible pairs), one GPU's share of
+  the causal workload split 8 ways by heads (B8 H4), the split-row softmax over
   4 rows of 2^24 columns (GB/s at 8 bytes per element; it moves 12), and the
   split-KV decode of one query per head against 32768 cached keys (GB/s of
   K, V, Q, O and LSE moved once), and the fp8 forward on the B8 H32 N8192 d128
@@ -528,6 +529,25 @@ def main():
     bs_tflops = bs_flop / (bs_ms * 1e-3) / 1e12
     print(f"[bench] blocksparse {bs_ms:.3f} ms", file=sys.stderr, flush=True)
 
+    # One GPU's share of the same workload split over 8 GPUs by heads (4 of the 32
+    # heads of every batch row): the kernel at the shape it would run at there.
+    sh_h = w.H // 8
+    sq, sk, sv = (t[:, :sh_h].contiguous() for t in (qd, kd, vd))
+    so = torch.empty_like(sq)
+    sl = torch.empty((w.B, sh_h, w.N), dtype=torch.float32, device=dev)
+
+    def shard():
+        fa.fa_fwd(sq, sk, sv, so, sl, w.B, sh_h, w.N, w.d, w.sm_scale, int(w.causal), stream)
+
+    for _ in range(args.warmup):
+        shard()
+    sh_each = timed(shard, args.steps)
+    sh_ms = sum(sh_each) / args.steps
+    sh_flop = w.flops / 8
+    sh_tflops = sh_flop / (sh_ms * 1e-3) / 1e12
+    del sq, sk, sv, so, sl
+    print(f"[bench] 8-way head shard {sh_ms:.3f} ms", file=sys.stderr, flush=True)
+
     # Split-row softmax on few very long rows (several workgroups per row), and
     # the one-workgroup-per-row path on the same input for comparison.
     spw = workloads.SOFTMAX[SPLIT_WORKLOAD]
@@ -656,6 +676,14 @@ def main():
                                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                                      "frac": round(bs_tflops / PEAK_BF16_TFLOPS, 4),
                                      "kernel": "attn_fwd_mfma<bf16,128,causal,blocksparse>"}},
+        "shard_8way_heads": {"workload": f"attn_bf16_b{w.B}h{sh_h}n{w.N}_causal (heads 0-{sh_h - 1} of each batch row)",
+                             "value": round(sh_tflops, 2), "unit": "TFLOP/s",
+                             "flop_per_launch": sh_flop, "avg_launch_ms": round(sh_ms, 5),
+                             "median_launch_ms": round(sh_each[len(sh_each) // 2], 5),
+                             "roofline": {"bound": "mfma", "achieved": round(sh_tflops, 2),
+                                          "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                                          "frac": round(sh_tflops / PEAK_BF16_TFLOPS, 4),
+                                          "kernel": "attn_fwd_mfma<bf16,128,causal>"}},
         "softmax_split": {"workload": spw.name, "value": round(sp_gbps, 1), "unit": "GB/s",
                           "bytes_per_launch": spw.algorithmic_bytes,
                           "bytes_moved_per_launch": 12 * spw.rows * spw.cols,
