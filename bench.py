@@ -99,6 +99,19 @@ def _counter_rows(d):
     return rows
 
 
+def _attn_grid() -> int:
+    """Threads of the headline attention launch (the benchmark also launches the same
+    kernel at other shapes; its dispatches are told apart by grid size)."""
+    import workloads
+    w = workloads.ATTN[ATTN_WORKLOAD]
+    return w.B * w.H * (-(-w.N // 256)) * 512
+
+
+def _is_attn_dispatch(r) -> bool:
+    grid = r.get("Grid_Size") or r.get("Grid_Size_X")
+    return KERNEL_NAME_PART["attn"] in r.get("Kernel_Name", "") and grid is not None and int(grid) == _attn_grid()
+
+
 def _per_kernel(rows, counter):
     """Mean counter value per dispatch for each kernel family (attn, softmax, copy)."""
     per_dispatch = {}
@@ -107,6 +120,8 @@ def _per_kernel(rows, counter):
             continue
         name = r.get("Kernel_Name", "")
         for kind, part in KERNEL_NAME_PART.items():
+            if kind == "attn" and not _is_attn_dispatch(r):
+                continue
             if part in name:
                 key = (kind, r.get("Dispatch_Id"))
                 per_dispatch[key] = per_dispatch.get(key, 0.0) + float(r["Counter_Value"])
@@ -190,7 +205,7 @@ def ingest_mfma(dir_a: str, dir_b: str):
     vals, durs = {}, {}
     for d in (dir_a, dir_b):
         for r in _counter_rows(d):
-            if KERNEL_NAME_PART["attn"] not in r.get("Kernel_Name", ""):
+            if not _is_attn_dispatch(r):
                 continue
             key = (d, r["Dispatch_Id"])
             vals.setdefault(key, {})
@@ -265,11 +280,16 @@ def ingest_trace(d: str, warmup: int):
     traces = glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True)
     if not stats or not traces:
         raise SystemExit(f"no kernel_stats.csv / kernel_trace.csv under {d}")
-    rows = list(csv.DictReader(open(stats[0])))
+    share = {r["Name"]: float(r["Percentage"]) for r in csv.DictReader(open(stats[0]))}
+    total_ns = sum(float(r["TotalDurationNs"]) for r in csv.DictReader(open(stats[0])))
+    # calls grouped by kernel and grid size: the benchmark runs some kernels at two shapes
     per_call = {}
     for r in csv.DictReader(open(traces[0])):
-        per_call.setdefault(r["Kernel_Name"], []).append(
+        per_call.setdefault((r["Kernel_Name"], int(r["Grid_Size_X"])), []).append(
             (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    grids = {}
+    for name, grid in per_call:
+        grids.setdefault(name, []).append(grid)
     path = os.path.join(ROOT, "profiles", f"kernel_trace_{ATTN_WORKLOAD}+{SOFTMAX_WORKLOAD}.md")
     with open(path, "w") as fh:
         fh.write(f"# Kernel durations: {ATTN_WORKLOAD} + {SOFTMAX_WORKLOAD}\n\n")
@@ -281,17 +301,18 @@ def ingest_trace(d: str, warmup: int):
                  f"{source_hash('softmax')}.\n\n")
         fh.write(f"\"timed mean\" skips each kernel's first {warmup} calls (the benchmark's untimed "
                  "warm-up steps, while the clock ramps up).\n\n")
-        fh.write("| kernel | calls | timed mean (us) | mean of all calls (us) | min (us) | max (us) | share |\n"
-                 "|---|---|---|---|---|---|---|\n")
-        for r in rows:
-            name = r["Name"]
+        fh.write("Rows are per kernel and grid size (threads); the headline attention launch is "
+                 f"the one with {_attn_grid()} threads.\n\n")
+        fh.write("| kernel | grid | calls | timed mean (us) | mean of all calls (us) | min (us) | max (us) | share |\n"
+                 "|---|---|---|---|---|---|---|---|\n")
+        for (name, grid), calls in sorted(per_call.items(), key=lambda kv: -sum(kv[1])):
             short = name if len(name) < 90 else name[:87] + "..."
-            calls = per_call.get(name, [])
             timed = calls[warmup:] if len(calls) > warmup else []
             tm = f"{sum(timed) / len(timed):.2f}" if timed else "-"
-            fh.write(f"| `{short}` | {r['Calls']} | {tm} | {float(r['AverageNs']) / 1e3:.2f} | "
-                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
-                     f"{float(r['Percentage']):.2f}% |\n")
+            sh = (f"{share[name]:.2f}%" if len(grids[name]) == 1 and name in share
+                  else f"{sum(calls) * 1e3 / total_ns * 100:.2f}%")
+            fh.write(f"| `{short}` | {grid} | {len(calls)} | {tm} | {sum(calls) / len(calls):.2f} | "
+                     f"{min(calls):.2f} | {max(calls):.2f} | {sh} |\n")
     print(open(path).read())
 
 
