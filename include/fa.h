@@ -158,7 +158,7 @@ int fa_fwd_blocksparse_f16(const void* q, const void* k, const void* v, void* o,
  *  o          [B, H, N, d] bf16, 16-byte aligned, written.
  *  lse        [B, H, N] fp32 or NULL.
  *  q_descale, k_descale, v_descale  finite, > 0 (else FA_ERR_INVALID_ARG).
- *  d = 128 only (else FA_ERR_UNSUPPORTED).  Every other argument, layout and
+ *  d = 64 or 128 (else FA_ERR_UNSUPPORTED).  Every other argument, layout and
  *  error is that of fa_fwd.
  */
 int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,

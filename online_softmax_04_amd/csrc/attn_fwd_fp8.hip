@@ -69,21 +69,27 @@ __device__ __forceinline__ void mfma_settle() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-constexpr int kD = 128;         // head dim (bytes per row)
 constexpr int kBM = 256;        // queries per workgroup
 constexpr int kBN = 64;         // keys per tile
 constexpr int kThreads = 512;   // two groups of 4 waves
 constexpr float kPScale = 7.f;  // P is stored as 2^7 P
 constexpr float kSlack = 1.5f;  // how far (log2 units) the row maximum may pass m: 2^(7 + 1.5) < 448
 
-// 16-byte chunk swizzles of 128-byte rows (physical chunk = logical ^ swizzle):
+// 16-byte chunk swizzles of D-byte rows (physical chunk = logical ^ swizzle):
 // K is read as 16-byte pieces of 32 consecutive rows at one chunk position,
-// V^T as 8 rows x 32 bytes per 32 lanes; both spread over all 64 banks.
-__device__ __forceinline__ int kswz8(int row) { return (row >> 1) & 7; }
-__device__ __forceinline__ int vswz8(int row) { return 2 * ((row >> 1) & 3); }
+// V^T as 8 rows x 32 bytes per 32 lanes; both spread over all 64 banks.  With
+// 128-byte rows, rows 2 apart share a bank line; with 64-byte rows, rows 4 apart.
+// Rows 32 (K) and 16 (V) apart keep their swizzle, as the operand reads assume.
+template <int D>
+__device__ __forceinline__ int kswz8(int row) { return D == 128 ? (row >> 1) & 7 : (row >> 2) & 3; }
+template <int D>
+__device__ __forceinline__ int vswz8(int row) {
+  return D == 128 ? 2 * ((row >> 1) & 3) : 2 * ((row >> 2) & 1);
+}
 
-template <bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8(
+// The kernel body for head dim kD (64 or 128); the kernels below instantiate it.
+template <int kD, bool CAUSAL>
+__device__ __forceinline__ void fp8_forward(
     const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K, const uint8_t* __restrict__ V,
     uint16_t* __restrict__ O, float* __restrict__ LSE, int BH, int N, int n_mtiles, float c,
     float v_descale, int xcd_groups) {
@@ -170,8 +176,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8(
   for (int j = 0; j < NI; ++j) {
     const int row = ((wave & 3) * NI + j) * RPI + lane / CPR;
     const int p = lane % CPR;
-    kgoff[j] = row * ROW_BYTES + (p ^ kswz8(row)) * 16;
-    vgoff[j] = row * ROW_BYTES + (p ^ vswz8(row)) * 16;
+    kgoff[j] = row * ROW_BYTES + (p ^ kswz8<kD>(row)) * 16;
+    vgoff[j] = row * ROW_BYTES + (p ^ vswz8<kD>(row)) * 16;
   }
   auto load_k = [&](int t, auto st) __attribute__((always_inline)) {
     const auto r = make_rsrc(Kh + (size_t)t * kBN * kD, (int64_t)(N - t * kBN) * ROW_BYTES);
@@ -192,7 +198,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8(
   for (int kb = 0; kb < NK; ++kb)
 #pragma unroll
     for (int h = 0; h < 2; ++h)
-      kroff[kb][h] = l32 * ROW_BYTES + ((4 * kb + 2 * hf + h) ^ kswz8(l32)) * 16;
+      kroff[kb][h] = l32 * ROW_BYTES + ((4 * kb + 2 * hf + h) ^ kswz8<kD>(l32)) * 16;
   // V^T: read i of head-dim block db takes rows 16 i + 8 hf + (q >> 1), bytes
   // 32 db + 16 ((lane >> 4) & 1) + 8 (q & 1) (q = lane % 16); rows 16 i apart share
   // the swizzle, so one offset per db serves all four reads
@@ -202,7 +208,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8(
     const int row = 8 * hf + (q >> 1);
 #pragma unroll
     for (int db = 0; db < ND; ++db)
-      vroff[db] = row * ROW_BYTES + ((2 * db + ((lane >> 4) & 1)) ^ vswz8(row)) * 16 + 8 * (q & 1);
+      vroff[db] = row * ROW_BYTES + ((2 * db + ((lane >> 4) & 1)) ^ vswz8<kD>(row)) * 16 + 8 * (q & 1);
   }
 
   auto qk = [&](auto st) __attribute__((always_inline)) {
@@ -390,25 +396,44 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8(
     LSE[(size_t)bh * N + qi] = (m_run + log2f(l_tot) - kPScale) * kLn2;
 }
 
+#define FP8_KERNEL_ARGS                                                                         \
+  const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K, const uint8_t* __restrict__ V,  \
+      uint16_t* __restrict__ O, float* __restrict__ LSE, int BH, int N, int n_mtiles, float c, \
+      float v_descale, int xcd_groups
+template <bool CAUSAL>
+__global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_d128(FP8_KERNEL_ARGS) {
+  fp8_forward<128, CAUSAL>(Q, K, V, O, LSE, BH, N, n_mtiles, c, v_descale, xcd_groups);
+}
+template <bool CAUSAL>
+__global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_d64(FP8_KERNEL_ARGS) {
+  fp8_forward<64, CAUSAL>(Q, K, V, O, LSE, BH, N, n_mtiles, c, v_descale, xcd_groups);
+}
+#undef FP8_KERNEL_ARGS
+
 }  // namespace
+
+static const void* pick_fp8(int d, bool causal) {
+  if (d == 64) return causal ? (const void*)attn_fwd_fp8_d64<true> : (const void*)attn_fwd_fp8_d64<false>;
+  return causal ? (const void*)attn_fwd_fp8_d128<true> : (const void*)attn_fwd_fp8_d128<false>;
+}
 
 hipError_t launch_attn_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
                                int B, int H, int N, int d, float scale, float q_descale,
                                float k_descale, float v_descale, bool causal, hipStream_t stream) {
-  if (d != kD) return hipErrorInvalidValue;
+  if (d != 64 && d != 128) return hipErrorInvalidValue;
   int BH = B * H;
   int n_mtiles = (N + kBM - 1) / kBM;
   float c = scale * q_descale * k_descale * kLog2e;
   int xcd_groups = (BH % 8 == 0) ? 1 : 0;
-  const void* fn = causal ? (const void*)attn_fwd_fp8<true> : (const void*)attn_fwd_fp8<false>;
+  const void* fn = pick_fp8(d, causal);
   void* args[] = {(void*)&q, (void*)&k, (void*)&v, (void*)&o, (void*)&lse, (void*)&BH,
                   (void*)&N, (void*)&n_mtiles, (void*)&c, (void*)&v_descale, (void*)&xcd_groups};
   return hipLaunchKernel(fn, dim3(BH * n_mtiles), dim3(kThreads), args, 0, stream);
 }
 
-hipError_t attn_fwd_fp8_attributes(bool causal, hipFuncAttributes* attr, int* threads,
+hipError_t attn_fwd_fp8_attributes(int d, bool causal, hipFuncAttributes* attr, int* threads,
                                    int* blocks_per_cu) {
-  const void* fn = causal ? (const void*)attn_fwd_fp8<true> : (const void*)attn_fwd_fp8<false>;
+  const void* fn = pick_fp8(d, causal);
   *threads = kThreads;
   hipError_t e = hipFuncGetAttributes(attr, fn);
   if (e != hipSuccess) return e;

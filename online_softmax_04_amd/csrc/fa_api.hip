@@ -101,7 +101,7 @@ int fp8_entry(const void* q, const void* k, const void* v, void* o, float* lse, 
   const uint64_t out_bytes = tensor_bytes(B, H, N, d, 2);
   const uint64_t lse_bytes = tensor_bytes(B, H, N, 1, 4);
   if (in_bytes == 0 || out_bytes == 0 || lse_bytes == 0) return FA_ERR_INVALID_ARG;
-  if (d != 128) return FA_ERR_UNSUPPORTED;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
   if ((uint64_t)N * (uint64_t)d * 2 >= ((uint64_t)1 << 31)) return FA_ERR_UNSUPPORTED;
   const uint64_t blocks = (uint64_t)B * (uint64_t)H * (((uint64_t)N + 255) / 256);
   if (blocks > (uint64_t)INT_MAX) return FA_ERR_INVALID_ARG;
@@ -374,8 +374,8 @@ int fa_kernel_attributes(int op, int d, int causal, fa_kernel_attrs* out) {
     e = osm::attn_fwd_attributes(osm::Elem::bf16, d, causal != 0, &attr, &threads, &blocks,
                                  op == 8 ? osm::kMaskSparse : osm::kMaskLocal);
   } else if (op == 7) {
-    if (d != 128) return FA_ERR_UNSUPPORTED;
-    e = osm::attn_fwd_fp8_attributes(causal != 0, &attr, &threads, &blocks);
+    if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+    e = osm::attn_fwd_fp8_attributes(d, causal != 0, &attr, &threads, &blocks);
   } else if (op == 6) {
     if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
     e = osm::attn_decode_attributes(d, causal != 0, &attr, &threads, &blocks);

@@ -33,11 +33,11 @@ hipError_t launch_attn_fwd_blocksparse(Elem elem, const void* q, const void* k, 
                                        const int* blk_idx, int nnz, int B, int H, int N, int d,
                                        float scale, bool causal, hipStream_t stream);
 
-// Attention forward with fp8 E4M3 Q/K/V (value = descale * code), bf16 O; d = 128.
+// Attention forward with fp8 E4M3 Q/K/V (value = descale * code), bf16 O; d = 64 or 128.
 hipError_t launch_attn_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
                                int B, int H, int N, int d, float scale, float q_descale,
                                float k_descale, float v_descale, bool causal, hipStream_t stream);
-hipError_t attn_fwd_fp8_attributes(bool causal, hipFuncAttributes* attr, int* threads,
+hipError_t attn_fwd_fp8_attributes(int d, bool causal, hipFuncAttributes* attr, int* threads,
                                    int* blocks_per_cu);
 
 // Attention backward (bf16 / fp16): dQ and D into `workspace` ([B, H, N] fp32),

@@ -315,7 +315,7 @@ def call_fp8(q=A, k=A + 64 * MB, v=A + 128 * MB, o=A + 192 * MB, lse=A + 256 * M
     (dict(N=0), fa.FA_ERR_INVALID_ARG), (dict(scale=-1.0), fa.FA_ERR_INVALID_ARG),
     (dict(qs=0.0), fa.FA_ERR_INVALID_ARG), (dict(ks=float("inf")), fa.FA_ERR_INVALID_ARG),
     (dict(vs=float("nan")), fa.FA_ERR_INVALID_ARG), (dict(causal=3), fa.FA_ERR_INVALID_ARG),
-    (dict(d=64), fa.FA_ERR_UNSUPPORTED), (dict(N=1 << 23), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED), (dict(N=1 << 23), fa.FA_ERR_UNSUPPORTED),
     (dict(q=A + 8), fa.FA_ERR_ALIGNMENT), (dict(o=A + 192 * MB + 4), fa.FA_ERR_ALIGNMENT),
     (dict(lse=A + 256 * MB + 1), fa.FA_ERR_ALIGNMENT),
     (dict(o=A + 128 * MB + 16), fa.FA_ERR_INVALID_ARG),    # o over v

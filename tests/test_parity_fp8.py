@@ -110,15 +110,16 @@ def random_fp8(B, H, N, d, seed, desc=(1 / 64, 1 / 64, 1 / 64), std=1.0):
     return tuple(workloads.cast(t / s, "fp8") for t, s in zip((q, k, v), desc))
 
 
+@pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("N", [1, 2, 63, 64, 65, 129, 200, 300, 1000])
-def test_fp8_edge_shapes(orc, causal, N):
-    B, H, d = 1, 3, 128
+def test_fp8_edge_shapes(orc, causal, N, d):
+    B, H = 1, 3
     desc = (1 / 64, 1 / 64, 1 / 64)
-    say(f"[attention fp8 edge] causal={causal} N={N}")
-    q8, k8, v8 = random_fp8(B, H, N, d, seed=N + 7, desc=desc)
+    say(f"[attention fp8 edge] d={d} causal={causal} N={N}")
+    q8, k8, v8 = random_fp8(B, H, N, d, seed=N + 7 + d, desc=desc)
     o, lse = run(q8, k8, v8, 1 / np.sqrt(d), desc, causal)
-    check(orc, f"fp8 c{int(causal)} N{N}", q8, k8, v8, 1 / np.sqrt(d), desc, causal, o, lse)
+    check(orc, f"fp8 d{d} c{int(causal)} N{N}", q8, k8, v8, 1 / np.sqrt(d), desc, causal, o, lse)
 
 
 def test_fp8_workload(orc):
@@ -189,22 +190,33 @@ def emulate(orc, q8, k8, v8, desc, scale, causal, tile=64):
     return O, L
 
 
+@pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
-def test_fp8_matches_its_arithmetic(orc, causal):
+def test_fp8_matches_its_arithmetic(orc, causal, d):
     """Against the emulation of the kernel's own rounding every output element
-    is expected within the bf16 rounding of O (2^-8 |O|) plus the rare weight whose
-    E4M3 rounding flips between fp32 and fp64 exponents; every wave group of the
-    workgroup is covered (N = 300 spans 256 + 44 queries).  This bound is far
-    tighter than the gate against the exact result."""
-    B, H, N, d = 1, 3, 300, 128
+    is expected within the bf16 rounding of O (2^-8 |O|) plus a small absolute
+    term; every wave group of the workgroup is covered (N = 300 spans 256 + 44
+    queries).  This bound is far tighter than the gate against the exact result.
+    The exception is a weight whose E4M3 rounding flips between the kernel's fp32
+    and the emulation's fp64 arguments: that moves its row by one E4M3 step
+    (2^-3 relative) of the weight's share, which exceeds the bound when the weight
+    dominates the row.  A flip needs the argument within about 2^-20 of a rounding
+    midpoint, so at most one row per head is allowed outside the bound, and that
+    row is held to the one-flip bounds below (the gate against the exact result
+    holds for every row in the other tests)."""
+    B, H, N = 1, 3, 300
     desc = (1 / 64, 1 / 64, 1 / 64)
     q8, k8, v8 = random_fp8(B, H, N, d, seed=N + 7, desc=desc)
     o, lse = run(q8, k8, v8, 1 / np.sqrt(d), desc, causal)
     for h in range(H):
         eo, el = emulate(orc, q8[0, h], k8[0, h], v8[0, h], desc, 1 / np.sqrt(d), causal)
         go, gl = to_f64(o[0, h]), to_f64(lse[0, h])
-        err = np.abs(go - eo)
-        say(f"  fp8 emulation c{int(causal)} head {h}: max |O - emul| {err.max():.2e}, "
-            f"max |LSE - emul| {np.abs(gl - el).max():.2e}")
-        assert np.all(err <= 2.0 ** -7 * np.abs(eo) + 0.01), f"head {h}: O off the kernel's arithmetic"
-        assert np.max(np.abs(gl - el)) <= 5e-3
+        err, lerr = np.abs(go - eo), np.abs(gl - el)
+        off = np.unique(np.concatenate([np.nonzero(err > 2.0 ** -7 * np.abs(eo) + 0.01)[0],
+                                        np.nonzero(lerr > 5e-3)[0]]))
+        say(f"  fp8 emulation d{d} c{int(causal)} head {h}: max |O - emul| {err.max():.2e}, "
+            f"max |LSE - emul| {lerr.max():.2e}, rows outside the tight bound {off.tolist()}")
+        assert off.size <= 1, f"head {h}: rows {off.tolist()} off the kernel's arithmetic"
+        vmax = float(np.abs(orc.to_f64(v8[0, h], "fp8")).max() * desc[2])
+        for r in off:  # one flipped weight: |dO| <= 2^-3 * 2 max|v|, |dLSE| <= ln(1 + 2^-3)
+            assert err[r].max() <= 2.0 ** -3 * 2 * vmax and lerr[r] <= np.log1p(2.0 ** -3)
