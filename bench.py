@@ -722,7 +722,7 @@ def main():
                 "roofline": {"bound": "mfma", "achieved": round(f8_tflops, 2),
                              "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
                              "frac": round(f8_tflops / PEAK_FP8_TFLOPS, 4),
-                             "kernel": "attn_fwd_fp8<128,causal>"}},
+                             "kernel": "attn_fwd_fp8_d128<causal>"}},
         "decode": {"workload": dw.name, "value": round(dec_gbps, 1), "unit": "GB/s",
                    "bytes_per_launch": dw.algorithmic_bytes, "workspace_bytes": dec_wsb,
                    "avg_launch_us": round(dec_ms * 1e3, 2),
