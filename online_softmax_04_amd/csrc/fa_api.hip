@@ -64,9 +64,9 @@ int attn_entry(osm::Elem elem, const void* q, const void* k, const void* v, void
     if (nnz > 0 && (overlaps(blk_idx, idx_bytes, o, bytes) ||
                     (lse && overlaps(blk_idx, idx_bytes, lse, lse_bytes))))
       return FA_ERR_INVALID_ARG;
-    hipError_t e = osm::launch_attn_fwd_blocksparse(elem, q, k, v, o, lse, blk_ptr,
-                                                    nnz > 0 ? blk_idx : blk_ptr, nnz, B, H, N, d,
-                                                    scale, causal != 0, stream);
+    // with nnz = 0 every row range clamps to empty and blk_idx is never read
+    hipError_t e = osm::launch_attn_fwd_blocksparse(elem, q, k, v, o, lse, blk_ptr, blk_idx, nnz,
+                                                    B, H, N, d, scale, causal != 0, stream);
     return e == hipSuccess ? FA_OK : FA_ERR_HIP;
   }
   if (mask == osm::kMaskLocal) {
