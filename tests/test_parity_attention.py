@@ -209,3 +209,25 @@ def test_wrapper_allocates_and_rejects_bad_tensors():
     with pytest.raises(fa.FaError):
         q96 = torch.zeros((1, 1, 64, 96), dtype=torch.bfloat16, device="cuda")
         fa.attention(q96, q96.clone(), q96.clone())
+
+
+def test_head_shard_shape(orc):
+    """One GPU's share of the B8 H32 N8192 d128 causal workload split 8 ways by
+    heads (heads 0-3 of every batch row, B8 H4), the shape the benchmark's shard
+    line times: 1024 workgroups, XCD-grouped; heads (0, 0), (3, 3) and (7, 1)
+    checked on 256 sampled rows each."""
+    w = workloads.ATTN["attn_bf16_b8h32n8192_causal"]
+    hs = w.H // 8
+    say(f"[attention shard] B={w.B} H={hs} N={w.N} d={w.d}")
+    heads = [[workloads.attn_head(w, b, h) for h in range(hs)] for b in range(w.B)]
+    q, k, v = (np.stack([np.stack([heads[b][h][i] for h in range(hs)]) for b in range(w.B)])
+               for i in range(3))
+    o, lse = run_gpu(q, k, v, w.dtype, w.sm_scale, w.causal)
+    assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
+    for b, h in [(0, 0), (3, 3), (7, 1)]:
+        rows = workloads.attn_sample_rows(w, b, h)
+        ro, rl = orc.attention_head(q[b, h], k[b, h], v[b, h], w.sm_scale, True, rows, dtype=w.dtype)
+        rt = torch.from_numpy(rows).cuda()
+        gate(f"shard head ({b},{h}) O", to_f64(o[b, h].index_select(0, rt)), ro, w.dtype, rows)
+        gate(f"shard head ({b},{h}) LSE", to_f64(lse[b, h].index_select(0, rt))[:, None], rl[:, None],
+             w.dtype, rows, scaled=True)
