@@ -113,7 +113,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(
   constexpr int NH = BN / 32;                  // 32-key blocks of a tile
   constexpr int CPR = D / 8;                   // 16-byte chunks per row
   constexpr int RPI = 1024 / ROW_BYTES;        // rows per 1 KiB wave-wide load
-  constexpr int NI = TILE_BYTES / 1024 / 8;    // such loads per wave per tile
+  // At d = 64 the softmax of a 128-key tile takes longer than the tile's products,
+  // so the wave running the products has room to issue the tile loads too: only
+  // group 0 loads, in slot Y where it runs the products (as in the fp8 kernel).
+  // At d = 128 the two roles are balanced and every wave loads its share.
+  constexpr bool LG = D == 64;
+  constexpr int NI = TILE_BYTES / 1024 / (LG ? 4 : 8);  // such loads per loading wave per tile
   static_assert(NI >= 1, "tile shape");
   // One array per stage and operand, always named at compile time: the compiler
   // tracks the pending direct loads per array, so a read of one stage does not
@@ -261,7 +266,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(
   int kgoff[NI], vgoff[NI];
 #pragma unroll
   for (int j = 0; j < NI; ++j) {
-    const int row = (wave * NI + j) * RPI + lane / CPR;
+    const int row = ((LG ? wave & 3 : wave) * NI + j) * RPI + lane / CPR;
     const int p = lane % CPR;
     kgoff[j] = row * ROW_BYTES + (p ^ kswz<D>(row)) * 16;
     vgoff[j] = row * ROW_BYTES + (p ^ vswz<D>(row)) * 16;
@@ -270,13 +275,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(
     const auto r = make_rsrc(Kh + (size_t)t * BN * D, (int64_t)(N - t * BN) * ROW_BYTES);
 #pragma unroll
     for (int j = 0; j < NI; ++j)
-      load16_to_lds(r, kbuf(st) + (wave_s * NI + j) * 1024, kgoff[j]);
+      load16_to_lds(r, kbuf(st) + ((LG ? wave_s & 3 : wave_s) * NI + j) * 1024, kgoff[j]);
   };
   auto load_v = [&](int t, auto st) __attribute__((always_inline)) {
     const auto r = make_rsrc(Vh + (size_t)t * BN * D, (int64_t)(N - t * BN) * ROW_BYTES);
 #pragma unroll
     for (int j = 0; j < NI; ++j)
-      load16_to_lds(r, vbuf(st) + (wave_s * NI + j) * 1024, vgoff[j]);
+      load16_to_lds(r, vbuf(st) + ((LG ? wave_s & 3 : wave_s) * NI + j) * 1024, vgoff[j]);
   };
   // direct loads write LDS behind the compiler's back: wait for them explicitly
   auto loads_landed = [&]() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
@@ -430,8 +435,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(
     loads_landed();  // K of position i + 1, V of position i
     __syncthreads();
     // ---- slot Y
-    if (i + 2 < n_list) load_k(tile_of(i + 2), cur);
-    if (i + 1 < n_list) load_v(tile_of(i + 1), other);
+    if (!LG || group == 0) {
+      if (i + 2 < n_list) load_k(tile_of(i + 2), cur);
+      if (i + 1 < n_list) load_v(tile_of(i + 1), other);
+    }
     if (group == 0) {
       __builtin_amdgcn_s_setprio(1);
       const bool a_next = i + 1 < n_list && act_at(i + 1);
@@ -460,7 +467,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(
   // groups in opposite phases.  The dense kernel starts at tile t0 = 0; the
   // LOCAL one at the workgroup's first visible tile, each wave computing from
   // its own first tile tw0.
-  if (n_list > 0) load_k(tile_of(0), StageTag<0>{});
+  const bool loader = !LG || group == 0;
+  if (loader && n_list > 0) load_k(tile_of(0), StageTag<0>{});
   loads_landed();
   __syncthreads();
   // Retire the Q loads here.  Left pending, they would make the first MFMA that
@@ -469,8 +477,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(
 #pragma unroll
   for (int kb = 0; kb < NK; ++kb) asm volatile("" ::"v"(qf[kb]));
   // slot Y(t0 - 1): load K(t0+1), V(t0); group 0 computes S(t0)
-  if (1 < n_list) load_k(tile_of(1), StageTag<1>{});
-  if (n_list > 0) load_v(tile_of(0), StageTag<0>{});
+  if (loader && 1 < n_list) load_k(tile_of(1), StageTag<1>{});
+  if (loader && n_list > 0) load_v(tile_of(0), StageTag<0>{});
   if (group == 0 && n_list > 0 && act_at(0)) {
     __builtin_amdgcn_s_setprio(1);
     qk(StageTag<0>{});
