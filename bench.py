@@ -55,7 +55,7 @@ PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBPS = 8000.0         # MI355X HBM3E, published
 PEAK_FP8_TFLOPS = 5000.0       # MI355X dense fp8 MFMA, published
 COPY_BYTES = 256 << 20         # probe copy kernel: 256 MiB read + 256 MiB written
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.md")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", f"traffic_{ATTN_WORKLOAD}+{SOFTMAX_WORKLOAD}.md")
 KERNEL_SOURCES = {
     "attn": ["online_softmax_04_amd/csrc/attn_fwd.hip", "online_softmax_04_amd/csrc/common.h"],
     "softmax": ["online_softmax_04_amd/csrc/softmax.hip", "online_softmax_04_amd/csrc/common.h"],
