@@ -1,0 +1,106 @@
+"""Seeded random shapes for the forward entry points (dense, window + documents,
+block-sparse), each against the fp64 oracle on every row: B, H, N, d, the
+element type, causality, the window, the document lengths and the pattern are
+drawn from one seeded generator, so a failure names a reproducible case."""
+import numpy as np
+import pytest
+import torch
+
+import online_softmax_04_amd as fa
+import oracle
+import workloads
+from gpu_util import gate, say, to_device, to_f64
+
+pytestmark = pytest.mark.gpu
+
+CASES = 24
+
+
+@pytest.fixture(scope="module")
+def orc():
+    return oracle.load()
+
+
+def draw(case):
+    rng = np.random.default_rng([4242, case])
+    return dict(B=int(rng.integers(1, 3)), H=int(rng.integers(1, 4)), N=int(rng.integers(1, 2500)),
+                d=int(rng.choice([64, 128])), dtype=str(rng.choice(["bf16", "f16"])),
+                causal=bool(rng.integers(0, 2)), window=int(rng.choice([0, 1, 17, 300, 1024])),
+                seed=int(rng.integers(0, 1 << 30)), p=float(rng.uniform(0.0, 0.6)))
+
+
+def compare(orc, name, outs, refs, dtype):
+    go, gl = np.concatenate([o for o, _ in outs]), np.concatenate([l for _, l in outs])
+    ro, rl = np.concatenate([o for o, _ in refs]), np.concatenate([l for _, l in refs])
+    empty = np.isneginf(rl)
+    assert np.all(np.isneginf(gl[empty])) and np.all(go[empty] == 0.0), f"{name}: empty rows"
+    if (~empty).any():
+        gate(f"{name} O", go[~empty], ro[~empty], dtype)
+        gate(f"{name} LSE", gl[~empty][:, None], rl[~empty][:, None], dtype, scaled=True)
+
+
+@pytest.mark.parametrize("case", range(CASES))
+def test_random_dense(orc, case):
+    c = draw(case)
+    B, H, N, d, dt = c["B"], c["H"], c["N"], c["d"], c["dtype"]
+    say(f"[random dense {case}] {c}")
+    q, k, v = workloads.random_attn(B, H, N, d, dt, seed=c["seed"])
+    qd, kd, vd = (to_device(t, dt) for t in (q, k, v))
+    o, lse = torch.empty_like(qd), torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    (fa.fa_fwd if dt == "bf16" else fa.fa_fwd_f16)(qd, kd, vd, o, lse, B, H, N, d, d ** -0.5, int(c["causal"]))
+    torch.cuda.synchronize()
+    outs, refs = [], []
+    for b in range(B):
+        for h in range(H):
+            refs.append(orc.attention_head(q[b, h], k[b, h], v[b, h], d ** -0.5, c["causal"], dtype=dt))
+            outs.append((to_f64(o[b, h]), to_f64(lse[b, h])))
+    compare(orc, f"random dense {case}", outs, refs, dt)
+
+
+@pytest.mark.parametrize("case", range(CASES))
+def test_random_local(orc, case):
+    c = draw(case + 100)
+    B, H, N, d, dt = c["B"], c["H"], c["N"], c["d"], c["dtype"]
+    say(f"[random local {case}] {c}")
+    q, k, v = workloads.random_attn(B, H, N, d, dt, seed=c["seed"])
+    doc = workloads.packed_doc_starts(B, N, c["seed"] % 1000, 1, max(2, N // 2))
+    qd, kd, vd = (to_device(t, dt) for t in (q, k, v))
+    o, lse = torch.empty_like(qd), torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    entry = fa.fa_fwd_local if dt == "bf16" else fa.fa_fwd_local_f16
+    entry(qd, kd, vd, o, lse, torch.from_numpy(doc).cuda(), c["window"], B, H, N, d, d ** -0.5)
+    torch.cuda.synchronize()
+    outs, refs = [], []
+    for b in range(B):
+        lo, hi = workloads.local_ranges(doc[b], c["window"])
+        for h in range(H):
+            refs.append(orc.attention_ranged(q[b, h], k[b, h], v[b, h], d ** -0.5, lo, hi, np.arange(N), dtype=dt))
+            outs.append((to_f64(o[b, h]), to_f64(lse[b, h])))
+    compare(orc, f"random local {case}", outs, refs, dt)
+
+
+@pytest.mark.parametrize("case", range(CASES))
+def test_random_blocksparse(orc, case):
+    c = draw(case + 200)
+    B, H, N, d, dt = c["B"], c["H"], c["N"], c["d"], c["dtype"]
+    say(f"[random block-sparse {case}] {c}")
+    q, k, v = workloads.random_attn(B, H, N, d, dt, seed=c["seed"])
+    rng = np.random.default_rng(c["seed"])
+    nqb, nkb = (N + 255) // 256, (N + 127) // 128
+    lists = [sorted(int(x) for x in np.nonzero(rng.random(nkb) < c["p"])[0]) for _ in range(nqb)]
+    ptr = np.zeros(nqb + 1, np.int32)
+    ptr[1:] = np.cumsum([len(x) for x in lists])
+    idx = np.asarray([x for l in lists for x in l], np.int32)
+    qd, kd, vd = (to_device(t, dt) for t in (q, k, v))
+    o, lse = torch.empty_like(qd), torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    entry = fa.fa_fwd_blocksparse if dt == "bf16" else fa.fa_fwd_blocksparse_f16
+    entry(qd, kd, vd, o, lse, torch.from_numpy(ptr).cuda(),
+          torch.from_numpy(idx).cuda() if idx.size else None, idx.size, B, H, N, d, d ** -0.5,
+          int(c["causal"]))
+    torch.cuda.synchronize()
+    outs, refs = [], []
+    for b in range(B):
+        for h in range(H):
+            refs.append(orc.attention_blocksparse(q[b, h], k[b, h], v[b, h], d ** -0.5, c["causal"],
+                                                  ptr, idx, 256, 128, dtype=dt))
+            outs.append((to_f64(o[b, h]), to_f64(lse[b, h])))
+    compare(orc, f"random block-sparse {case}", outs, refs, dt)
