@@ -104,3 +104,32 @@ def test_random_blocksparse(orc, case):
                                                   ptr, idx, 256, 128, dtype=dt))
             outs.append((to_f64(o[b, h]), to_f64(lse[b, h])))
     compare(orc, f"random block-sparse {case}", outs, refs, dt)
+
+
+@pytest.mark.parametrize("case", range(CASES))
+def test_random_decode(orc, case):
+    """Split-KV attention of Nq queries at the end of Nk keys, Nq <= Nk when causal."""
+    import test_parity_decode as dec
+    c = draw(case + 300)
+    rng = np.random.default_rng([4343, case])
+    Nk = int(rng.integers(1, 20000))
+    Nq = int(rng.integers(1, min(Nk, 64) + 1)) if c["causal"] else int(rng.integers(1, 64))
+    B, H, d, dt = c["B"], c["H"], c["d"], c["dtype"]
+    say(f"[random decode {case}] B={B} H={H} Nq={Nq} Nk={Nk} d={d} {dt} causal={c['causal']}")
+    q = workloads.random_attn(B, H, Nq, d, dt, seed=c["seed"])[0]
+    _, k, v = workloads.random_attn(B, H, Nk, d, dt, seed=c["seed"] + 1)
+    o, lse = dec.run(q, k, v, dt, d ** -0.5, c["causal"])
+    dec.check(orc, f"random decode {case}", q, k, v, dt, d ** -0.5, c["causal"], o, lse)
+
+
+@pytest.mark.parametrize("case", range(CASES))
+def test_random_fp8(orc, case):
+    """fp8 forward with the derived E4M3 bounds of the fp8 parity tests."""
+    import test_parity_fp8 as f8
+    c = draw(case + 400)
+    B, H, N, d = c["B"], c["H"], min(c["N"], 1200), c["d"]
+    say(f"[random fp8 {case}] B={B} H={H} N={N} d={d} causal={c['causal']}")
+    desc = (1 / 64, 1 / 64, 1 / 64)
+    q8, k8, v8 = f8.random_fp8(B, H, N, d, seed=c["seed"] % 100000, desc=desc)
+    o, lse = f8.run(q8, k8, v8, d ** -0.5, desc, c["causal"])
+    f8.check(orc, f"random fp8 {case}", q8, k8, v8, d ** -0.5, desc, c["causal"], o, lse)
