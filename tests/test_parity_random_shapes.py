@@ -133,3 +133,17 @@ def test_random_fp8(orc, case):
     q8, k8, v8 = f8.random_fp8(B, H, N, d, seed=c["seed"] % 100000, desc=desc)
     o, lse = f8.run(q8, k8, v8, d ** -0.5, desc, c["causal"])
     f8.check(orc, f"random fp8 {case}", q8, k8, v8, d ** -0.5, desc, c["causal"], o, lse)
+
+
+@pytest.mark.parametrize("case", range(CASES))
+def test_random_backward(orc, case):
+    """dQ, dK, dV from the oracle's O and logsumexp, with the backward tests' gates."""
+    import test_parity_backward as bw
+    c = draw(case + 500)
+    B, H, N, d, dt = c["B"], c["H"], min(c["N"], 900), c["d"], c["dtype"]
+    say(f"[random backward {case}] B={B} H={H} N={N} d={d} {dt} causal={c['causal']}")
+    q, k, v = workloads.random_attn(B, H, N, d, dt, seed=c["seed"])
+    g = workloads.cast(bw.upstream((B, H, N, d), c["seed"] % 1000), dt)
+    o, lse = bw.oracle_forward(orc, q, k, v, dt, d ** -0.5, c["causal"])
+    grads = bw.run_bwd(q, k, v, o, g, lse, dt, d ** -0.5, c["causal"])
+    bw.check(orc, f"random backward {case}", q, k, v, g, dt, d ** -0.5, c["causal"], grads, o=o)
