@@ -1,4 +1,4 @@
-"""Seeded random shapes for the forward entry points (dense, window + documents,
+"""Seeded random shapes for the entry points (dense, window + documents,
 block-sparse), each against the fp64 oracle on every row: B, H, N, d, the
 element type, causality, the window, the document lengths and the pattern are
 drawn from one seeded generator, so a failure names a reproducible case."""
@@ -147,3 +147,23 @@ def test_random_backward(orc, case):
     o, lse = bw.oracle_forward(orc, q, k, v, dt, d ** -0.5, c["causal"])
     grads = bw.run_bwd(q, k, v, o, g, lse, dt, d ** -0.5, c["causal"])
     bw.check(orc, f"random backward {case}", q, k, v, g, dt, d ** -0.5, c["causal"], grads, o=o)
+
+
+@pytest.mark.parametrize("case", range(CASES))
+def test_random_softmax(orc, case):
+    """Row softmax, one workgroup per row and split over workgroups, on random
+    row counts, lengths, offsets (aligned or not) and spike densities."""
+    import test_parity_softmax as sm
+    import test_parity_softmax_split as sp
+    rng = np.random.default_rng([4444, case])
+    rows = int(rng.integers(1, 40))
+    cols = int(rng.choice([int(rng.integers(1, 5000)), int(rng.integers(30000, 70000)),
+                           int(rng.integers(100000, 400000))]))
+    offset = int(rng.choice([0, 0, 1, 3]))
+    x = workloads.random_rows(rows, cols, seed=int(rng.integers(0, 1 << 30)),
+                              std=float(rng.uniform(0.5, 4.0)), spike_prob=float(rng.choice([0.0, 1e-3, 0.02])))
+    say(f"[random softmax {case}] rows={rows} cols={cols} offset={offset}")
+    ref = orc.softmax_rows(x)
+    for name, got in (("rows", sm.run_gpu(x, offset)), ("split", sp.run_split(x, offset))):
+        g = got.cpu().numpy().astype(np.float64)
+        gate(f"random softmax {case} {name}", g, ref, "f32")
