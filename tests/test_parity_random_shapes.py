@@ -1,7 +1,9 @@
-"""Seeded random shapes for the entry points (dense, window + documents,
-block-sparse), each against the fp64 oracle on every row: B, H, N, d, the
-element type, causality, the window, the document lengths and the pattern are
-drawn from one seeded generator, so a failure names a reproducible case."""
+"""Seeded random shapes for the entry points (dense, window + documents and
+block-sparse forward, split-KV decode, fp8 forward, backward, row softmax and
+its split form), each against the fp64 oracle with the gates of the entry's own
+parity tests: the sizes, element type, causality, window, document lengths,
+pattern and value scales are drawn from seeded generators, so a failure names
+a reproducible case."""
 import numpy as np
 import pytest
 import torch
