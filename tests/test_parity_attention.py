@@ -109,6 +109,16 @@ def test_workload(orc, name):
         # output-rounding diagnostic: distance to the oracle rounded to bf16
         rb = workloads.bf16_bits_to_f32(workloads.f32_to_bf16_bits(ro.astype(np.float32)))
         say(f"  vs oracle rounded to bf16: max_abs={np.max(np.abs(go - rb)):.3e}")
+    if w.dtype == "f32":
+        # diagnostic: the pages' stricter fp32 check, rtol = max(1e-5, 4 * 2^-23 * sqrt(n))
+        # with n the keys a row reduces over, relative to max(|ref|, 1e-3)
+        n = w.N if not w.causal else np.arange(1, w.N + 1)
+        rtol = np.maximum(1e-5, 4 * 2.0 ** -23 * np.sqrt(n))
+        rows_all = np.tile(np.arange(w.N), w.B * w.H)
+        rel = np.abs(go - ro) / np.maximum(np.abs(ro), 1e-3)
+        lim = rtol if np.isscalar(rtol) else rtol[rows_all][:, None]
+        say(f"  pages' fp32 check: {np.mean(rel <= lim):.4%} of elements within rtol "
+            f"(max rel {rel.max():.2e}, rtol {np.min(lim):.2e})")
     if name == "attn_f32_n256_last":
         # the loud key N-3 dominates every row: O is (nearly) v[N-3]
         assert np.max(np.abs(go - v[0, 0, w.N - 3].astype(np.float64)[None, :])) < 1e-3
