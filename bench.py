@@ -59,6 +59,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", f"traffic_{ATTN_WORKLOAD}+{SOFTMAX
 KERNEL_SOURCES = {
     "attn": ["online_softmax_04_amd/csrc/attn_fwd.hip", "online_softmax_04_amd/csrc/common.h"],
     "softmax": ["online_softmax_04_amd/csrc/softmax.hip", "online_softmax_04_amd/csrc/common.h"],
+    "fp8": ["online_softmax_04_amd/csrc/attn_fwd_fp8.hip", "online_softmax_04_amd/csrc/common.h"],
 }
 # kernel-name fragments of the three dispatches the counters are read for; the
 # probe copy is torch's elementwise multiply by 1 (reads and writes 256 MiB)
@@ -194,6 +195,64 @@ def kernel_mfma_count(w) -> int:
             n_w = min(n_kt, (qw0 + 31) // bn + 1) if w.causal else n_kt
             total += n_w * per_tile
     return total * w.B * w.H
+
+
+def ingest_mfma_fp8(dir_a: str, dir_b: str):
+    """Matrix-pipe and instruction counters of the fp8 forward on its workload, from the
+    same two --pmc passes (the fp8 MFMA op count is not among them; busy cycles are)."""
+    import csv
+    import workloads
+    w = workloads.ATTN[FP8_WORKLOAD]
+    vals = {}
+    for d in (dir_a, dir_b):
+        for r in _counter_rows(d):
+            name = r.get("Kernel_Name", "")
+            if "attn_fwd_fp8_d128" not in name or int(r.get("Grid_Size") or 0) != _attn_grid():
+                continue
+            key = (d, r["Dispatch_Id"])
+            vals.setdefault(key, {})
+            vals[key][r["Counter_Name"]] = vals[key].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    if not vals:
+        print("no fp8 dispatches in the counter runs")
+        return
+    mean = {}
+    for cs in vals.values():
+        for name, v in cs.items():
+            mean.setdefault(name, []).append(v)
+    mean = {k: sum(v) / len(v) for k, v in mean.items()}
+    cu, simd, xcc = 256, 4, 8
+    for f in glob.glob(os.path.join(dir_a, "**", "*agent_info.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            if r.get("Agent_Type") == "GPU":
+                cu, simd = int(r["Cu_Count"]), int(r["Simd_Per_Cu"])
+                xcc = int(r.get("Num_Xcc") or xcc)
+    busy = mean.get("SQ_VALU_MFMA_BUSY_CYCLES", float("nan"))
+    active = mean.get("GRBM_GUI_ACTIVE", float("nan")) / xcc
+    n_mfma = mean.get("SQ_INSTS_MFMA", float("nan"))
+    lines = [
+        f"# MFMA utilisation: attn_fwd_fp8_d128<causal> on {w.name}\n",
+        "Commands (run from the repository root on one MI355X): the two --pmc passes of "
+        f"`profiles/mfma_{ATTN_WORKLOAD}.md`, then\n",
+        "    python3 bench.py --ingest-mfma gpurun_out/pmc_mfma_a gpurun_out/pmc_mfma_b\n",
+        f"Kernel source sha {source_hash('fp8')}; means over {len(vals)} profiled dispatch records "
+        f"of the {_attn_grid()}-thread launch.\n",
+        "| quantity | value |", "|---|---|",
+        f"| SQ_VALU_MFMA_BUSY_CYCLES (summed over SIMDs) | {busy:.4g} |",
+        f"| fp8 MFMA instructions (SQ_INSTS_MFMA) | {n_mfma:.4g} |",
+        f"| busy cycles per 32x32x64 fp8 MFMA | {busy / n_mfma:.2f} |",
+        f"| GRBM_GUI_ACTIVE per XCD | {active:.4g} |",
+        f"| **MFMA pipe utilisation = busy / (active x {cu} CUs x {simd} SIMDs)** | **{busy / (active * cu * simd):.1%}** |",
+        "",
+        "| counter | value | per MFMA |", "|---|---|---|",
+    ]
+    for name in MFMA_PASS_B.split():
+        v = mean.get(name, float("nan"))
+        lines.append(f"| {name} | {v:.4g} | {v / n_mfma:.3f} |")
+    lines.append("")
+    path = os.path.join(ROOT, "profiles", f"mfma_{FP8_WORKLOAD}.md")
+    with open(path, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print(open(path).read())
 
 
 def ingest_mfma(dir_a: str, dir_b: str):
@@ -399,6 +458,7 @@ def main():
         return
     if args.ingest_mfma:
         ingest_mfma(*args.ingest_mfma)
+        ingest_mfma_fp8(*args.ingest_mfma)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path is "
