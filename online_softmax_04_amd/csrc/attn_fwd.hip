@@ -86,6 +86,10 @@ __device__ __forceinline__ float add_pair<_Float16>(unsigned x, float acc) {
 }
 
 
+// two 16-bit ones in one word
+template <typename T>
+constexpr unsigned kOnePair = sizeof(T) == 2 && __is_same(T, __bf16) ? 0x3f803f80u : 0x3c003c00u;
+
 constexpr float kSlack = 8.f;  // how far (log2 units) the running maximum may pass m
 constexpr int kBM = 256;       // queries per workgroup
 // keys per tile: 128 at d = 64, where the per-tile fixed costs weigh most and the
@@ -181,6 +185,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(
 #pragma unroll
   for (int db = 0; db < ND; ++db) o[db] = f32x16{};
   f32x16 s[NH];
+  // At d = 64 the softmax wave is the longer one, so the row sum of P runs on the
+  // matrix unit: with a block of ones as the A operand, every row of the
+  // accumulator receives the sum over the step's keys of each query's P.
+  constexpr bool RS = D == 64;
+  f32x16 lacc = f32x16{};
+  const v8 ones = __builtin_bit_cast(
+      v8, u32x4{kOnePair<T>, kOnePair<T>, kOnePair<T>, kOnePair<T>});
   v8 pf[NH][2];  // P^T as 16-bit B operands: [32-key block][16-key step]
   float m_run = kNegInf, l_run = 0.f;
 
@@ -358,20 +369,23 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(
     // l sums the 16-bit P that the PV product consumes, so O / l weights V
     // by exactly the rounded P normalised to 1: a rounding error d of one weight
     // then moves O by d p (v - O) / l, not by d p v / l.
-    float ls[4] = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (!RS) {
+      float ls[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kh = 0; kh < NH; ++kh)
+      for (int kh = 0; kh < NH; ++kh)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const u32x4 w = __builtin_bit_cast(u32x4, pf[kh][kb]);
+        for (int kb = 0; kb < 2; ++kb) {
+          const u32x4 w = __builtin_bit_cast(u32x4, pf[kh][kb]);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) ls[e] = add_pair<T>(w[e], ls[e]);
-      }
-    l_run = fmaf(l_run, alpha, (ls[0] + ls[1]) + (ls[2] + ls[3]));
+          for (int e = 0; e < 4; ++e) ls[e] = add_pair<T>(w[e], ls[e]);
+        }
+      l_run = fmaf(l_run, alpha, (ls[0] + ls[1]) + (ls[2] + ls[3]));
+    }
     m_run = m_new;
     if (__any(alpha != 1.f)) {  // wave-uniform; skipped while no row's reference moves
 #pragma unroll
       for (int db = 0; db < ND; ++db) o[db] *= alpha;
+      if constexpr (RS) lacc *= alpha;
     }
   };
   // PV: O^T += V^T P^T, from V stage st.
@@ -389,6 +403,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(
           const v8 vf = __builtin_bit_cast(v8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
           o[db] = Mma<T>::run(vf, pf[kh][kb], o[db]);
         }
+        if constexpr (RS) lacc = Mma<T>::run(ones, pf[kh][kb], lacc);
       }
     }
   };
@@ -401,14 +416,21 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(
     qk(stq);
     // PV MFMAs take two transposed reads each, QK MFMAs one read
     constexpr int kAhead = 4;               // MFMAs whose operands are read ahead
-    constexpr int kPv = 2 * NH * ND, kQk = NH * NK;
-    __builtin_amdgcn_sched_group_barrier(0x100, 2 * kAhead, 0);  // DS reads
+    // (the row-sum MFMA that ends each 16-key step when RS reads nothing)
+    constexpr int kStep = ND + (RS ? 1 : 0);  // PV MFMAs per 16-key step
+    constexpr int kPv = 2 * NH * kStep, kQk = NH * NK;
+#pragma unroll
+    for (int j = 0; j < kAhead; ++j)
+      if (!(RS && j % kStep == ND)) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS reads
 #pragma unroll
     for (int i = 0; i < kPv + kQk; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
       const int j = i + kAhead;                           // operand reads for MFMA j
-      if (j < kPv) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      else if (j < kPv + kQk) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      if (j < kPv) {
+        if (!(RS && j % kStep == ND)) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      } else if (j < kPv + kQk) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
     }
   };
 
@@ -495,7 +517,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(
   }
 
   // ---- epilogue: O / l, logsumexp --------------------------------------------------
-  const float l_tot = sum_halves(l_run);
+  const float l_tot = RS ? lacc[0] : sum_halves(l_run);
   // a block-sparse row can see no key at all: O = 0 and logsumexp -inf there
   const float inv = (SPARSE && l_tot == 0.f) ? 0.f : 1.f / l_tot;
   {
