@@ -214,8 +214,8 @@ int fa_decode_f16(const void* q, const void* k, const void* v, void* o, float* l
  *
  * The N x N weights are not stored by the forward pass; they are recomputed
  * tile by tile from Q and K and normalised in one step with the saved per-row
- * statistic (the backward-pass paragraphs of "Online softmax, and the register
- * that can't move"): P = exp(scale * q_i . k_j - lse_i).  With D_i = <dO_i, O_i>:
+ * statistic (the backward-pass paragraphs of "Online Softmax: Tiling Across
+ * a Reduction"): P = exp(scale * q_i . k_j - lse_i).  With D_i = <dO_i, O_i>:
  *   dV = P^T dO,  dS = P o (dO V^T - D),  dQ = scale dS K,  dK = scale dS^T Q.
  *
  *  q, k, v, o, dout [B, H, N, d] bfloat16, 16-byte aligned, read only; o is

@@ -6,8 +6,7 @@
 // N x N weights: with the saved per-row statistic lse_i (natural-log
 // logsumexp of the scaled scores), every score tile is rebuilt from Q and K and
 // normalised in one step, P = exp(scale * s - lse), with no running update
-// (backward-pass paragraphs of "Online softmax, and the register that can't
-// move").  The gradients are the chain rule through the forward definition:
+// (backward-pass paragraphs of "Online Softmax: Tiling Across a Reduction").  The gradients are the chain rule through the forward definition:
 //     dV = P^T dO,  dP = dO V^T,  dS = P o (dP - D),  D_i = sum_j P_ij dP_ij,
 //     dQ = scale dS K,  dK = scale dS^T Q,
 // and D_i = <dO_i, O_i> because O = P V.  Exponentials run in base 2 with

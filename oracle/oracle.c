@@ -33,8 +33,7 @@
  *                                 rescaled by exp(m_old - m_new), O/l once at
  *                                 the end.  It records every rescale factor.
  *
- * The backward pass (gradients of O with respect to Q, K and V for an
- * upstream gradient dO) is the chain rule through that definition:
+ * The masked forms are the same definition over an explicit visible set:
  *
  *   oracle_attention_ranged   -- the same with an explicit key range per query
  *                                (sliding windows and document boundaries of
@@ -43,13 +42,16 @@
  *   oracle_attention_keyset   -- the same with an explicit key list per query
  *                                (block-sparse masks, same paragraph).
  *
+ * The backward pass (gradients of O with respect to Q, K and V for an
+ * upstream gradient dO) is the chain rule through that definition:
+ *
  *   oracle_attention_backward -- dV = P^T dO, dP = dO V^T,
  *                                dS = P o (dP - D) with D_i = sum_j P_ij dP_ij
  *                                (= <dO_i, O_i>; optionally from a given O),
  *                                dQ = scale dS K, dK = scale dS^T Q,
  *                                in the order the backward-pass paragraphs of
- *                                "Online softmax, and the register that can't
- *                                move" describe: the forward statistics of
+ *                                "Online Softmax: Tiling Across a Reduction"
+ *                                describe: the forward statistics of
  *                                every row first, then every score recomputed
  *                                from Q and K and normalised with the saved
  *                                statistic in one step (no running update).

@@ -13,7 +13,8 @@ import torch
 import online_softmax_04_amd as fa
 import oracle
 import workloads
-from gpu_util import TORCH_DTYPE, gate, say, to_device, to_f64
+from gpu_util import (TORCH_DTYPE, causal_vis, gate, gate_lse, lse_tolerance, say, to_device,
+                      to_f64)
 
 pytestmark = pytest.mark.gpu
 
@@ -39,7 +40,7 @@ def run_gpu(q, k, v, dtype, scale, causal, with_lse=True):
 def check_against_oracle(orc, name, q, k, v, dtype, scale, causal, o, lse, rows_of=None,
                          max_abs=None):
     B, H, N, d = q.shape
-    got_o, ref_o, got_l, ref_l = [], [], [], []
+    got_o, ref_o, got_l, ref_l, lb, ls = [], [], [], [], [], []
     for b in range(B):
         for h in range(H):
             rows = np.arange(N) if rows_of is None else rows_of(b, h)
@@ -49,13 +50,24 @@ def check_against_oracle(orc, name, q, k, v, dtype, scale, causal, o, lse, rows_
             got_l.append(to_f64(lse[b, h].index_select(0, rows_t)))
             ref_o.append(ro)
             ref_l.append(rl)
+            bd, sg = head_lse_tolerance(orc, q[b, h], k[b, h], rows, rl, scale, causal, dtype)
+            lb.append(bd)
+            ls.append(sg)
     go, ro = np.concatenate(got_o), np.concatenate(ref_o)
     gl, rl = np.concatenate(got_l), np.concatenate(ref_l)
     rows_all = np.concatenate([np.arange(N) if rows_of is None else rows_of(b, h)
                                for b in range(B) for h in range(H)])
     gate(f"{name} O", go, ro, dtype, rows_all, max_abs=max_abs)
-    gate(f"{name} LSE", gl[:, None], rl[:, None], dtype, rows_all, scaled=True)
+    gate_lse(f"{name} LSE", gl, rl, np.concatenate(lb), np.concatenate(ls), rows_all)
     return go, ro
+
+
+def head_lse_tolerance(orc, q, k, rows, ref_lse, scale, causal, dtype):
+    """The derived logsumexp bound and spread (gpu_util.lse_tolerance) of one head's
+    checked rows under the dense or causal rule."""
+    qv, kv = orc.to_f64(q, dtype), orc.to_f64(k, dtype)
+    n = kv.shape[0]
+    return lse_tolerance(qv[rows], kv, ref_lse, scale, dtype, causal_vis(rows, n) if causal else None)
 
 
 UNIT_ROUNDOFF = {"bf16": 2.0 ** -8, "f16": 2.0 ** -11}
@@ -73,26 +85,34 @@ def check_peaked(orc, name, q, k, v, dtype, scale, causal, o, lse):
     and their v differ, that sum is of order max|v| and exceeds the stated 1e-2,
     so an element passes when |got - ref| <= max(1e-2, 4u M + u |ref|),
     M = sum_j P_ij |v_j - O*_i| from the oracle's probabilities."""
-    B, H, N, d = q.shape
-    u = UNIT_ROUNDOFF[dtype]
+    B, H = q.shape[:2]
     for b in range(B):
         for h in range(H):
-            ro, rl = orc.attention_head(q[b, h], k[b, h], v[b, h], scale, causal, dtype=dtype)
-            vv = orc.to_f64(v[b, h], dtype)
-            m = np.stack([orc.attention_probs(q[b, h], k[b, h], scale, causal, i, dtype=dtype)
-                          @ np.abs(vv - ro[i]) for i in range(N)])
-            got = to_f64(o[b, h])
-            err = np.abs(got - ro)
-            bound = np.maximum(1e-2, 4 * u * m + u * np.abs(ro))
-            worst = float(np.max(err / bound))
-            say(f"  {name} O[{b},{h}]: max_abs={float(err.max()):.3e} worst err/bound={worst:.3f}")
-            if worst > 1.0:
-                r, c = np.unravel_index(int(np.argmax(err / bound)), err.shape)
-                raise AssertionError(f"{name}: row {r} dim {c}: |err| {err[r, c]:.3e} > bound "
-                                     f"{bound[r, c]:.3e}")
-            rel = float(np.linalg.norm(got - ro) / np.linalg.norm(ro))
-            assert rel <= 5e-3, f"{name}: rel_l2 {rel:.3e} > 5e-3"
-            gate(f"{name} LSE[{b},{h}]", to_f64(lse[b, h])[:, None], rl[:, None], dtype, scaled=True)
+            peaked_gate(orc, f"{name}[{b},{h}]", q[b, h], k[b, h], v[b, h], to_f64(o[b, h]),
+                        to_f64(lse[b, h]), dtype, scale, causal)
+
+
+def peaked_gate(orc, name, q, k, v, got, got_lse, dtype, scale, causal):
+    """check_peaked's gates for one head: storage arrays q, k, v [N, d], float64
+    outputs got [N, d] and got_lse [N]."""
+    N = q.shape[0]
+    u = UNIT_ROUNDOFF[dtype]
+    ro, rl = orc.attention_head(q, k, v, scale, causal, dtype=dtype)
+    vv = orc.to_f64(v, dtype)
+    m = np.stack([orc.attention_probs(q, k, scale, causal, i, dtype=dtype) @ np.abs(vv - ro[i])
+                  for i in range(N)])
+    err = np.abs(got - ro)
+    bound = np.maximum(1e-2, 4 * u * m + u * np.abs(ro))
+    worst = float(np.max(err / bound))
+    say(f"  {name} O: max_abs={float(err.max()):.3e} worst err/bound={worst:.3f}")
+    if worst > 1.0:
+        r, c = np.unravel_index(int(np.argmax(err / bound)), err.shape)
+        raise AssertionError(f"{name}: row {r} dim {c}: |err| {err[r, c]:.3e} > bound "
+                             f"{bound[r, c]:.3e}")
+    rel = float(np.linalg.norm(got - ro) / np.linalg.norm(ro))
+    assert rel <= 5e-3, f"{name}: rel_l2 {rel:.3e} > 5e-3"
+    bd, sg = head_lse_tolerance(orc, q, k, np.arange(N), rl, scale, causal, dtype)
+    gate_lse(f"{name} LSE", got_lse, rl, bd, sg)
 
 
 @pytest.mark.parametrize("name", ["attn_f32_n256", "attn_f32_n256_last", "attn_bf16_n4096",
@@ -151,47 +171,64 @@ def test_edge_shapes(orc, dtype, d, causal, N):
                          causal, o, lse)
 
 
+def large_score_inputs(dtype, d):
+    """Q x 10 over iid N(0, 1) inputs, [1, 2, 777, d] storage arrays."""
+    q, k, v = workloads.random_attn(1, 2, 777, d, "f32", seed=99 if d == 128 else 199)
+    q = q * np.float32(10.0)
+    return tuple(workloads.cast(t, dtype) for t in (q, k, v))
+
+
+def rising_inputs(dtype, d, step):
+    """[1, 2, 1024, d] storage arrays whose scores climb by about `step` (log2
+    units, c * score) per key tile of the 16-bit kernel (64 keys at d = 128, 128
+    at d = 64): row i climbs at rate (1 + u_i / 2), u_i uniform, on top of N(0, 1)
+    noise in the other head dims."""
+    B, H, N = 1, 2, 1024
+    scale = 1.0 / np.sqrt(d)
+    bn = 128 if d == 64 else 64
+    salt = 0 if d == 128 else 1000
+    q, k, v = workloads.random_attn(B, H, N, d, "f32", seed=int(step * 10) + 3 + salt)
+    rng = np.random.default_rng([17, int(step * 10) + salt])
+    rate = np.float32(step / (bn * scale * np.log2(np.e)))
+    q[..., 0] = np.float32(1.0) + np.float32(0.5) * rng.random((B, H, N), dtype=np.float32)
+    k[..., 0] = rate * np.arange(N, dtype=np.float32)[None, None, :]
+    return tuple(workloads.cast(t, dtype) for t in (q, k, v))
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
-def test_large_scores_force_rescales(orc, dtype, causal):
+def test_large_scores_force_rescales(orc, dtype, d, causal):
     """Q x 10 (scores of order 100): the running max keeps moving and the rescale
-    factor is far from 1 on many tiles.
+    factor is far from 1 on many tiles, at both head dims (the d = 64 kernel keeps
+    l in a matrix accumulator with its own rescale).
 
     This case lies outside the stated workloads, and its softmax rows are so
     peaked that a handful of keys carry the weight, so the 16-bit rounding of
     P no longer averages out: gated by check_peaked."""
-    B, H, N, d = 1, 2, 777, 128
-    say(f"[attention large scores] dtype={dtype} causal={causal}")
-    q, k, v = workloads.random_attn(B, H, N, d, "f32", seed=99)
-    q = q * np.float32(10.0)
-    q, k, v = (workloads.cast(t, dtype) for t in (q, k, v))
+    say(f"[attention large scores] dtype={dtype} d={d} causal={causal}")
+    q, k, v = large_score_inputs(dtype, d)
     o, lse = run_gpu(q, k, v, dtype, 1.0 / np.sqrt(d), causal)
-    check_peaked(orc, f"large {dtype} c{int(causal)}", q, k, v, dtype, 1.0 / np.sqrt(d), causal, o,
-                 lse)
+    check_peaked(orc, f"large {dtype} d{d} c{int(causal)}", q, k, v, dtype, 1.0 / np.sqrt(d),
+                 causal, o, lse)
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("step", [0.5, 3.0, 7.9, 8.1, 30.0])
-def test_rising_scores(orc, dtype, causal, step):
-    """Scores that climb by about `step` (in log2 units, c * score) per 64-key
-    tile, so the running maximum keeps moving by a controlled amount: below
-    the kernel's 2^8 slack (its reference maximum lags and O is not rescaled),
-    right at it, and far above it (rescaled on every tile).  Row i climbs at
-    rate (1 + u_i / 2), u_i uniform, on top of N(0, 1) noise in the other head
-    dims.  Late rows are peaked: gated by check_peaked."""
-    B, H, N, d = 1, 2, 1024, 128
-    say(f"[attention rising scores] dtype={dtype} causal={causal} step={step}")
+def test_rising_scores(orc, dtype, d, causal, step):
+    """Scores that climb by about `step` per key tile (rising_inputs), so the
+    running maximum keeps moving by a controlled amount: below the kernel's 2^8
+    slack (its reference maximum lags and O is not rescaled), right at it, and
+    far above it (rescaled on every tile).  Late rows are peaked: gated by
+    check_peaked."""
+    say(f"[attention rising scores] dtype={dtype} d={d} causal={causal} step={step}")
+    q, k, v = rising_inputs(dtype, d, step)
     scale = 1.0 / np.sqrt(d)
-    q, k, v = workloads.random_attn(B, H, N, d, "f32", seed=int(step * 10) + 3)
-    rng = np.random.default_rng([17, int(step * 10)])
-    rate = np.float32(step / (64 * scale * np.log2(np.e)))
-    q[..., 0] = np.float32(1.0) + np.float32(0.5) * rng.random((B, H, N), dtype=np.float32)
-    k[..., 0] = rate * np.arange(N, dtype=np.float32)[None, None, :]
-    q, k, v = (workloads.cast(t, dtype) for t in (q, k, v))
     o, lse = run_gpu(q, k, v, dtype, scale, causal)
-    check_peaked(orc, f"rising {dtype} c{int(causal)} step{step}", q, k, v, dtype, scale, causal,
-                 o, lse)
+    check_peaked(orc, f"rising {dtype} d{d} c{int(causal)} step{step}", q, k, v, dtype, scale,
+                 causal, o, lse)
 
 
 def test_lse_optional(orc):
@@ -239,5 +276,5 @@ def test_head_shard_shape(orc):
         ro, rl = orc.attention_head(q[b, h], k[b, h], v[b, h], w.sm_scale, True, rows, dtype=w.dtype)
         rt = torch.from_numpy(rows).cuda()
         gate(f"shard head ({b},{h}) O", to_f64(o[b, h].index_select(0, rt)), ro, w.dtype, rows)
-        gate(f"shard head ({b},{h}) LSE", to_f64(lse[b, h].index_select(0, rt))[:, None], rl[:, None],
-             w.dtype, rows, scaled=True)
+        bd, sg = head_lse_tolerance(orc, q[b, h], k[b, h], rows, rl, w.sm_scale, True, w.dtype)
+        gate_lse(f"shard head ({b},{h}) LSE", to_f64(lse[b, h].index_select(0, rt)), rl, bd, sg, rows)

@@ -171,11 +171,12 @@ def test_backward_chain(orc, causal, N):
 
 def test_backward_headline_shape(orc):
     """The B8 H32 N8192 d128 causal workload (K rows x U(0.5, 2)) in its full launch;
-    heads (0, 0) and (7, 31) get the oracle's O and logsumexp and are checked in full,
-    the other heads get the GPU forward's."""
+    eight heads, one in each batch row and spread over the head index (so over
+    the XCD groups of the launch), get the oracle's O and logsumexp and are
+    checked in full; the other heads get the GPU forward's."""
     w = workloads.ATTN["attn_bf16_b8h32n8192_causal"]
-    heads = [(0, 0), (7, 31)]
-    say("[attention backward] attn_bf16_b8h32n8192_causal, heads (0,0) and (7,31) checked")
+    heads = [(b, (9 * b) % w.H) for b in range(w.B)]
+    say(f"[attention backward] attn_bf16_b8h32n8192_causal, heads {heads} checked")
     q, k, v = workloads.attn_full(w, threads=16)
     g = workloads.cast(upstream((w.B, w.H, w.N, w.d), 1), "bf16")
     qd, kd, vd = (to_device(t, "bf16") for t in (q, k, v))

@@ -2,7 +2,8 @@
 against the fp64 oracle's explicit key lists: query i sees every key of the
 128-key blocks listed for its 256-row query block, cut at N, and with causal
 only keys j <= i.  Gates are the stated ones (bf16 / fp16: max-abs 1e-2,
-relative L2 5e-3; the logsumexp scaled by max(1, |lse|)); rows that see no key
+relative L2 5e-3; the logsumexp within the bound derived from its arithmetic,
+gpu_util.lse_tolerance, over each row's visible keys); rows that see no key
 must hold O = 0 and lse = -inf exactly."""
 import numpy as np
 import pytest
@@ -11,7 +12,7 @@ import torch
 import online_softmax_04_amd as fa
 import oracle
 import workloads
-from gpu_util import gate, say, to_device, to_f64
+from gpu_util import gate, gate_lse, lse_tolerance, say, set_vis, to_device, to_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -51,7 +52,7 @@ def check(orc, name, q, k, v, ptr, idx, causal, dtype, scale, o, lse, rows_of=No
     B, H, N, d = q.shape
     optr = ptr if oracle_ptr is None else oracle_ptr
     oidx = idx if oracle_idx is None else oracle_idx
-    go, ro, gl, rl = [], [], [], []
+    go, ro, gl, rl, lb, ls = [], [], [], [], [], []
     for b, h in heads or [(b, h) for b in range(B) for h in range(H)]:
         rows = np.arange(N) if rows_of is None else rows_of(b, h)
         oo, ll = orc.attention_blocksparse(q[b, h], k[b, h], v[b, h], scale, causal, optr, oidx,
@@ -61,7 +62,11 @@ def check(orc, name, q, k, v, ptr, idx, causal, dtype, scale, o, lse, rows_of=No
         gl.append(to_f64(lse[b, h].index_select(0, rt)))
         ro.append(oo)
         rl.append(ll)
-    go, ro, gl, rl = (np.concatenate(x) for x in (go, ro, gl, rl))
+        bd, sg = blocksparse_lse_tolerance(orc, q[b, h], k[b, h], rows, ll, scale, causal, optr, oidx,
+                                           dtype)
+        lb.append(bd)
+        ls.append(sg)
+    go, ro, gl, rl, lb, ls = (np.concatenate(x) for x in (go, ro, gl, rl, lb, ls))
     empty = np.isneginf(rl)
     say(f"  {name}: {int(empty.sum())} of {rl.size} checked rows see no key")
     if empty.any():
@@ -69,7 +74,21 @@ def check(orc, name, q, k, v, ptr, idx, causal, dtype, scale, o, lse, rows_of=No
         assert np.all(go[empty] == 0.0), f"{name}: O of a row without keys is not 0"
     if (~empty).any():
         gate(f"{name} O", go[~empty], ro[~empty], dtype)
-        gate(f"{name} LSE", gl[~empty][:, None], rl[~empty][:, None], dtype, scaled=True)
+        gate_lse(f"{name} LSE", gl[~empty], rl[~empty], lb[~empty], ls[~empty])
+
+
+def blocksparse_lse_tolerance(orc, q, k, rows, ref_lse, scale, causal, ptr, idx, dtype):
+    """gpu_util.lse_tolerance over each row's listed keys (rows without keys get
+    an infinite bound; their -inf is checked exactly)."""
+    n = q.shape[0]
+    sets = [orc.block_sparse_keys(n, int(i), ptr, idx, QB, KB, causal) for i in rows]
+    live = np.array([len(s) > 0 for s in sets], bool)
+    bound, sigma = np.full(len(rows), np.inf), np.full(len(rows), np.inf)
+    if live.any():
+        vis = set_vis([s for s, a in zip(sets, live) if a], n)
+        bound[live], sigma[live] = lse_tolerance(orc.to_f64(q, dtype)[np.asarray(rows)[live]],
+                                                 orc.to_f64(k, dtype), ref_lse[live], scale, dtype, vis)
+    return bound, sigma
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])

@@ -1,8 +1,9 @@
 """Causal attention with a sliding window and packed-document starts
 (fa_fwd_local) on the GPU, through the C ABI, against the fp64 oracle's
 explicit key ranges: query i sees keys max(doc start, i - window + 1) .. i.
-Gates are the stated ones (bf16 / fp16: max-abs 1e-2, relative L2 5e-3; the
-logsumexp scaled by max(1, |lse|))."""
+Gates are the stated ones (bf16 / fp16: max-abs 1e-2, relative L2 5e-3); the
+logsumexp takes the bound derived from its arithmetic (gpu_util.lse_tolerance)
+over each row's visible keys."""
 import numpy as np
 import pytest
 import torch
@@ -10,7 +11,7 @@ import torch
 import online_softmax_04_amd as fa
 import oracle
 import workloads
-from gpu_util import TORCH_DTYPE, gate, say, to_device, to_f64
+from gpu_util import TORCH_DTYPE, gate, gate_lse, lse_tolerance, range_vis, say, to_device, to_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -35,7 +36,7 @@ def run_local(q, k, v, doc, window, dtype, scale):
 
 def check(orc, name, q, k, v, doc, window, dtype, scale, o, lse, rows_of=None, heads=None):
     B, H, N, d = q.shape
-    go, ro, gl, rl = [], [], [], []
+    go, ro, gl, rl, lb, ls = [], [], [], [], [], []
     for b, h in heads or [(b, h) for b in range(B) for h in range(H)]:
         lo, hi = workloads.local_ranges(np.zeros(N, np.int64) if doc is None else doc[b], window)
         rows = np.arange(N) if rows_of is None else rows_of(b, h)
@@ -45,8 +46,12 @@ def check(orc, name, q, k, v, doc, window, dtype, scale, o, lse, rows_of=None, h
         gl.append(to_f64(lse[b, h].index_select(0, rt)))
         ro.append(oo)
         rl.append(ll)
+        bd, sg = lse_tolerance(orc.to_f64(q[b, h], dtype)[rows], orc.to_f64(k[b, h], dtype), ll, scale,
+                               dtype, range_vis(rows, lo, hi, N))
+        lb.append(bd)
+        ls.append(sg)
     gate(f"{name} O", np.concatenate(go), np.concatenate(ro), dtype)
-    gate(f"{name} LSE", np.concatenate(gl)[:, None], np.concatenate(rl)[:, None], dtype, scaled=True)
+    gate_lse(f"{name} LSE", np.concatenate(gl), np.concatenate(rl), np.concatenate(lb), np.concatenate(ls))
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])

@@ -11,7 +11,8 @@ import torch
 import online_softmax_04_amd as fa
 import oracle
 import workloads
-from gpu_util import gate, say, to_device, to_f64
+from gpu_util import (causal_vis, gate, gate_lse, lse_tolerance, range_vis, say, softmax_rel_gate,
+                      to_device, to_f64)
 
 pytestmark = pytest.mark.gpu
 
@@ -31,14 +32,16 @@ def draw(case):
                 seed=int(rng.integers(0, 1 << 30)), p=float(rng.uniform(0.0, 0.6)))
 
 
-def compare(orc, name, outs, refs, dtype):
+def compare(orc, name, outs, refs, dtype, tols):
+    """tols: per head, the (bound, sigma) of gpu_util.lse_tolerance for its rows."""
     go, gl = np.concatenate([o for o, _ in outs]), np.concatenate([l for _, l in outs])
     ro, rl = np.concatenate([o for o, _ in refs]), np.concatenate([l for _, l in refs])
+    lb, ls = np.concatenate([t[0] for t in tols]), np.concatenate([t[1] for t in tols])
     empty = np.isneginf(rl)
     assert np.all(np.isneginf(gl[empty])) and np.all(go[empty] == 0.0), f"{name}: empty rows"
     if (~empty).any():
         gate(f"{name} O", go[~empty], ro[~empty], dtype)
-        gate(f"{name} LSE", gl[~empty][:, None], rl[~empty][:, None], dtype, scaled=True)
+        gate_lse(f"{name} LSE", gl[~empty], rl[~empty], lb[~empty], ls[~empty])
 
 
 @pytest.mark.parametrize("case", range(CASES))
@@ -51,12 +54,14 @@ def test_random_dense(orc, case):
     o, lse = torch.empty_like(qd), torch.empty((B, H, N), dtype=torch.float32, device="cuda")
     (fa.fa_fwd if dt == "bf16" else fa.fa_fwd_f16)(qd, kd, vd, o, lse, B, H, N, d, d ** -0.5, int(c["causal"]))
     torch.cuda.synchronize()
-    outs, refs = [], []
+    outs, refs, tols = [], [], []
     for b in range(B):
         for h in range(H):
             refs.append(orc.attention_head(q[b, h], k[b, h], v[b, h], d ** -0.5, c["causal"], dtype=dt))
             outs.append((to_f64(o[b, h]), to_f64(lse[b, h])))
-    compare(orc, f"random dense {case}", outs, refs, dt)
+            tols.append(lse_tolerance(orc.to_f64(q[b, h], dt), orc.to_f64(k[b, h], dt), refs[-1][1],
+                                      d ** -0.5, dt, causal_vis(np.arange(N), N) if c["causal"] else None))
+    compare(orc, f"random dense {case}", outs, refs, dt, tols)
 
 
 @pytest.mark.parametrize("case", range(CASES))
@@ -71,13 +76,15 @@ def test_random_local(orc, case):
     entry = fa.fa_fwd_local if dt == "bf16" else fa.fa_fwd_local_f16
     entry(qd, kd, vd, o, lse, torch.from_numpy(doc).cuda(), c["window"], B, H, N, d, d ** -0.5)
     torch.cuda.synchronize()
-    outs, refs = [], []
+    outs, refs, tols = [], [], []
     for b in range(B):
         lo, hi = workloads.local_ranges(doc[b], c["window"])
         for h in range(H):
             refs.append(orc.attention_ranged(q[b, h], k[b, h], v[b, h], d ** -0.5, lo, hi, np.arange(N), dtype=dt))
             outs.append((to_f64(o[b, h]), to_f64(lse[b, h])))
-    compare(orc, f"random local {case}", outs, refs, dt)
+            tols.append(lse_tolerance(orc.to_f64(q[b, h], dt), orc.to_f64(k[b, h], dt), refs[-1][1],
+                                      d ** -0.5, dt, range_vis(np.arange(N), lo, hi, N)))
+    compare(orc, f"random local {case}", outs, refs, dt, tols)
 
 
 @pytest.mark.parametrize("case", range(CASES))
@@ -99,13 +106,16 @@ def test_random_blocksparse(orc, case):
           torch.from_numpy(idx).cuda() if idx.size else None, idx.size, B, H, N, d, d ** -0.5,
           int(c["causal"]))
     torch.cuda.synchronize()
-    outs, refs = [], []
+    import test_parity_blocksparse as bs
+    outs, refs, tols = [], [], []
     for b in range(B):
         for h in range(H):
             refs.append(orc.attention_blocksparse(q[b, h], k[b, h], v[b, h], d ** -0.5, c["causal"],
                                                   ptr, idx, 256, 128, dtype=dt))
             outs.append((to_f64(o[b, h]), to_f64(lse[b, h])))
-    compare(orc, f"random block-sparse {case}", outs, refs, dt)
+            tols.append(bs.blocksparse_lse_tolerance(orc, q[b, h], k[b, h], np.arange(N), refs[-1][1],
+                                                     d ** -0.5, c["causal"], ptr, idx, dt))
+    compare(orc, f"random block-sparse {case}", outs, refs, dt, tols)
 
 
 @pytest.mark.parametrize("case", range(CASES))
@@ -169,3 +179,4 @@ def test_random_softmax(orc, case):
     for name, got in (("rows", sm.run_gpu(x, offset)), ("split", sp.run_split(x, offset))):
         g = got.cpu().numpy().astype(np.float64)
         gate(f"random softmax {case} {name}", g, ref, "f32")
+        softmax_rel_gate(f"random softmax {case} {name}", g, ref, x)

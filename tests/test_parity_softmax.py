@@ -3,7 +3,9 @@
 The full 4096 x 32768 workload is compared element by element; edge cases
 cover every register-cache size class and its boundaries, the streaming path
 (rows longer than the cache, unaligned pointers, columns not a multiple of 4),
-constant rows, spiked rows and extreme magnitudes.  Gate: max-abs <= 1e-4.
+constant rows, spiked rows and extreme magnitudes.  Gates: max-abs <= 1e-4
+(the stated fp32 tolerance) and, on every element held as a normal fp32
+number, the relative bound of gpu_util.softmax_rel_gate.
 """
 import numpy as np
 import pytest
@@ -12,7 +14,7 @@ import torch
 import online_softmax_04_amd as fa
 import oracle
 import workloads
-from gpu_util import gate, say, to_f64
+from gpu_util import gate, say, softmax_rel_gate, to_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -44,6 +46,7 @@ def test_workload(orc):
     got = to_f64(y)
     ref = orc.softmax_rows(x)
     gate(w.name, got, ref, "f32")
+    softmax_rel_gate(w.name, got, ref, x)
     sums = got.sum(axis=1)
     assert np.max(np.abs(sums - 1.0)) < 1e-4
     # relative accuracy where it matters: the +50 entries carry the mass
@@ -68,7 +71,9 @@ def test_edge_cols(orc, cols, offset):
     rows = 5
     say(f"[softmax edge] cols={cols} offset={offset}")
     x = workloads.random_rows(rows, cols, seed=cols, std=3.0, spike_prob=0.01)
-    gate(f"cols={cols} off={offset}", to_f64(run_gpu(x, offset)), orc.softmax_rows(x), "f32")
+    got, ref = to_f64(run_gpu(x, offset)), orc.softmax_rows(x)
+    gate(f"cols={cols} off={offset}", got, ref, "f32")
+    softmax_rel_gate(f"cols={cols} off={offset}", got, ref, x)
 
 
 @pytest.mark.parametrize("cols", [7, 4096, 32768, 40000])
@@ -81,8 +86,9 @@ def test_special_rows(orc, cols):
     x[2] = np.linspace(-60, 60, cols, dtype=np.float32)
     x[3] = -3e38                                 # extreme but finite
     x[3, 0] = 0.0
-    got = to_f64(run_gpu(x))
-    gate(f"special cols={cols}", got, orc.softmax_rows(x), "f32")
+    got, ref = to_f64(run_gpu(x)), orc.softmax_rows(x)
+    gate(f"special cols={cols}", got, ref, "f32")
+    softmax_rel_gate(f"special cols={cols}", got, ref, x)
     assert np.allclose(got[0], 1.0 / cols, rtol=1e-5, atol=0)
     assert got[1, cols // 2] == 1.0
 
@@ -90,7 +96,9 @@ def test_special_rows(orc, cols):
 def test_many_rows_small_cols(orc):
     x = workloads.random_rows(70000, 33, seed=3)
     say("[softmax many rows]")
-    gate("70000x33", to_f64(run_gpu(x)), orc.softmax_rows(x), "f32")
+    got, ref = to_f64(run_gpu(x)), orc.softmax_rows(x)
+    gate("70000x33", got, ref, "f32")
+    softmax_rel_gate("70000x33", got, ref, x)
 
 
 def test_wrapper():

@@ -22,7 +22,7 @@ import torch
 import online_softmax_04_amd as fa
 import oracle
 import workloads
-from gpu_util import gate, say, to_f64
+from gpu_util import gate, say, softmax_rel_gate, to_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -100,6 +100,7 @@ def test_special_rows(orc, cols):
     got = to_f64(run_split(x))
     ref = orc.softmax_rows(x)
     gate(f"split special cols={cols}", got, ref, "f32")
+    softmax_rel_gate(f"split special cols={cols}", got, ref, x)
     assert np.allclose(got[0], 1.0 / cols, rtol=1e-5, atol=0)
     assert got[1, cols // 2] == 1.0 and got[3, cols - 1] == 1.0
 
