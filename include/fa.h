@@ -57,7 +57,8 @@ typedef enum {
   FA_ERR_INVALID_ARG = -1, /* null pointer, size < 1, bad scale, overlapping buffers, size overflow */
   FA_ERR_UNSUPPORTED = -2, /* a head dimension the library has no kernel for (d other than 64, 128) */
   FA_ERR_ALIGNMENT = -3,   /* a pointer without the alignment the operation needs */
-  FA_ERR_HIP = -4          /* the HIP runtime reported an error at launch */
+  FA_ERR_HIP = -4,         /* the HIP runtime reported an error at launch */
+  FA_ERR_SCRATCH_LIMIT = -5 /* fa_decode_static: the sizes need more than its static scratch */
 } fa_status;
 
 /*
@@ -207,6 +208,28 @@ int fa_decode(const void* q, const void* k, const void* v, void* o, float* lse, 
 int fa_decode_f16(const void* q, const void* k, const void* v, void* o, float* lse,
                   float* workspace, size_t workspace_bytes, int B, int H, int Nq, int Nk, int d,
                   float scale, int causal, hipStream_t stream);
+
+/*
+ * fa_decode without a workspace argument, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  The call allocates nothing (no hipMalloc, hipFree or
+ * allocating library routine) and clears nothing; the partials live in a
+ * static device array of FA_DECODE_STATIC_SCRATCH_BYTES that the library holds
+ * on every GPU it runs on until the process ends (its address is looked up
+ * once per device, on the first call there).
+ *
+ *  Arguments, layouts, arithmetic and results are those of fa_decode (bf16)
+ *  with the workspace taken from that array.
+ *  FA_ERR_SCRATCH_LIMIT when fa_decode_workspace_bytes(B, H, Nq, Nk, d)
+ *  exceeds FA_DECODE_STATIC_SCRATCH_BYTES (every other error as fa_decode).
+ *  Every call on one GPU shares that GPU's array and leaves its partials
+ *  there: calls that overlap in time on one GPU (different streams, or other
+ *  host threads, without ordering between them) race on it and give wrong
+ *  results.  Calls ordered on one stream are safe.
+ */
+#define FA_DECODE_STATIC_SCRATCH_BYTES ((size_t)8 << 20)
+int fa_decode_static(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                     int H, int Nq, int Nk, int d, float scale, int causal, hipStream_t stream);
 
 /*
  * Attention backward: the gradients dQ, dK, dV of O = softmax(scale * Q K^T) V

@@ -17,6 +17,7 @@ __all__ = [
     "FaError", "lib", "fa_fwd", "fa_fwd_f16", "fa_fwd_f32", "online_softmax_rows",
     "online_softmax_rows_split", "online_softmax_split_workspace_bytes", "softmax_split",
     "fa_decode", "fa_decode_f16", "fa_decode_workspace_bytes", "attention_decode", "fa_fwd_fp8",
+    "fa_decode_static", "DECODE_STATIC_SCRATCH_BYTES", "FA_ERR_SCRATCH_LIMIT",
     "fa_fwd_local", "fa_fwd_local_f16", "fa_fwd_blocksparse", "fa_fwd_blocksparse_f16",
     "attention_blocksparse", "SPARSE_QBLOCK", "SPARSE_KBLOCK",
     "fa_status_string", "kernel_attributes", "attention", "softmax", "LIB_PATH",
@@ -30,6 +31,10 @@ FA_ERR_INVALID_ARG = -1
 FA_ERR_UNSUPPORTED = -2
 FA_ERR_ALIGNMENT = -3
 FA_ERR_HIP = -4
+FA_ERR_SCRATCH_LIMIT = -5
+
+# bytes of the static device array fa_decode_static takes its partials from
+DECODE_STATIC_SCRATCH_BYTES = 8 << 20
 
 OP_FA_FWD, OP_FA_FWD_F16, OP_FA_FWD_F32, OP_SOFTMAX = 0, 1, 2, 3
 OP_FA_BWD_DQ, OP_FA_BWD_DKDV, OP_FA_DECODE, OP_FA_FWD_FP8 = 4, 5, 6, 7
@@ -85,6 +90,8 @@ def lib() -> ctypes.CDLL:
             fn = getattr(L, name)
             fn.argtypes = [vp] * 6 + [ctypes.c_size_t, i, i, i, i, i, f, i, vp]
             fn.restype = i
+        L.fa_decode_static.argtypes = [vp] * 5 + [i, i, i, i, i, f, i, vp]
+        L.fa_decode_static.restype = i
         L.fa_decode_workspace_bytes.argtypes = [i, i, i, i, i]
         L.fa_decode_workspace_bytes.restype = ctypes.c_size_t
         L.fa_bwd_workspace_bytes.argtypes = [i, i, i]
@@ -237,6 +244,14 @@ def fa_decode_f16(q, k, v, o, lse, workspace, workspace_bytes, B, H, Nq, Nk, d, 
     """fp16 split-KV attention of Nq queries at the end of Nk keys (see include/fa.h)."""
     _decode("fa_decode_f16", q, k, v, o, lse, workspace, workspace_bytes, B, H, Nq, Nk, d, scale,
             causal, stream)
+
+
+def fa_decode_static(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, stream=None):
+    """fa_decode (bf16) with its partials in the library's static device array: no
+    workspace argument, nothing allocated (see include/fa.h)."""
+    _check(lib().fa_decode_static(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), int(B), int(H),
+                                  int(Nq), int(Nk), int(d), float(scale), int(causal),
+                                  _stream(stream)), "fa_decode_static")
 
 
 def fa_decode_workspace_bytes(B, H, Nq, Nk, d) -> int:

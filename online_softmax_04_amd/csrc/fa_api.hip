@@ -4,11 +4,40 @@
 #include <climits>
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "fa.h"
 #include "kernels.h"
 
+// Scratch memory of fa_decode_static: the decode partials (m, l, unnormalised
+// O) live in this file-scope device array instead of a caller's workspace.
+// Every GPU the library runs on holds one copy until the process ends, and
+// every fa_decode_static call on that GPU shares it.  In host code `scratch`
+// names a host-side stand-in, not the device array: its device address is
+// looked up per device with hipGetSymbolAddress (decode_scratch below) and
+// only that address is handed to kernels.
+static __device__ __align__(256) unsigned char scratch[FA_DECODE_STATIC_SCRATCH_BYTES];
+
 namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device, looked up on the first
+// call per device and kept.
+int decode_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return FA_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return FA_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return FA_OK;
+}
 
 bool overlaps(const void* a, uint64_t abytes, const void* b, uint64_t bbytes) {
   const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
@@ -168,10 +197,13 @@ uint64_t decode_workspace(int B, int H, int Nq, int Nk, int d, int* n_chunks) {
   return tensor_bytes((int)bh, nc, Nq, 1, 4 * (uint64_t)d + 8);
 }
 
+// static_scratch: take the partials from the library's scratch array (workspace
+// and workspace_bytes are ignored); a call needing more than it holds gets
+// FA_ERR_SCRATCH_LIMIT.
 int decode_entry(osm::Elem elem, const void* q, const void* k, const void* v, void* o, float* lse,
                  float* workspace, size_t workspace_bytes, int B, int H, int Nq, int Nk, int d,
-                 float scale, int causal, hipStream_t stream) {
-  if (!q || !k || !v || !o || !workspace) return FA_ERR_INVALID_ARG;
+                 float scale, int causal, hipStream_t stream, bool static_scratch = false) {
+  if (!q || !k || !v || !o || (!workspace && !static_scratch)) return FA_ERR_INVALID_ARG;
   if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || d < 1) return FA_ERR_INVALID_ARG;
   if (!std::isfinite(scale) || !(scale > 0.f)) return FA_ERR_INVALID_ARG;
   if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
@@ -190,9 +222,13 @@ int decode_entry(osm::Elem elem, const void* q, const void* k, const void* v, vo
   if (bh * (uint64_t)n_chunks * (((uint64_t)Nq + 31) / 32) > (uint64_t)INT_MAX ||
       bh * (uint64_t)Nq > (uint64_t)INT_MAX)
     return FA_ERR_INVALID_ARG;
-  if ((uint64_t)workspace_bytes < ws) return FA_ERR_INVALID_ARG;
+  if (static_scratch) {
+    if (ws > (uint64_t)FA_DECODE_STATIC_SCRATCH_BYTES) return FA_ERR_SCRATCH_LIMIT;
+  } else if ((uint64_t)workspace_bytes < ws) {
+    return FA_ERR_INVALID_ARG;
+  }
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
-      !aligned(workspace, 16))
+      (!static_scratch && !aligned(workspace, 16)))
     return FA_ERR_ALIGNMENT;
   if (lse && !aligned(lse, 4)) return FA_ERR_ALIGNMENT;
   // outputs (o, lse, workspace) overlap neither each other nor any input
@@ -205,6 +241,15 @@ int decode_entry(osm::Elem elem, const void* q, const void* k, const void* v, vo
     if (overlaps(outs[a], out_bytes[a], q, qbytes) || overlaps(outs[a], out_bytes[a], k, kbytes) ||
         overlaps(outs[a], out_bytes[a], v, kbytes))
       return FA_ERR_INVALID_ARG;
+  }
+  if (static_scratch) {
+    // every host-side check has passed: only now touch the runtime
+    void* p = nullptr;
+    const int st = decode_scratch(&p);
+    if (st != FA_OK) return st;
+    if (overlaps(o, qbytes, p, ws) || (lse && overlaps(lse, lse_bytes, p, ws)))
+      return FA_ERR_INVALID_ARG;
+    workspace = static_cast<float*>(p);
   }
   hipError_t e = osm::launch_attn_decode(elem, q, k, v, o, lse, workspace, B, H, Nq, Nk, d, scale,
                                          causal != 0, stream);
@@ -232,6 +277,12 @@ int fa_decode_f16(const void* q, const void* k, const void* v, void* o, float* l
                   float scale, int causal, hipStream_t stream) {
   return decode_entry(osm::Elem::f16, q, k, v, o, lse, workspace, workspace_bytes, B, H, Nq, Nk, d,
                       scale, causal, stream);
+}
+
+int fa_decode_static(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                     int H, int Nq, int Nk, int d, float scale, int causal, hipStream_t stream) {
+  return decode_entry(osm::Elem::bf16, q, k, v, o, lse, nullptr, 0, B, H, Nq, Nk, d, scale, causal,
+                      stream, true);
 }
 
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
@@ -352,6 +403,8 @@ const char* fa_status_string(int status) {
     case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: head dimension without a kernel (64 and 128 are supported)";
     case FA_ERR_ALIGNMENT: return "FA_ERR_ALIGNMENT: pointer not aligned as the operation requires";
     case FA_ERR_HIP: return "FA_ERR_HIP: the HIP runtime reported a launch error";
+    case FA_ERR_SCRATCH_LIMIT:
+      return "FA_ERR_SCRATCH_LIMIT: the call needs more scratch memory than the library's static array holds";
     default: return "unknown fa_status";
   }
 }

@@ -32,6 +32,7 @@ def test_header_declares_the_entry_points():
               "fa_fwd_blocksparse", "fa_fwd_blocksparse_f16", "fa_bwd",
               "fa_bwd_f16", "fa_bwd_workspace_bytes",
               "fa_decode", "fa_decode_f16", "fa_decode_workspace_bytes", "fa_fwd_fp8",
+              "fa_decode_static",
               "online_softmax_rows", "online_softmax_rows_split",
               "online_softmax_split_workspace_bytes", "fa_status_string", "fa_kernel_attributes"):
         assert n in names
@@ -45,7 +46,7 @@ def test_library_exports_declared_symbol(name):
 
 def test_status_strings():
     for s in (fa.FA_OK, fa.FA_ERR_INVALID_ARG, fa.FA_ERR_UNSUPPORTED, fa.FA_ERR_ALIGNMENT,
-              fa.FA_ERR_HIP):
+              fa.FA_ERR_HIP, fa.FA_ERR_SCRATCH_LIMIT):
         assert fa.fa_status_string(s).startswith("FA_")
     assert fa.fa_status_string(12345) == "unknown fa_status"
 
@@ -303,6 +304,35 @@ def call_decode(q=A, k=A + 64 * MB, v=A + 128 * MB, o=A + 192 * MB, lse=A + 200 
 ])
 def test_decode_validation(kw, status):
     assert call_decode(**kw) == status
+
+
+def call_decode_static(q=A, k=A + 64 * MB, v=A + 128 * MB, o=A + 192 * MB, lse=A + 200 * MB,
+                       B=1, H=2, Nq=3, Nk=100, d=128, scale=0.1, causal=1):
+    return fa.lib().fa_decode_static(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=0), fa.FA_ERR_INVALID_ARG), (dict(o=0), fa.FA_ERR_INVALID_ARG),
+    (dict(Nq=0), fa.FA_ERR_INVALID_ARG), (dict(scale=-1.0), fa.FA_ERR_INVALID_ARG),
+    (dict(causal=2), fa.FA_ERR_INVALID_ARG), (dict(Nq=101), fa.FA_ERR_INVALID_ARG),
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(B=8, H=32, Nq=64, Nk=65536), fa.FA_ERR_SCRATCH_LIMIT),  # 545 MB of partials
+    (dict(q=A + 8), fa.FA_ERR_ALIGNMENT), (dict(lse=A + 200 * MB + 2), fa.FA_ERR_ALIGNMENT),
+    (dict(o=A + 64 * MB + 512), fa.FA_ERR_INVALID_ARG),     # o inside k
+])
+def test_decode_static_validation(kw, status):
+    """Every error of fa_decode_static is found on the host, before the scratch
+    array is looked up (no GPU here)."""
+    assert call_decode_static(**kw) == status
+
+
+def test_decode_static_limit_is_the_headers():
+    hdr = open(os.path.join(ROOT, "include", "fa.h")).read()
+    m = re.search(r"#define FA_DECODE_STATIC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", hdr)
+    assert m and int(m.group(1)) << int(m.group(2)) == fa.DECODE_STATIC_SCRATCH_BYTES
+    # the decode workload fits
+    assert fa.fa_decode_workspace_bytes(8, 32, 1, 32768, 128) <= fa.DECODE_STATIC_SCRATCH_BYTES
+    assert fa.fa_status_string(fa.FA_ERR_SCRATCH_LIMIT).startswith("FA_ERR_SCRATCH_LIMIT")
 
 
 def call_fp8(q=A, k=A + 64 * MB, v=A + 128 * MB, o=A + 192 * MB, lse=A + 256 * MB, B=1, H=2,
