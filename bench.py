@@ -22,8 +22,11 @@ Prints ONE JSON line:
   the causal workload split 8 ways by heads (B8 H4), the split-row softmax over
   4 rows of 2^24 columns (GB/s at 8 bytes per element; it moves 12), and the
   split-KV decode of one query per head against 32768 cached keys (GB/s of
-  K, V, Q, O and LSE moved once), and the fp8 forward on the B8 H32 N8192 d128
-  causal shape (TFLOP/s against the dense fp8 peak).
+  K, V, Q, O and LSE moved once), the fp8 forward on the B8 H32 N8192 d128
+  causal shape (TFLOP/s against the dense fp8 peak), and the two head-dim-64
+  workloads (one head of 4096 keys, one causal head of 131072).  Beside the
+  softmax: a hand-written non-temporal 16-byte device copy of 512 MiB
+  (fa_stream_copy), the practical HBM ceiling, timed in the same run.
 
 Other modes:
   --ingest-counters DIR_FETCH DIR_WRITE   turn two rocprofv3 --pmc runs
@@ -51,22 +54,24 @@ SOFTMAX_WORKLOAD = "softmax_4096x32768"
 SPLIT_WORKLOAD = "softmax_split_4x16777216"
 DECODE_WORKLOAD = "decode_bf16_b8h32_q1_kv32768_d128"
 FP8_WORKLOAD = "attn_fp8_b8h32n8192_causal"
+D64_WORKLOADS = ["attn_bf16_n4096", "attn_bf16_n131072_causal"]
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBPS = 8000.0         # MI355X HBM3E, published
 PEAK_FP8_TFLOPS = 5000.0       # MI355X dense fp8 MFMA, published
-COPY_BYTES = 256 << 20         # probe copy kernel: 256 MiB read + 256 MiB written
+COPY_BYTES = 512 << 20         # probe copy (fa_stream_copy): 512 MiB read + 512 MiB written
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", f"traffic_{ATTN_WORKLOAD}+{SOFTMAX_WORKLOAD}.md")
+_SHARED = ["online_softmax_04_amd/csrc/common.h", "online_softmax_04_amd/csrc/mfma_tile.h",
+           "online_softmax_04_amd/csrc/kernels.h"]
 KERNEL_SOURCES = {
-    "attn": ["online_softmax_04_amd/csrc/attn_fwd.hip", "online_softmax_04_amd/csrc/common.h"],
-    "softmax": ["online_softmax_04_amd/csrc/softmax.hip", "online_softmax_04_amd/csrc/common.h"],
-    "fp8": ["online_softmax_04_amd/csrc/attn_fwd_fp8.hip", "online_softmax_04_amd/csrc/common.h"],
+    "attn": ["online_softmax_04_amd/csrc/attn_fwd.hip", *_SHARED],
+    "softmax": ["online_softmax_04_amd/csrc/softmax.hip", *_SHARED],
+    "fp8": ["online_softmax_04_amd/csrc/attn_fwd_fp8.hip", *_SHARED],
 }
-# kernel-name fragments of the three dispatches the counters are read for; the
-# probe copy is torch's elementwise multiply by 1 (reads and writes 256 MiB)
 # name parts that pick each kernel out of a profile of this script (the attention entry is
-# the mangled dense causal bf16 d=128 instance, not the sliding-window one)
+# the mangled dense causal bf16 d=128 instance, not the sliding-window one); the probe
+# copy is fa_stream_copy (reads and writes COPY_BYTES)
 KERNEL_NAME_PART = {"attn": "attn_fwd_mfmaIDF16bLi128ELb1ELi0E", "softmax": "softmax_cached",
-                    "copy": "MulFunctor"}
+                    "copy": "stream_copy"}
 
 
 def source_hash(kind: str) -> str:
@@ -485,6 +490,14 @@ def main():
     yd = torch.empty_like(xd)
     cs = torch.randn(COPY_BYTES // 4, device=dev)
     cd = torch.empty_like(cs)
+    # the d = 64 workloads: one head of 4096 keys, and one causal head of 131072
+    d64 = {}
+    for name in D64_WORKLOADS:
+        wd = workloads.ATTN[name]
+        hq, hk, hv = workloads.attn_full(wd, threads=16)
+        d64[name] = (wd, to(hq), to(hk), to(hv), torch.empty((wd.B, wd.H, wd.N, wd.d),
+                     dtype=torch.bfloat16, device=dev),
+                     torch.empty((wd.B, wd.H, wd.N), dtype=torch.float32, device=dev))
     stream = torch.cuda.current_stream()
     print("[bench] inputs resident; warming up", file=sys.stderr, flush=True)
 
@@ -500,15 +513,18 @@ def main():
 
     for _ in range(args.warmup):
         step()
-    # probe copy: the known-size kernel that scales the byte counters
-    torch.mul(cs, 1.0, out=cd)
-    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    c0.record(stream)
-    for _ in range(5):
-        torch.mul(cs, 1.0, out=cd)
-    c1.record(stream)
+    # probe copy (non-temporal 16-byte loads and stores): the practical HBM ceiling
+    # beside the softmax, and the known-size kernel that scales the byte counters
+    for _ in range(3):
+        fa.fa_stream_copy(cs, cd, COPY_BYTES, stream)
+    cev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(10)]
+    for e in cev:
+        e[0].record(stream)
+        fa.fa_stream_copy(cs, cd, COPY_BYTES, stream)
+        e[1].record(stream)
     torch.cuda.synchronize()
-    copy_ms = c0.elapsed_time(c1) / 5
+    copy_each = sorted(e[0].elapsed_time(e[1]) for e in cev)
+    copy_ms = sum(copy_each) / len(copy_each)
 
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     torch.cuda.synchronize()
@@ -694,6 +710,29 @@ def main():
     del dqd, dkd, dvd
     print(f"[bench] decode {dec_ms * 1e3:.1f} us", file=sys.stderr, flush=True)
 
+    # the d = 64 workloads (one head each): TFLOP/s against the same bf16 peak
+    d64_out = {}
+    for name, (wd, hq, hk, hv, ho, hl) in d64.items():
+        def fwd64(wd=wd, hq=hq, hk=hk, hv=hv, ho=ho, hl=hl):
+            fa.fa_fwd(hq, hk, hv, ho, hl, wd.B, wd.H, wd.N, wd.d, wd.sm_scale, int(wd.causal), stream)
+
+        for _ in range(args.warmup):
+            fwd64()
+        each = timed(fwd64, args.steps)
+        ms = sum(each) / args.steps
+        tf = wd.flops / (ms * 1e-3) / 1e12
+        d64_out[name] = {
+            "value": round(tf, 2), "unit": "TFLOP/s", "flop_per_launch": wd.flops,
+            "B": wd.B, "H": wd.H, "N": wd.N, "d": wd.d, "causal": wd.causal,
+            "avg_launch_ms": round(ms, 5), "median_launch_ms": round(each[len(each) // 2], 5),
+            "min_launch_ms": round(each[0], 5),
+            "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                         "kernel": f"attn_fwd_mfma<bf16,64,{'causal' if wd.causal else 'dense'}>",
+                         "workgroups": wd.B * wd.H * (-(-wd.N // 256))}}
+        print(f"[bench] {name} {ms:.3f} ms", file=sys.stderr, flush=True)
+    del d64
+
     tflops = w.flops / (attn_ms * 1e-3) / 1e12
     sm_bytes = sw.algorithmic_bytes
     sm_gbps = sm_bytes / (sm_ms * 1e-3) / 1e9
@@ -730,7 +769,10 @@ def main():
                                  "bytes_per_launch": sm_bytes, "avg_launch_us": round(sm_ms * 1e3, 2),
                                  "median_launch_us": round(sm_each[len(sm_each) // 2] * 1e3, 2),
                                  "min_launch_us": round(sm_each[0] * 1e3, 2)},
-                    "copy_gbps": round(2 * COPY_BYTES / (copy_ms * 1e-3) / 1e9, 1)},
+                    "copy_gbps": round(2 * COPY_BYTES / (copy_ms * 1e-3) / 1e9, 1),
+                    "copy_kernel": "stream_copy (fa_stream_copy, 16-byte non-temporal, "
+                                   f"{COPY_BYTES >> 20} MiB read + {COPY_BYTES >> 20} MiB written)",
+                    "frac_of_copy": round(sm_gbps / (2 * COPY_BYTES / (copy_ms * 1e-3) / 1e9), 4)},
         "backward": {"value": round(bwd_tflops, 2), "unit": "TFLOP/s",
                      "flop_per_launch": bwd_flop,
                      "mfma_flop_issued_per_launch": 3.5 * w.flops,
@@ -792,6 +834,7 @@ def main():
                                 "frac": round(dec_gbps / PEAK_HBM_GBPS, 4),
                                 "kernels": ["attn_decode_partial<bf16,128,causal>",
                                             "attn_decode_merge<bf16,128>"]}},
+        "d64": d64_out,
         "kernel_resources": {"attention": attrs, "softmax": sm_attrs,
                              "decode": fa.kernel_attributes(fa.OP_FA_DECODE, dw.d, dw.causal),
                              "backward_dq": fa.kernel_attributes(fa.OP_FA_BWD_DQ, w.d, True),

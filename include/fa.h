@@ -304,6 +304,17 @@ size_t online_softmax_split_workspace_bytes(int rows, int cols);
 int online_softmax_rows_split(const float* x, float* y, int rows, int cols, float* workspace,
                               size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * Measurement utility: y[0 .. bytes) = x[0 .. bytes) with 16-byte non-temporal
+ * loads and stores, the practical HBM ceiling of a streaming kernel (one read
+ * and one write per byte, as the register-cached row softmax moves; "5.2 CUDA
+ * Online Softmax", section 6).  Benchmarks time it beside the softmax and use
+ * it as the kernel of known size that calibrates byte counters.
+ *  x, y   device pointers, 16-byte aligned (FA_ERR_ALIGNMENT), not overlapping.
+ *  bytes  a positive multiple of 16 (else FA_ERR_INVALID_ARG).
+ */
+int fa_stream_copy(const void* x, void* y, size_t bytes, hipStream_t stream);
+
 /* Static description of an fa_status value (never NULL). */
 const char* fa_status_string(int status);
 

@@ -17,7 +17,7 @@ __all__ = [
     "FaError", "lib", "fa_fwd", "fa_fwd_f16", "fa_fwd_f32", "online_softmax_rows",
     "online_softmax_rows_split", "online_softmax_split_workspace_bytes", "softmax_split",
     "fa_decode", "fa_decode_f16", "fa_decode_workspace_bytes", "attention_decode", "fa_fwd_fp8",
-    "fa_decode_static", "DECODE_STATIC_SCRATCH_BYTES", "FA_ERR_SCRATCH_LIMIT",
+    "fa_decode_static", "DECODE_STATIC_SCRATCH_BYTES", "FA_ERR_SCRATCH_LIMIT", "fa_stream_copy",
     "fa_fwd_local", "fa_fwd_local_f16", "fa_fwd_blocksparse", "fa_fwd_blocksparse_f16",
     "attention_blocksparse", "SPARSE_QBLOCK", "SPARSE_KBLOCK",
     "fa_status_string", "kernel_attributes", "attention", "softmax", "LIB_PATH",
@@ -102,12 +102,20 @@ def lib() -> ctypes.CDLL:
         L.online_softmax_split_workspace_bytes.restype = ctypes.c_size_t
         L.online_softmax_rows_split.argtypes = [vp, vp, i, i, vp, ctypes.c_size_t, vp]
         L.online_softmax_rows_split.restype = i
+        L.fa_stream_copy.argtypes = [vp, vp, ctypes.c_size_t, vp]
+        L.fa_stream_copy.restype = i
         L.fa_status_string.argtypes = [i]
         L.fa_status_string.restype = ctypes.c_char_p
         L.fa_kernel_attributes.argtypes = [i, i, i, ctypes.POINTER(_Attrs)]
         L.fa_kernel_attributes.restype = i
         _lib = L
     return _lib
+
+
+def fa_stream_copy(x, y, nbytes, stream=None):
+    """Copy nbytes (multiple of 16) with non-temporal 16-byte accesses: the HBM
+    ceiling the benchmark reports beside the row softmax (see include/fa.h)."""
+    _check(lib().fa_stream_copy(_ptr(x), _ptr(y), int(nbytes), _stream(stream)), "fa_stream_copy")
 
 
 def fa_status_string(status: int) -> str:

@@ -396,6 +396,15 @@ int online_softmax_rows_split(const float* x, float* y, int rows, int cols, floa
   return FA_OK;
 }
 
+int fa_stream_copy(const void* x, void* y, size_t bytes, hipStream_t stream) {
+  if (!x || !y || bytes == 0 || bytes % 16 != 0) return FA_ERR_INVALID_ARG;
+  if (bytes >= ((uint64_t)1 << 62) || osm::stream_copy_blocks(bytes) > (uint64_t)INT_MAX)
+    return FA_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(y, 16)) return FA_ERR_ALIGNMENT;
+  if (overlaps(x, bytes, y, bytes)) return FA_ERR_INVALID_ARG;
+  return osm::launch_stream_copy(x, y, bytes, stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 const char* fa_status_string(int status) {
   switch (status) {
     case FA_OK: return "FA_OK: success";

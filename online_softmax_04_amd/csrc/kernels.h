@@ -71,4 +71,9 @@ void softmax_split_plan(int rows, int cols, int* chunk, int* nchunks);
 hipError_t launch_softmax_split(const float* x, float* y, int rows, int cols, bool vec_ok,
                                 float* workspace, hipStream_t stream);
 
+// Copy of `bytes` (a multiple of 16, 16-byte aligned) with non-temporal 16-byte
+// accesses; the grid size it uses.
+uint64_t stream_copy_blocks(uint64_t bytes);
+hipError_t launch_stream_copy(const void* x, void* y, size_t bytes, hipStream_t stream);
+
 }  // namespace osm

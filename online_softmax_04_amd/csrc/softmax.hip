@@ -25,6 +25,7 @@
 // keeps every CU fed, so no software grid-stride loop is needed).
 #include "common.h"
 #include "kernels.h"
+#include "mfma_tile.h"
 
 namespace osm {
 namespace {
@@ -116,6 +117,90 @@ __attribute__((amdgpu_waves_per_eu(THREADS >= 1024 ? 8 : 1, 8))) void softmax_ca
       const f32x4 v = c[i] * f;
       __builtin_nontemporal_store(v, yr + idx);
     }
+  }
+}
+
+// Persistent form of the register-cached kernel for many rows: one workgroup
+// per compute unit walks rows blockIdx.x, blockIdx.x + gridDim.x, ... with two
+// register caches, issuing the loads of its next row before it reduces,
+// normalises and stores the current one, so the memory system sees no gap
+// between the rows of a compute unit.  The arithmetic is softmax_cached's.
+template <int THREADS, int NV>
+__global__ __launch_bounds__(THREADS) void softmax_persist(const float* __restrict__ x,
+                                                           float* __restrict__ y, int rows,
+                                                           int cols) {
+  constexpr int W = THREADS / 64;
+  __shared__ float sm[2][W], sl[2][W];  // per-parity wave partials: rows r and r + 1 never share
+  const int nvec = cols >> 2;
+  const int t = threadIdx.x;
+  f32x4 a[NV], b[NV];
+  // Branch-free loads and stores through buffer descriptors bounded by the row
+  // (out-of-range lanes read zeros, replaced by -inf, and their stores are
+  // dropped), so the compiler can count the loads still in flight and wait
+  // only for the current row's, not for the prefetched one's.
+  auto load = [&](f32x4 (&c)[NV], int row) __attribute__((always_inline)) {
+    const auto r = make_rsrc(x + row * (size_t)cols, row < rows ? (int64_t)cols * 4 : 0);
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int idx = i * THREADS + t;
+      const f32x4 v = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, idx * 16, 0, 2));
+      c[i] = idx < nvec ? v : f32x4{kNegInf, kNegInf, kNegInf, kNegInf};
+    }
+    // keep the scheduler from sinking the loads towards their first use
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto process = [&](f32x4 (&c)[NV], int row, int par) __attribute__((always_inline)) {
+    float m = kNegInf;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) m = fmaxf(m, max4(c[i]));
+    const float m_lane = m;
+    const float ms = (m == kNegInf) ? 0.f : m;
+    float l = 0.f;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      c[i] = (c[i] - ms) * kLog2e;
+      c[i].x = exp2_fast(c[i].x);
+      c[i].y = exp2_fast(c[i].y);
+      c[i].z = exp2_fast(c[i].z);
+      c[i].w = exp2_fast(c[i].w);
+      l += (c[i].x + c[i].y) + (c[i].z + c[i].w);
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      const float mo = __shfl_xor(m, off);
+      const float lo = __shfl_xor(l, off);
+      merge_ml(m, l, mo, lo);
+    }
+    const int wave = t >> 6;
+    if ((t & 63) == 0) {
+      sm[par][wave] = m;
+      sl[par][wave] = l;
+    }
+    __syncthreads();
+    m = sm[par][0];
+    l = sl[par][0];
+#pragma unroll
+    for (int w = 1; w < W; ++w) merge_ml(m, l, sm[par][w], sl[par][w]);
+    const float f = exp2_fast((m_lane - m) * kLog2e) / l;
+    const auto ry = make_rsrc(y + row * (size_t)cols, row < rows ? (int64_t)nvec * 16 : 0);
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, c[i] * f), ry,
+                                             (i * THREADS + t) * 16, 0, 2);
+  };
+  // Rows are taken two at a time in one straight-line body: the loads of the
+  // next row sit in the same block as the work on the current one, where the
+  // compiler leaves them.  A row index past the end gets empty descriptors: its
+  // loads fetch nothing and its stores are dropped.
+  int row = blockIdx.x;
+  if (row >= rows) return;  // workgroup-uniform
+  load(a, row);
+  for (; row < rows; row += 2 * gridDim.x) {
+    const int n1 = row + gridDim.x;
+    load(b, n1);
+    process(a, row, 0);
+    load(a, n1 + gridDim.x);
+    process(b, n1, 1);
   }
 }
 
@@ -270,11 +355,34 @@ static void pick_softmax(int cols, bool vec_ok, const void** fn, int* threads) {
   *threads = 512;
 }
 
+// Compute units of the current device (looked up once per device).
+static int device_cus() {
+  static int cus[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
+      n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+
 hipError_t launch_softmax(const float* x, float* y, int rows, int cols, bool vec_ok,
                           hipStream_t stream) {
   const void* fn;
   int threads;
   pick_softmax(cols, vec_ok, &fn, &threads);
+  if (fn == (const void*)softmax_cached<1024, 8>) {
+    // many rows of 16385 .. 32768 columns: one persistent workgroup per compute unit
+    const int cus = device_cus();
+    if (rows >= 2 * cus) {
+      const void* pf = (const void*)softmax_persist<1024, 8>;
+      void* pargs[] = {(void*)&x, (void*)&y, (void*)&rows, (void*)&cols};
+      return hipLaunchKernel(pf, dim3(cus), dim3(1024), pargs, 0, stream);
+    }
+  }
   void* args[] = {(void*)&x, (void*)&y, (void*)&cols};
   return hipLaunchKernel(fn, dim3(rows), dim3(threads), args, 0, stream);
 }

@@ -32,7 +32,7 @@ def test_header_declares_the_entry_points():
               "fa_fwd_blocksparse", "fa_fwd_blocksparse_f16", "fa_bwd",
               "fa_bwd_f16", "fa_bwd_workspace_bytes",
               "fa_decode", "fa_decode_f16", "fa_decode_workspace_bytes", "fa_fwd_fp8",
-              "fa_decode_static",
+              "fa_decode_static", "fa_stream_copy",
               "online_softmax_rows", "online_softmax_rows_split",
               "online_softmax_split_workspace_bytes", "fa_status_string", "fa_kernel_attributes"):
         assert n in names
@@ -353,6 +353,16 @@ def call_fp8(q=A, k=A + 64 * MB, v=A + 128 * MB, o=A + 192 * MB, lse=A + 256 * M
 ])
 def test_fp8_validation(kw, status):
     assert call_fp8(**kw) == status
+
+
+@pytest.mark.parametrize("args,status", [
+    ((0, A + 64 * MB, 1024), fa.FA_ERR_INVALID_ARG), ((A, 0, 1024), fa.FA_ERR_INVALID_ARG),
+    ((A, A + 64 * MB, 0), fa.FA_ERR_INVALID_ARG), ((A, A + 64 * MB, 1000), fa.FA_ERR_INVALID_ARG),
+    ((A + 4, A + 64 * MB, 1024), fa.FA_ERR_ALIGNMENT), ((A, A + 64 * MB + 8, 1024), fa.FA_ERR_ALIGNMENT),
+    ((A, A + 512, 1024), fa.FA_ERR_INVALID_ARG),            # overlapping
+])
+def test_stream_copy_validation(args, status):
+    assert fa.lib().fa_stream_copy(*args, None) == status
 
 
 def test_python_wrappers_raise():

@@ -93,12 +93,45 @@ def test_special_rows(orc, cols):
     assert got[1, cols // 2] == 1.0
 
 
+@pytest.mark.parametrize("rows,cols", [(512, 32768), (513, 32768), (777, 20004), (1000, 16388),
+                                       (4096 + 37, 24000)])
+def test_persistent_rows(orc, rows, cols):
+    """Many rows of 16385-32768 columns run one persistent workgroup per compute unit,
+    two rows in flight each; row counts that are not a multiple of twice the grid
+    leave some workgroups a padded last step (empty descriptors: nothing read or
+    written).  Every row is checked, and the output buffer past the rows is untouched."""
+    say(f"[softmax persistent] rows={rows} cols={cols}")
+    x = workloads.random_rows(rows, cols, seed=rows + cols, std=3.0, spike_prob=0.01)
+    xd = torch.from_numpy(x).cuda()
+    yb = torch.full((rows * cols + 1024,), 7.0, dtype=torch.float32, device="cuda")
+    fa.online_softmax_rows(xd, yb[: rows * cols], rows, cols)
+    torch.cuda.synchronize()
+    got, ref = to_f64(yb[: rows * cols].view(rows, cols)), orc.softmax_rows(x)
+    gate(f"persistent {rows}x{cols}", got, ref, "f32")
+    softmax_rel_gate(f"persistent {rows}x{cols}", got, ref, x)
+    assert torch.all(yb[rows * cols:] == 7.0)
+
+
 def test_many_rows_small_cols(orc):
     x = workloads.random_rows(70000, 33, seed=3)
     say("[softmax many rows]")
     got, ref = to_f64(run_gpu(x)), orc.softmax_rows(x)
     gate("70000x33", got, ref, "f32")
     softmax_rel_gate("70000x33", got, ref, x)
+
+
+@pytest.mark.parametrize("nbytes", [16, 1024, 16384 + 16, 3 * 16384 - 48, 100 << 20])
+def test_stream_copy_is_exact(nbytes):
+    """fa_stream_copy (the benchmark's HBM ceiling) copies every byte, including a
+    ragged last 16 KiB chunk, and nothing past the end."""
+    say(f"[stream copy] {nbytes} bytes")
+    g = torch.Generator(device="cuda").manual_seed(nbytes)
+    x = torch.randint(0, 256, (nbytes,), dtype=torch.uint8, device="cuda", generator=g)
+    y = torch.zeros(nbytes + 64, dtype=torch.uint8, device="cuda")
+    fa.fa_stream_copy(x, y, nbytes)
+    torch.cuda.synchronize()
+    assert torch.equal(x, y[:nbytes])
+    assert not y[nbytes:].any()
 
 
 def test_wrapper():
