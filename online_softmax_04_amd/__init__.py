@@ -24,7 +24,10 @@ __all__ = [
     "FA_OK", "FA_ERR_INVALID_ARG", "FA_ERR_UNSUPPORTED", "FA_ERR_ALIGNMENT", "FA_ERR_HIP",
 ]
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
+# ONLINE_SOFTMAX_04_AMD_LIB names another build of the same library (for example one
+# whose host code carries sanitizers); by default the in-tree libfa.so.
+LIB_PATH = (os.environ.get("ONLINE_SOFTMAX_04_AMD_LIB")
+            or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so"))
 
 FA_OK = 0
 FA_ERR_INVALID_ARG = -1

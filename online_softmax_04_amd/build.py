@@ -52,5 +52,19 @@ def build(verbose: bool = False) -> str:
     return OUT
 
 
+PROBE_SRC = os.path.join(ROOT, "tests", "probes", "layout_probe.hip")
+PROBE_OUT = os.path.join(ROOT, "tests", "probes", "liblayout_probe.so")
+
+
+def build_probes() -> str:
+    """The single-wave instruction probes the GPU tests load (tests/probes)."""
+    tmp = PROBE_OUT + ".tmp"
+    r = subprocess.run([HIPCC, *FLAGS, "-shared", PROBE_SRC, "-o", tmp], capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("hipcc failed on layout_probe.hip:\n" + r.stderr[-3000:])
+    os.replace(tmp, PROBE_OUT)
+    return PROBE_OUT
+
+
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))

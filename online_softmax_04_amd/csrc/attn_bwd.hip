@@ -325,8 +325,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dkdv(
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hf = lane >> 5;
   const int wave_s = __builtin_amdgcn_readfirstlane(wave);
-  const int kg = wave & 3;   // 32-key group of this wave
-  const int qh = wave >> 2;  // which 32 queries of each tile
+  // wave-uniform indices in scalar registers: the accumulators leave few vector ones
+  const int kg = wave_s & 3;   // 32-key group of this wave
+  const int qh = wave_s >> 2;  // which 32 queries of each tile
   int bh, kbk;
   block_of(BH, n_kblocks, xcd_groups, false, &bh, &kbk);
   const int k0 = kbk * kKB;

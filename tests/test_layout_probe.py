@@ -1,0 +1,188 @@
+"""The instruction behaviour the attention kernels are built on, pinned on the GPU
+with single-wave probes (tests/probes/layout_probe.hip) and index-encoded or
+exactly representable inputs:
+
+* the 32x32x16 bf16 MFMA: lane l holds row (A) / column (B) l % 32 and the 8
+  consecutive k from 8 (l / 32); accumulator register r of lane l is element
+  (8 (r / 4) + 4 (l / 32) + r % 4, l % 32) -- one output column per lane, the
+  layout that lets the softmax take a query's row maximum inside one lane plus
+  one exchange with lane l ^ 32 ("Online softmax, and the register that can't
+  move", section "Why the output must live in registers");
+* v_permlane32_swap with both operands equal: half 0 of the result holds lanes
+  0..31 of the input in both halves of the wave, half 1 lanes 32..63, so each lane
+  sees its own value and that of lane l ^ 32;
+* ds_read_b64_tr_b16 with the V^T read addresses of the forward kernel: within
+  each group of 16 lanes, the lane at position q supplies the address of row
+  R + q / 4, columns C + 4 (q % 4) .. + 3, and receives the column C + q of rows
+  R .. R + 3;
+* the 32x32x64 fp8 MFMA: the same one-row-per-lane layout with 32 consecutive k
+  per lane half, and its summation -- products in groups of 8 consecutive k, each
+  truncated toward zero to 2^(E - 13) with E the group's largest exponent sum (the
+  rule the fp8 kernel's emulation in test_parity_fp8 follows).  The eight group
+  sums are then added in fp32 in an order the probes do not pin down: the result
+  lies within 8 2^-24 of the sum of their magnitudes (measured: at most 1.8) and
+  is bit-equal to the exact sum of the truncated products rounded once in ~95% of
+  cases; the exact sum of the untruncated products is off by hundreds of those
+  units once products span the whole E4M3 range.  With the magnitudes of scaled
+  attention inputs (products within 8 binades) nothing is truncated and every
+  result is the exact sum rounded once;
+* v_cvt_pk_fp8_f32: round to nearest even into OCP E4M3.
+"""
+import ctypes
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from test_parity_fp8 import e4m3_exponent, mfma_fp8_dot
+
+pytestmark = pytest.mark.gpu
+
+LIB = os.path.join(os.path.dirname(os.path.abspath(__file__)), "probes", "liblayout_probe.so")
+
+
+@pytest.fixture(scope="module")
+def probe():
+    if not os.path.exists(LIB):
+        raise ImportError(f"{LIB} is missing: build it with __graft_entry__.build()")
+    L = ctypes.CDLL(LIB)
+    for name, n in (("mfma_bf16_probe", 3), ("permlane32_probe", 2), ("ds_read_tr16_probe", 3),
+                    ("mfma_fp8_probe", 3), ("cvt_fp8_probe", 2)):
+        getattr(L, name).argtypes = [ctypes.c_void_p] * n
+        getattr(L, name).restype = ctypes.c_int
+    return L
+
+
+# bytes each probe reads or writes per buffer (the fixed sizes of layout_probe.hip)
+SIZES = {"mfma_bf16_probe": (32 * 16 * 2, 16 * 32 * 2, 64 * 16 * 4),
+         "permlane32_probe": (64 * 4, 2 * 64 * 4),
+         "ds_read_tr16_probe": (64 * 64 * 2, 64 * 4, 64 * 4 * 2),
+         "mfma_fp8_probe": (32 * 64, 64 * 32, 64 * 16 * 4),
+         "cvt_fp8_probe": (64 * 4 * 4, 64 * 4)}
+
+
+def run(probe, name, *bufs):
+    """Launch probe `name` on device tensors whose sizes match what it touches."""
+    for b, need in zip(bufs, SIZES[name], strict=True):
+        assert b.is_cuda and b.is_contiguous() and b.numel() * b.element_size() == need, name
+    assert getattr(probe, name)(*(b.data_ptr() for b in bufs)) == 0
+    torch.cuda.synchronize()
+
+
+def acc_index(l, r):
+    """(row, column) of accumulator register r of lane l in the 32x32 layout."""
+    return 8 * (r // 4) + 4 * (l // 32) + r % 4, l % 32
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_mfma_32x32x16_layout(probe, seed):
+    rng = np.random.default_rng([61, seed])
+    A = rng.integers(-8, 9, (32, 16)).astype(np.float32)  # small integers: exact in bf16 and fp32
+    B = rng.integers(-8, 9, (16, 32)).astype(np.float32)
+    D = A @ B
+    a = torch.from_numpy(workloads.f32_to_bf16_bits(A).view(np.int16)).cuda()
+    b = torch.from_numpy(workloads.f32_to_bf16_bits(B).view(np.int16)).cuda()
+    out = torch.empty((64, 16), dtype=torch.float32, device="cuda")
+    run(probe, "mfma_bf16_probe", a, b, out)
+    got = out.cpu().numpy()
+    for l in range(64):
+        for r in range(16):
+            i, j = acc_index(l, r)
+            assert got[l, r] == D[i, j], f"lane {l} register {r}: {got[l, r]} != D[{i}, {j}] = {D[i, j]}"
+
+
+def test_permlane32_swap(probe):
+    x = torch.arange(1000, 1064, dtype=torch.int32, device="cuda")
+    out = torch.empty(128, dtype=torch.int32, device="cuda")
+    run(probe, "permlane32_probe", x, out)
+    got = out.cpu().numpy().reshape(2, 64)
+    lanes = np.arange(64)
+    assert np.array_equal(got[0], 1000 + lanes % 32)
+    assert np.array_equal(got[1], 1000 + 32 + lanes % 32)
+    # so max / sum of the two halves give every lane its value and lane l ^ 32's
+    assert np.array_equal(np.maximum(got[0], got[1]), np.maximum(1000 + lanes, 1000 + (lanes ^ 32)))
+
+
+@pytest.mark.parametrize("row0,col0", [(0, 0), (12, 0), (40, 32), (4, 16)])
+def test_ds_read_tr16_order(probe, row0, col0):
+    """The forward kernel's V^T read addresses, at a few base rows and columns."""
+    lds = (np.arange(64)[:, None] * 64 + np.arange(64)[None, :]).astype(np.uint16)
+    addr = np.empty(64, np.int32)
+    for l in range(64):
+        q, hf = l & 15, l >> 5
+        row = row0 + 4 * hf + (q >> 2)
+        col = col0 + 16 * ((l >> 4) & 1) + 4 * (q & 3)
+        addr[l] = (row * 64 + col) * 2
+    out = torch.empty((64, 4), dtype=torch.int16, device="cuda")
+    run(probe, "ds_read_tr16_probe", torch.from_numpy(lds.view(np.int16)).cuda(),
+        torch.from_numpy(addr).cuda(), out)
+    got = out.cpu().numpy().view(np.uint16)
+    for l in range(64):
+        q, hf = l & 15, l >> 5
+        R, C = row0 + 4 * hf, col0 + 16 * ((l >> 4) & 1)
+        want = [lds[R + k, C + q] for k in range(4)]
+        assert list(got[l]) == want, f"lane {l}: {list(got[l])} != {want}"
+
+
+def fp8_codes(rng, shape, wide):
+    """E4M3 codes without NaN: the whole range (subnormals to 448) or the range of
+    scaled attention inputs (magnitudes 2^4 .. 2^7.9)."""
+    mag = rng.integers(0, 0x7F, shape) if wide else rng.integers(0x58, 0x70, shape)
+    return (mag | (rng.integers(0, 2, shape) << 7)).astype(np.uint8)
+
+
+@pytest.mark.parametrize("seed,wide", [(0, True), (1, True), (2, True), (3, False), (4, False)])
+def test_mfma_fp8_layout_and_summation(probe, seed, wide):
+    from oracle import Oracle
+    rng = np.random.default_rng([62, seed])
+    A8, B8 = fp8_codes(rng, (32, 64), wide), fp8_codes(rng, (64, 32), wide)
+    A, B = Oracle.to_f64(A8, "fp8"), Oracle.to_f64(B8, "fp8")
+    ea, eb = e4m3_exponent(A8), e4m3_exponent(B8)
+    # the model: row i of A against column j of B, groups of 8 consecutive k
+    model = mfma_fp8_dot(A[:, None, :], ea[:, None, :], B.T[None, :, :], eb.T[None, :, :])
+    # magnitudes of the group sums (the fp32 rounding budget of adding them)
+    prod = (A[:, None, :] * B.T[None, :, :]).reshape(32, 32, 8, 8)
+    gmag = np.zeros((32, 32))
+    for g in range(8):
+        sl = slice(8 * g, 8 * g + 8)
+        gmag += np.abs(mfma_fp8_dot(A[:, None, sl], ea[:, None, sl], B.T[None, :, sl], eb.T[None, :, sl]))
+    exact = prod.sum(axis=(2, 3))
+    out = torch.empty((64, 16), dtype=torch.float32, device="cuda")
+    run(probe, "mfma_fp8_probe", torch.from_numpy(A8).cuda(), torch.from_numpy(B8).cuda(), out)
+    raw = out.cpu().numpy()
+    got = np.empty((32, 32))
+    for l in range(64):
+        for r in range(16):
+            i, j = acc_index(l, r)
+            got[i, j] = raw[l, r]
+    unit = 2.0 ** -24 * gmag + 1e-300
+    err_model = np.abs(got - model) / unit
+    err_exact = np.abs(got - exact) / unit
+    equal = float(np.mean(got == model.astype(np.float32)))
+    print(f"fp8 seed {seed} wide={wide}: model within {err_model.max():.2f} units (bit-equal {equal:.1%}); "
+          f"exact sum median {np.median(err_exact):.1f} units")
+    i, j = np.unravel_index(int(np.argmax(err_model)), err_model.shape)
+    assert err_model.max() <= 8, f"D[{i},{j}]: {got[i, j]!r} vs model {model[i, j]!r}"
+    if wide:
+        assert equal >= 0.9 and np.median(err_exact) > 100  # the truncation is real and modelled
+    else:
+        assert equal == 1.0 and np.all(got == exact.astype(np.float32))
+
+
+def test_cvt_pk_fp8_rounds_to_nearest_even(probe):
+    pos = np.sort(workloads._e4m3_table())
+    mids = (pos[:-1] + pos[1:]) / 2                     # ties: to the even code
+    rng = np.random.default_rng(63)
+    vals = np.concatenate([mids[:60], pos[:40], rng.uniform(0, 448, 60), -mids[60:80], -rng.uniform(0, 8, 76)])
+    assert vals.size == 256
+    x = vals.astype(np.float32)
+    # the midpoints of E4M3 neighbours have at most 5 significant bits: exact in fp32
+    assert np.all(x[:60].astype(np.float64) == mids[:60]) and np.all(np.abs(x) <= 448)
+    out = torch.empty(256, dtype=torch.uint8, device="cuda")
+    run(probe, "cvt_fp8_probe", torch.from_numpy(x).cuda(), out)
+    got = out.cpu().numpy()
+    want = workloads.f32_to_e4m3(x)
+    bad = np.nonzero(got != want)[0]
+    assert bad.size == 0, f"{bad.size} codes differ, first at {x[bad[0]]!r}: {got[bad[0]]:#x} != {want[bad[0]]:#x}"
