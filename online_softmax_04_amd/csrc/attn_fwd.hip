@@ -13,8 +13,10 @@
 // factor is exactly 0 ("Day 97", Solution).  Exponentials run in base 2 with
 // c = scale * log2(e) folded into one FMA per score, so m is kept in units of
 // c * score; the logsumexp written out is ln 2 * (m + log2 l).  The row sum
-// in l is taken over P after its rounding to 16 bits, the same values that
-// multiply V.
+// in l runs on the matrix unit over P after its rounding to 16 bits, the same
+// values that multiply V: O / l then weights V by exactly the rounded P
+// normalised to 1, and a rounding error d of one weight moves O by
+// d p (v - O) / l, not by d p v / l.
 //
 // The m carried here is a reference point that trails the running maximum by
 // at most kSlack = 8 (a factor 2^8): it moves to the new maximum only when
@@ -53,8 +55,9 @@
 // loads that write LDS directly (no register staging), 16 bytes per lane.  The
 // buffer base is advanced by whole tiles on the scalar unit, so a load needs no
 // vector address arithmetic, and rows past N fall outside the buffer's range
-// and read as zero (their scores are masked).  K and V have separate double
-// buffers.  Both are stored row-major with 16-byte chunks XOR-swizzled by row
+// and read as zero (their scores are masked).  Half the waves issue the loads,
+// spread between their MFMAs (slot schedule in the kernel).  K and V have
+// separate double buffers.  Both are stored row-major with 16-byte chunks XOR-swizzled by row
 // so that the MFMA operand reads spread over the LDS banks; V^T operands are
 // read with the transposing ds_read_b64_tr_b16.
 //
@@ -68,23 +71,10 @@
 #include "kernels.h"
 #include "mfma_tile.h"
 
+#include <type_traits>
+
 namespace osm {
 namespace {
-
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-// acc + x.lo + x.hi for a word holding two 16-bit values (one dot2 instruction)
-template <typename T>
-__device__ __forceinline__ float add_pair(unsigned x, float acc);
-template <>
-__device__ __forceinline__ float add_pair<__bf16>(unsigned x, float acc) {
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x), __builtin_bit_cast(bf16x2, 0x3f803f80u), acc, false);
-}
-template <>
-__device__ __forceinline__ float add_pair<_Float16>(unsigned x, float acc) {
-  return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, x), __builtin_bit_cast(f16x2, 0x3c003c00u), acc, false);
-}
-
 
 // two 16-bit ones in one word
 template <typename T>
@@ -93,7 +83,7 @@ constexpr unsigned kOnePair = sizeof(T) == 2 && __is_same(T, __bf16) ? 0x3f803f8
 constexpr float kSlack = 8.f;  // how far (log2 units) the running maximum may pass m
 constexpr int kBM = 256;       // queries per workgroup
 // keys per tile: 128 at d = 64, where the per-tile fixed costs weigh most and the
-// registers allow it (208 VGPRs); 64 at d = 128 (198 VGPRs, 128 would need 250+)
+// registers allow it (222 VGPRs); 64 at d = 128 (217 VGPRs, 128 would need 250+)
 template <int D>
 constexpr int kBN = D == 64 ? 128 : 64;
 constexpr int kThreads = 512;  // 8 waves: two groups of 4, one wave of each group per SIMD
@@ -117,11 +107,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(
   constexpr int NH = BN / 32;                  // 32-key blocks of a tile
   constexpr int CPR = D / 8;                   // 16-byte chunks per row
   constexpr int RPI = 1024 / ROW_BYTES;        // rows per 1 KiB wave-wide load
-  // At d = 64 the softmax of a 128-key tile takes longer than the tile's products,
-  // so the wave running the products has room to issue the tile loads too: only
-  // group 0 loads, in slot Y where it runs the products (as in the fp8 kernel).
-  // At d = 128 the two roles are balanced and every wave loads its share.
-  constexpr bool LG = D == 64;
+  // Only group 0 loads, in slot Y where it runs the products, with its loads
+  // spread between the MFMAs.  A wave-wide load occupies the texture unit for
+  // several cycles, and a wave that issues one while the unit is busy stalls:
+  // eight waves each issuing their loads at the top of a slot held the softmax
+  // waves up for hundreds of cycles.
+  constexpr bool LG = true;
   constexpr int NI = TILE_BYTES / 1024 / (LG ? 4 : 8);  // such loads per loading wave per tile
   static_assert(NI >= 1, "tile shape");
   // One array per stage and operand, always named at compile time: the compiler
@@ -185,15 +176,17 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(
 #pragma unroll
   for (int db = 0; db < ND; ++db) o[db] = f32x16{};
   f32x16 s[NH];
-  // At d = 64 the softmax wave is the longer one, so the row sum of P runs on the
-  // matrix unit: with a block of ones as the A operand, every row of the
-  // accumulator receives the sum over the step's keys of each query's P.
-  constexpr bool RS = D == 64;
+  // The row sum of P runs on the matrix unit: with a block of ones as the A
+  // operand, every row of the accumulator receives the sum over the step's keys
+  // of each query's P.  One more MFMA per 16-key step; on the vector ALU the sum
+  // of the 16-bit P takes two-term dot products, which wait for the matrix unit
+  // while the other wave of the SIMD keeps it busy (measured slower at both
+  // head dims).
   f32x16 lacc = f32x16{};
   const v8 ones = __builtin_bit_cast(
       v8, u32x4{kOnePair<T>, kOnePair<T>, kOnePair<T>, kOnePair<T>});
   v8 pf[NH][2];  // P^T as 16-bit B operands: [32-key block][16-key step]
-  float m_run = kNegInf, l_run = 0.f;
+  float m_run = kNegInf;
 
   const int nk_all = (N + BN - 1) / BN;
   const int n_kt = CAUSAL ? min(nk_all, (i0 + kBM - 1) / BN + 1) : nk_all;
@@ -282,14 +275,16 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(
     kgoff[j] = row * ROW_BYTES + (p ^ kswz<D>(row)) * 16;
     vgoff[j] = row * ROW_BYTES + (p ^ vswz<D>(row)) * 16;
   }
-  auto load_k = [&](int t, auto st) __attribute__((always_inline)) {
-    const auto r = make_rsrc(Kh + (size_t)t * BN * D, (int64_t)(N - t * BN) * ROW_BYTES);
+  // valid = false gives an empty buffer: the loads then read nothing and write
+  // zeros into the stage
+  auto load_k = [&](int t, auto st, bool valid = true) __attribute__((always_inline)) {
+    const auto r = make_rsrc(Kh + (size_t)t * BN * D, valid ? (int64_t)(N - t * BN) * ROW_BYTES : 0);
 #pragma unroll
     for (int j = 0; j < NI; ++j)
       load16_to_lds(r, kbuf(st) + ((LG ? wave_s & 3 : wave_s) * NI + j) * 1024, kgoff[j]);
   };
-  auto load_v = [&](int t, auto st) __attribute__((always_inline)) {
-    const auto r = make_rsrc(Vh + (size_t)t * BN * D, (int64_t)(N - t * BN) * ROW_BYTES);
+  auto load_v = [&](int t, auto st, bool valid = true) __attribute__((always_inline)) {
+    const auto r = make_rsrc(Vh + (size_t)t * BN * D, valid ? (int64_t)(N - t * BN) * ROW_BYTES : 0);
 #pragma unroll
     for (int j = 0; j < NI; ++j)
       load16_to_lds(r, vbuf(st) + ((LG ? wave_s & 3 : wave_s) * NI + j) * 1024, vgoff[j]);
@@ -366,26 +361,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(
 #pragma unroll
       for (int r = 0; r < 16; ++r) pf[kh][r >> 3][r & 7] = (T)exp2_fast(fmaf(s[kh][r], c, -m_sub));
     }
-    // l sums the 16-bit P that the PV product consumes, so O / l weights V
-    // by exactly the rounded P normalised to 1: a rounding error d of one weight
-    // then moves O by d p (v - O) / l, not by d p v / l.
-    if constexpr (!RS) {
-      float ls[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kh = 0; kh < NH; ++kh)
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const u32x4 w = __builtin_bit_cast(u32x4, pf[kh][kb]);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) ls[e] = add_pair<T>(w[e], ls[e]);
-        }
-      l_run = fmaf(l_run, alpha, (ls[0] + ls[1]) + (ls[2] + ls[3]));
-    }
     m_run = m_new;
     if (__any(alpha != 1.f)) {  // wave-uniform; skipped while no row's reference moves
 #pragma unroll
       for (int db = 0; db < ND; ++db) o[db] *= alpha;
-      if constexpr (RS) lacc *= alpha;
+      lacc *= alpha;
     }
   };
   // PV: O^T += V^T P^T, from V stage st.
@@ -403,31 +383,38 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(
           const v8 vf = __builtin_bit_cast(v8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
           o[db] = Mma<T>::run(vf, pf[kh][kb], o[db]);
         }
-        if constexpr (RS) lacc = Mma<T>::run(ones, pf[kh][kb], lacc);
+        lacc = Mma<T>::run(ones, pf[kh][kb], lacc);
       }
     }
   };
 
   // PV(tp) then QK(tq) in one block, with the LDS operand reads running a fixed
   // distance ahead of the MFMAs that consume them: enough reads in flight to
-  // cover LDS latency, few enough registers to avoid spilling.
-  auto pv_qk = [&](auto stp, auto stq) __attribute__((always_inline)) {
+  // cover LDS latency, few enough registers to avoid spilling.  nld (a
+  // compile-time count) direct loads issued by loads() are spread evenly
+  // between the MFMAs.
+  auto pv_qk = [&](auto stp, auto stq, auto nld, auto&& loads) __attribute__((always_inline)) {
+    constexpr int NL = decltype(nld)::value;
+    loads();
     pv(stp);
     qk(stq);
     // PV MFMAs take two transposed reads each, QK MFMAs one read
     constexpr int kAhead = 4;               // MFMAs whose operands are read ahead
-    // (the row-sum MFMA that ends each 16-key step when RS reads nothing)
-    constexpr int kStep = ND + (RS ? 1 : 0);  // PV MFMAs per 16-key step
+    // (the row-sum MFMA that ends each 16-key step reads nothing)
+    constexpr int kStep = ND + 1;  // PV MFMAs per 16-key step
     constexpr int kPv = 2 * NH * kStep, kQk = NH * NK;
 #pragma unroll
     for (int j = 0; j < kAhead; ++j)
-      if (!(RS && j % kStep == ND)) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS reads
+      if (j % kStep != ND) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS reads
+    constexpr int kEvery = NL ? (kPv + kQk) / (NL + 1) : 1;
 #pragma unroll
     for (int i = 0; i < kPv + kQk; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+      if (NL && i % kEvery == kEvery - 1 && i / kEvery < NL)
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one direct load
       const int j = i + kAhead;                           // operand reads for MFMA j
       if (j < kPv) {
-        if (!(RS && j % kStep == ND)) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        if (j % kStep != ND) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       } else if (j < kPv + kQk) {
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
@@ -447,7 +434,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(
       __builtin_amdgcn_s_setprio(1);
       const bool a_prev = i > 0 && act_at(i - 1);
       if (a_prev && a_cur) {
-        pv_qk(other, cur);
+        pv_qk(other, cur, std::integral_constant<int, 0>{}, [] {});
       } else {
         if (a_prev) pv(other);
         if (a_cur) qk(cur);
@@ -457,16 +444,23 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(
     loads_landed();  // K of position i + 1, V of position i
     __syncthreads();
     // ---- slot Y
-    if (!LG || group == 0) {
-      if (i + 2 < n_list) load_k(tile_of(i + 2), cur);
-      if (i + 1 < n_list) load_v(tile_of(i + 1), other);
-    }
     if (group == 0) {
       __builtin_amdgcn_s_setprio(1);
       const bool a_next = i + 1 < n_list && act_at(i + 1);
+      // K(i + 2) into the stage K(i) leaves, V(i + 1) into the one V(i - 1) left;
+      // past the end of the list the loads are empty, and the zeros they write
+      // land in stages that no later read uses.  Unconditional loads keep the
+      // block straight, so the schedule can spread them.
+      const bool k_ok = i + 2 < n_list, v_ok = i + 1 < n_list;
+      const int tk = k_ok ? tile_of(i + 2) : 0, tv = v_ok ? tile_of(i + 1) : 0;
+      auto loads = [&]() __attribute__((always_inline)) {
+        load_k(tk, cur, k_ok);
+        load_v(tv, other, v_ok);
+      };
       if (a_cur && a_next) {
-        pv_qk(cur, other);
+        pv_qk(cur, other, std::integral_constant<int, 2 * NI>{}, loads);
       } else {
+        loads();
         if (a_cur) pv(cur);
         if (a_next) qk(other);
       }
@@ -481,10 +475,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(
   //   slot X(t): group 0 runs SM(t)          group 1 runs PV(t-1), QK(t)
   //   slot Y(t): group 0 runs PV(t), QK(t+1) group 1 runs SM(t)
   // so on every SIMD one wave keeps the matrix unit busy while the other runs
-  // the vector-ALU softmax.  K(t+1) and V(t) are read from Y(t) to X(t+1); they
-  // are loaded into LDS during Y(t-1) and X(t) (into the stages of K(t-1) and
-  // V(t-1), last read in X(t-1)) and published by the workgroup barrier that
-  // ends X(t).  That barrier is the only one per tile: no LDS stage changes
+  // the vector-ALU softmax.  K(t+1) and V(t) are read from Y(t) to X(t+1); group
+  // 0 issues their loads between its MFMAs in Y(t-1) (into the stages of K(t-1)
+  // and V(t-1), last read in X(t-1)), they land during Y(t-1) and X(t), and the
+  // workgroup barrier that ends X(t) publishes them.  That barrier is the only one per tile: no LDS stage changes
   // hands between Y(t) and X(t+1), and meeting once per tile keeps the two
   // groups in opposite phases.  The dense kernel starts at tile t0 = 0; the
   // LOCAL one at the workgroup's first visible tile, each wave computing from
@@ -517,7 +511,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(
   }
 
   // ---- epilogue: O / l, logsumexp --------------------------------------------------
-  const float l_tot = RS ? lacc[0] : sum_halves(l_run);
+  const float l_tot = lacc[0];
   // a block-sparse row can see no key at all: O = 0 and logsumexp -inf there
   const float inv = (SPARSE && l_tot == 0.f) ? 0.f : 1.f / l_tot;
   {
