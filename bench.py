@@ -26,7 +26,9 @@ Prints ONE JSON line:
   causal shape (TFLOP/s against the dense fp8 peak), and the two head-dim-64
   workloads (one head of 4096 keys, one causal head of 131072).  Beside the
   softmax: a hand-written non-temporal 16-byte device copy of 512 MiB
-  (fa_stream_copy), the practical HBM ceiling, timed in the same run.
+  (fa_stream_copy), the practical HBM ceiling, timed in the same run.  Beside
+  the attention: a stream of bf16 MFMAs on N(0,1) operands (fa_mfma_stream),
+  the rate the matrix units hold on such data with nothing else running.
 
 Other modes:
   --ingest-counters DIR_FETCH DIR_WRITE   turn two rocprofv3 --pmc runs
@@ -59,6 +61,9 @@ PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBPS = 8000.0         # MI355X HBM3E, published
 PEAK_FP8_TFLOPS = 5000.0       # MI355X dense fp8 MFMA, published
 COPY_BYTES = 512 << 20         # probe copy (fa_stream_copy): 512 MiB read + 512 MiB written
+MFMA_STREAM_BLOCKS = 2048      # matrix-unit probe (fa_mfma_stream): 8 workgroups per CU,
+MFMA_STREAM_ITERS = 512        # 4096 MFMAs per wave, ~1 ms per launch
+MFMA_STREAM_SEED = 97100
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", f"traffic_{ATTN_WORKLOAD}+{SOFTMAX_WORKLOAD}.md")
 _SHARED = ["online_softmax_04_amd/csrc/common.h", "online_softmax_04_amd/csrc/mfma_tile.h",
            "online_softmax_04_amd/csrc/kernels.h"]
@@ -70,7 +75,7 @@ KERNEL_SOURCES = {
 # name parts that pick each kernel out of a profile of this script (the attention entry is
 # the mangled dense causal bf16 d=128 instance, not the sliding-window one); the probe
 # copy is fa_stream_copy (reads and writes COPY_BYTES)
-KERNEL_NAME_PART = {"attn": "attn_fwd_mfmaIDF16bLi128ELb1ELi0E", "softmax": "softmax_cached",
+KERNEL_NAME_PART = {"attn": "attn_fwd_mfmaIDF16bLi128ELb1ELi0E", "softmax": "softmax_persist",
                     "copy": "stream_copy"}
 
 
@@ -184,11 +189,12 @@ MFMA_PASS_B = ("SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT SQ
 
 
 def kernel_mfma_count(w) -> int:
-    """32x32x16 MFMAs one attn_fwd_mfma launch issues on workload w: every wave runs QK and
-    PV (D/16 + D/16 MFMAs per 32-key block, two blocks per 64-key tile) on each key tile up
-    to the last one holding a key visible to one of its 32 queries."""
+    """32x32x16 MFMAs one attn_fwd_mfma launch issues on workload w (d = 128): every wave
+    runs QK and PV (D/16 + D/16 MFMAs per 32-key block, two blocks per 64-key tile) and the
+    row sum (one MFMA per 16 keys) on each key tile up to the last one holding a key
+    visible to one of its 32 queries."""
     bm, bn = 256, 64
-    per_tile = 2 * (w.d // 16) * 2
+    per_tile = 2 * (w.d // 16) * 2 + bn // 16
     n_mt = -(-w.N // bm)
     nk_all = -(-w.N // bn)
     total = 0
@@ -525,6 +531,23 @@ def main():
     torch.cuda.synchronize()
     copy_each = sorted(e[0].elapsed_time(e[1]) for e in cev)
     copy_ms = sum(copy_each) / len(copy_each)
+    # matrix-unit probe: bf16 MFMAs on N(0,1) operands (drawn like the attention inputs),
+    # the rate a dense contraction can hold on this data when nothing else runs
+    g = torch.Generator(device=dev).manual_seed(MFMA_STREAM_SEED)
+    mops = torch.randn(fa.MFMA_STREAM_OPERAND_BYTES // 2, device=dev, generator=g).to(torch.bfloat16)
+    mout = torch.empty(MFMA_STREAM_BLOCKS * 512, dtype=torch.float32, device=dev)
+    for _ in range(2):
+        fa.fa_mfma_stream(mops, mout, MFMA_STREAM_BLOCKS, MFMA_STREAM_ITERS, stream)
+    mev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(5)]
+    for e in mev:
+        e[0].record(stream)
+        fa.fa_mfma_stream(mops, mout, MFMA_STREAM_BLOCKS, MFMA_STREAM_ITERS, stream)
+        e[1].record(stream)
+    torch.cuda.synchronize()
+    mfma_ms = sum(e[0].elapsed_time(e[1]) for e in mev) / len(mev)
+    mfma_ceiling = MFMA_STREAM_BLOCKS * 8 * MFMA_STREAM_ITERS * 8 * 32768 / (mfma_ms * 1e-3) / 1e12
+    print(f"[bench] matrix-unit probe {mfma_ceiling:.1f} TFLOP/s on N(0,1) bf16 operands", file=sys.stderr,
+          flush=True)
 
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     torch.cuda.synchronize()
@@ -760,12 +783,17 @@ def main():
                      "traffic": attn_traffic, "kernel": "attn_fwd_mfma<bf16,128,causal>",
                      "flop_per_launch": w.flops, "avg_launch_ms": round(attn_ms, 5),
                      "median_launch_ms": round(attn_each[len(attn_each) // 2], 5),
-                     "min_launch_ms": round(attn_each[0], 5)},
+                     "min_launch_ms": round(attn_each[0], 5),
+                     "mfma_ceiling_tflops": round(mfma_ceiling, 1),
+                     "mfma_ceiling_kernel": "mfma_stream (fa_mfma_stream: 32x32x16 bf16 MFMAs from "
+                                            "registers, N(0,1) operands, 2 waves per SIMD, "
+                                            f"{MFMA_STREAM_BLOCKS} workgroups)",
+                     "frac_of_mfma_ceiling": round(tflops / mfma_ceiling, 4)},
         "softmax": {"value": round(sm_gbps, 1), "unit": "GB/s",
                     "roofline": {"bound": "hbm", "achieved": round(sm_gbps, 1),
                                  "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                                  "frac": round(sm_gbps / PEAK_HBM_GBPS, 4), "traffic": sm_traffic,
-                                 "kernel": "softmax_cached<1024,8>",
+                                 "kernel": "softmax_persist<1024,8>",
                                  "bytes_per_launch": sm_bytes, "avg_launch_us": round(sm_ms * 1e3, 2),
                                  "median_launch_us": round(sm_each[len(sm_each) // 2] * 1e3, 2),
                                  "min_launch_us": round(sm_each[0] * 1e3, 2)},

@@ -315,6 +315,28 @@ int online_softmax_rows_split(const float* x, float* y, int rows, int cols, floa
  */
 int fa_stream_copy(const void* x, void* y, size_t bytes, hipStream_t stream);
 
+/*
+ * Measurement utility: a stream of 32x32x16 bf16 matrix-unit products with
+ * operands held in registers, the ceiling of a dense contraction on this part
+ * for the given operand data (the attention forward is one: "Online Softmax:
+ * Tiling Across a Reduction", the matrix-unit paragraphs).  The matrix units'
+ * power draw depends on how many operand bits switch, and the clock falls with
+ * it, so benchmarks run this on operands drawn like the attention inputs.
+ * blocks workgroups of 512 threads; every wave runs iters * 8 products
+ * (iters * 8 * 32768 FLOP per wave, blocks * 8 waves).
+ *  operands  device pointer to FA_MFMA_STREAM_OPERAND_BYTES bytes of bf16 values
+ *            (16 sets of 64 lanes x 16 fragments x 16 bytes; a wave uses set
+ *            (global wave index % 16); fragments 0-7 are the A operands, 8-15
+ *            the B operands), 16-byte aligned (FA_ERR_ALIGNMENT);
+ *            operand_bytes its size (smaller: FA_ERR_INVALID_ARG).
+ *  out       device pointer to out_floats >= blocks * 512 floats, 4-byte aligned,
+ *            not overlapping operands: each thread's sum of its accumulators.
+ *  blocks, iters  in [1, 2^20] (else FA_ERR_INVALID_ARG).
+ */
+#define FA_MFMA_STREAM_OPERAND_BYTES ((size_t)16 * 16 * 64 * 16)
+int fa_mfma_stream(const void* operands, size_t operand_bytes, float* out, size_t out_floats,
+                   int blocks, int iters, hipStream_t stream);
+
 /* Static description of an fa_status value (never NULL). */
 const char* fa_status_string(int status);
 

@@ -18,6 +18,7 @@ __all__ = [
     "online_softmax_rows_split", "online_softmax_split_workspace_bytes", "softmax_split",
     "fa_decode", "fa_decode_f16", "fa_decode_workspace_bytes", "attention_decode", "fa_fwd_fp8",
     "fa_decode_static", "DECODE_STATIC_SCRATCH_BYTES", "FA_ERR_SCRATCH_LIMIT", "fa_stream_copy",
+    "fa_mfma_stream", "MFMA_STREAM_OPERAND_BYTES",
     "fa_fwd_local", "fa_fwd_local_f16", "fa_fwd_blocksparse", "fa_fwd_blocksparse_f16",
     "attention_blocksparse", "SPARSE_QBLOCK", "SPARSE_KBLOCK",
     "fa_status_string", "kernel_attributes", "attention", "softmax", "LIB_PATH",
@@ -38,6 +39,8 @@ FA_ERR_SCRATCH_LIMIT = -5
 
 # bytes of the static device array fa_decode_static takes its partials from
 DECODE_STATIC_SCRATCH_BYTES = 8 << 20
+# operand bytes fa_mfma_stream reads (16 sets x 16 fragments x 64 lanes x 16 bytes)
+MFMA_STREAM_OPERAND_BYTES = 16 * 16 * 64 * 16
 
 OP_FA_FWD, OP_FA_FWD_F16, OP_FA_FWD_F32, OP_SOFTMAX = 0, 1, 2, 3
 OP_FA_BWD_DQ, OP_FA_BWD_DKDV, OP_FA_DECODE, OP_FA_FWD_FP8 = 4, 5, 6, 7
@@ -107,6 +110,8 @@ def lib() -> ctypes.CDLL:
         L.online_softmax_rows_split.restype = i
         L.fa_stream_copy.argtypes = [vp, vp, ctypes.c_size_t, vp]
         L.fa_stream_copy.restype = i
+        L.fa_mfma_stream.argtypes = [vp, ctypes.c_size_t, vp, ctypes.c_size_t, i, i, vp]
+        L.fa_mfma_stream.restype = i
         L.fa_status_string.argtypes = [i]
         L.fa_status_string.restype = ctypes.c_char_p
         L.fa_kernel_attributes.argtypes = [i, i, i, ctypes.POINTER(_Attrs)]
@@ -119,6 +124,16 @@ def fa_stream_copy(x, y, nbytes, stream=None):
     """Copy nbytes (multiple of 16) with non-temporal 16-byte accesses: the HBM
     ceiling the benchmark reports beside the row softmax (see include/fa.h)."""
     _check(lib().fa_stream_copy(_ptr(x), _ptr(y), int(nbytes), _stream(stream)), "fa_stream_copy")
+
+
+def fa_mfma_stream(operands, out, blocks, iters, stream=None):
+    """Run blocks x 8 waves of iters x 8 bf16 32x32x16 MFMAs on `operands`
+    (MFMA_STREAM_OPERAND_BYTES of bf16 values) into `out` (blocks x 512 floats):
+    the matrix-unit ceiling the benchmark reports beside the attention forward
+    (see include/fa.h)."""
+    nbytes = operands.numel() * operands.element_size()
+    _check(lib().fa_mfma_stream(_ptr(operands), nbytes, _ptr(out), out.numel(), int(blocks),
+                                int(iters), _stream(stream)), "fa_mfma_stream")
 
 
 def fa_status_string(status: int) -> str:

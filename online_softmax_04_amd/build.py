@@ -16,7 +16,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libfa.so")
 SOURCES = ["fa_api.hip", "attn_fwd.hip", "attn_fwd_fp8.hip", "attn_bwd.hip", "attn_decode.hip",
-           "softmax.hip", "copy.hip"]
+           "softmax.hip", "copy.hip", "mfma_stream.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

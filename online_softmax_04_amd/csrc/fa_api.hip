@@ -405,6 +405,23 @@ int fa_stream_copy(const void* x, void* y, size_t bytes, hipStream_t stream) {
   return osm::launch_stream_copy(x, y, bytes, stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+static_assert(FA_MFMA_STREAM_OPERAND_BYTES ==
+                  (size_t)osm::kMfmaStreamVariants * osm::kMfmaStreamFragments * 64 * 16,
+              "operand layout of the MFMA stream");
+
+int fa_mfma_stream(const void* operands, size_t operand_bytes, float* out, size_t out_floats,
+                   int blocks, int iters, hipStream_t stream) {
+  if (!operands || !out || blocks < 1 || blocks > (1 << 20) || iters < 1 || iters > (1 << 20))
+    return FA_ERR_INVALID_ARG;
+  if (operand_bytes < FA_MFMA_STREAM_OPERAND_BYTES || out_floats < (size_t)blocks * 512)
+    return FA_ERR_INVALID_ARG;
+  if (!aligned(operands, 16) || !aligned(out, 4)) return FA_ERR_ALIGNMENT;
+  if (overlaps(operands, FA_MFMA_STREAM_OPERAND_BYTES, out, (size_t)blocks * 512 * sizeof(float)))
+    return FA_ERR_INVALID_ARG;
+  return osm::launch_mfma_stream(operands, out, blocks, iters, stream) == hipSuccess ? FA_OK
+                                                                                     : FA_ERR_HIP;
+}
+
 const char* fa_status_string(int status) {
   switch (status) {
     case FA_OK: return "FA_OK: success";

@@ -76,4 +76,13 @@ hipError_t launch_softmax_split(const float* x, float* y, int rows, int cols, bo
 uint64_t stream_copy_blocks(uint64_t bytes);
 hipError_t launch_stream_copy(const void* x, void* y, size_t bytes, hipStream_t stream);
 
+// MFMA stream: `blocks` workgroups of 8 waves, each wave running iters x 8
+// 32x32x16 bf16 MFMAs on operands read once from one of kMfmaStreamVariants sets
+// of kMfmaStreamFragments 16-byte fragments per lane (64 lanes); out receives
+// blocks x 512 floats.
+constexpr int kMfmaStreamVariants = 16;
+constexpr int kMfmaStreamFragments = 16;
+hipError_t launch_mfma_stream(const void* operands, float* out, int blocks, int iters,
+                              hipStream_t stream);
+
 }  // namespace osm

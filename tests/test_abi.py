@@ -32,7 +32,7 @@ def test_header_declares_the_entry_points():
               "fa_fwd_blocksparse", "fa_fwd_blocksparse_f16", "fa_bwd",
               "fa_bwd_f16", "fa_bwd_workspace_bytes",
               "fa_decode", "fa_decode_f16", "fa_decode_workspace_bytes", "fa_fwd_fp8",
-              "fa_decode_static", "fa_stream_copy",
+              "fa_decode_static", "fa_stream_copy", "fa_mfma_stream",
               "online_softmax_rows", "online_softmax_rows_split",
               "online_softmax_split_workspace_bytes", "fa_status_string", "fa_kernel_attributes"):
         assert n in names
@@ -363,6 +363,26 @@ def test_fp8_validation(kw, status):
 ])
 def test_stream_copy_validation(args, status):
     assert fa.lib().fa_stream_copy(*args, None) == status
+
+
+OPB = fa.MFMA_STREAM_OPERAND_BYTES
+
+
+@pytest.mark.parametrize("args,status", [
+    ((0, OPB, A + MB, 1024, 2, 1), fa.FA_ERR_INVALID_ARG),           # no operands
+    ((A, OPB, 0, 1024, 2, 1), fa.FA_ERR_INVALID_ARG),                # no output
+    ((A, OPB - 16, A + MB, 1024, 2, 1), fa.FA_ERR_INVALID_ARG),      # operands too small
+    ((A, OPB, A + MB, 1023, 2, 1), fa.FA_ERR_INVALID_ARG),           # output too small
+    ((A, OPB, A + MB, 1024, 0, 1), fa.FA_ERR_INVALID_ARG),           # no workgroups
+    ((A, OPB, A + MB, 1 << 30, (1 << 20) + 1, 1), fa.FA_ERR_INVALID_ARG),
+    ((A, OPB, A + MB, 1024, 2, 0), fa.FA_ERR_INVALID_ARG),           # no iterations
+    ((A, OPB, A + MB, 1024, 2, (1 << 20) + 1), fa.FA_ERR_INVALID_ARG),
+    ((A + 8, OPB, A + MB, 1024, 2, 1), fa.FA_ERR_ALIGNMENT),
+    ((A, OPB, A + MB + 2, 1024, 2, 1), fa.FA_ERR_ALIGNMENT),
+    ((A, OPB, A + OPB - 64, 1024, 2, 1), fa.FA_ERR_INVALID_ARG),     # overlapping
+])
+def test_mfma_stream_validation(args, status):
+    assert fa.lib().fa_mfma_stream(*args, None) == status
 
 
 def test_python_wrappers_raise():
