@@ -8,10 +8,10 @@
 // heads cannot fill 256 CUs with enough loads in flight.  The key range of a
 // head is cut into chunks instead; each wave runs the online-softmax recurrence
 // over its chunk and leaves a partial result (m, l, unnormalised O), and a
-// second kernel merges the partials of each query with the associative rule:
-// two partial results, each holding a maximum and a sum taken against it,
-// merge by rescaling to the larger maximum ("100 Days of GPU, Day 97", section
-// "Solution"), here
+// second kernel merges the partials of each query.  The merge is associative:
+// each partial's l and O are taken from its own reference m to the largest m
+// of the query by one factor 2^(m_s - M), then summed (the merge of partial
+// results in "100 Days of GPU, Day 97", section "Solution"):
 //     M = max_s m_s,  l = sum_s l_s 2^(m_s - M),  O = sum_s O_s 2^(m_s - M) / l.
 // No wave waits on another; the kernel boundary orders the two phases.
 //
