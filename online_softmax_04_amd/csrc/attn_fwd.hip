@@ -65,8 +65,10 @@
 // wholly before it run without a mask, and only tiles straddling the diagonal
 // (or the ragged end of the sequence) mask element by element ("Online Softmax:
 // Tiling Across a Reduction", causal paragraphs).  A wave stops computing at
-// the last tile holding a key visible to one of its queries.  Query blocks are
-// handed out longest first.
+// the last tile holding a key visible to one of its queries.  With 16-bit
+// operands a workgroup takes two query blocks, one near each end of the
+// sequence, so that every workgroup holds the same number of key tiles;
+// otherwise query blocks are handed out longest first.
 #include "common.h"
 #include "kernels.h"
 #include "mfma_tile.h"
@@ -83,7 +85,8 @@ constexpr unsigned kOnePair = sizeof(T) == 2 && __is_same(T, __bf16) ? 0x3f803f8
 constexpr float kSlack = 8.f;  // how far (log2 units) the running maximum may pass m
 constexpr int kBM = 256;       // queries per workgroup
 // keys per tile: 128 at d = 64, where the per-tile fixed costs weigh most and the
-// registers allow it (222 VGPRs); 64 at d = 128 (217 VGPRs, 128 would need 250+)
+// registers allow it (222 VGPRs); 64 at d = 128 (217 VGPRs, 128 would need 250+).
+// The causal kernels, with two query blocks inlined, take 226 and 237.
 template <int D>
 constexpr int kBN = D == 64 ? 128 : 64;
 constexpr int kThreads = 512;  // 8 waves: two groups of 4, one wave of each group per SIMD
@@ -95,7 +98,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE, int BH,
     int N, int n_mtiles, float c, int xcd_groups, int H, const int* __restrict__ doc_start,
-    int window, const int* __restrict__ blk_ptr, const int* __restrict__ blk_idx, int nnz) {
+    int window, const int* __restrict__ blk_ptr, const int* __restrict__ blk_idx, int nnz,
+    int pairs) {
   constexpr bool LOCAL = MASK == kMaskLocal;
   constexpr bool SPARSE = MASK == kMaskSparse;
   using v8 = typename Mma<T>::v8;
@@ -137,399 +141,422 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(
   // half a tile apart (see the slot schedule below).
   const int group = wave >> 2;
 
-  // ---- which (batch*head, query block) this workgroup owns ---------------------
-  int id = blockIdx.x, bh, mt;
+  // ---- which (batch*head, query blocks) this workgroup owns --------------------
+  // With pairs, a workgroup takes two query blocks of one head, mt and
+  // n_mtiles - 1 - mt, one after the other: under the causal mask every such
+  // pair holds the same number of key tiles.  The dispatcher hands workgroups to
+  // the compute units of an XCD in order, so with one block per workgroup the
+  // unequal causal blocks left compute units idle between workgroups (9% of
+  // the time at B8 H32 N8192, measured from per-workgroup timestamps).
+  const bool paired = CAUSAL && MASK == kMaskNone && pairs;  // compiled out elsewhere
+  int id = blockIdx.x, bh, mt_a, mt_b = 0;
+  const int n_units = paired ? (n_mtiles + 1) >> 1 : n_mtiles;
   if (xcd_groups) {
     // consecutive workgroup ids go round-robin over the 8 XCDs; give each XCD a
     // contiguous run of heads so the blocks sharing a head's K/V share its L2
     const int per = gridDim.x >> 3;
     id = (id & 7) * per + (id >> 3);
-    bh = id / n_mtiles;
-    mt = n_mtiles - 1 - (id - bh * n_mtiles);
+    bh = id / n_units;
+    mt_a = n_units - 1 - (id - bh * n_units);
   } else {
     bh = id % BH;
-    mt = n_mtiles - 1 - id / BH;
+    mt_a = n_units - 1 - id / BH;
   }
-  const int i0 = mt * kBM;
-  const size_t base = (size_t)bh * (size_t)N * D;
-  const uint16_t* Kh = K + base;
-  const uint16_t* Vh = V + base;
-  // 32-query blocks of the workgroup interleave between the groups, so both
-  // groups reach the causal diagonal at nearly the same key tile
-  const int qw0 = i0 + 32 * (2 * (wave & 3) + group);  // first query of this wave
-  const int qi = qw0 + l32;                             // this lane's query
-  // qw0 is uniform across the wave; the buffer descriptors built from it must
-  // be scalar, or every access through them becomes a per-lane loop
-  const int qw0_s = __builtin_amdgcn_readfirstlane(qw0);
-
-  // ---- Q^T fragments: B operand, lane = query, 8 consecutive head dims -------------
-  v8 qf[NK];
-  {
-    const auto rq = make_rsrc(Q + base + (size_t)qw0_s * D, (int64_t)(N - qw0_s) * ROW_BYTES);
-    const int off = l32 * ROW_BYTES + 16 * hf;
-#pragma unroll
-    for (int kb = 0; kb < NK; ++kb)
-      qf[kb] = __builtin_bit_cast(v8, __builtin_amdgcn_raw_buffer_load_b128(rq, off + 32 * kb, 0, 0));
+  if (paired) {
+    mt_b = mt_a;
+    mt_a = n_mtiles - 1 - mt_b;
   }
 
-  f32x16 o[ND];
-#pragma unroll
-  for (int db = 0; db < ND; ++db) o[db] = f32x16{};
-  f32x16 s[NH];
-  // The row sum of P runs on the matrix unit: with a block of ones as the A
-  // operand, every row of the accumulator receives the sum over the step's keys
-  // of each query's P.  One more MFMA per 16-key step; on the vector ALU the sum
-  // of the 16-bit P takes two-term dot products, which wait for the matrix unit
-  // while the other wave of the SIMD keeps it busy (measured slower at both
-  // head dims).
-  f32x16 lacc = f32x16{};
-  const v8 ones = __builtin_bit_cast(
-      v8, u32x4{kOnePair<T>, kOnePair<T>, kOnePair<T>, kOnePair<T>});
-  v8 pf[NH][2];  // P^T as 16-bit B operands: [32-key block][16-key step]
-  float m_run = kNegInf;
+  // one query block; called twice when paired (inlined twice: a loop around it
+  // spilled registers)
+  auto block = [&](const int mt) __attribute__((always_inline)) {
+    const int i0 = mt * kBM;
+    const size_t base = (size_t)bh * (size_t)N * D;
+    const uint16_t* Kh = K + base;
+    const uint16_t* Vh = V + base;
+    // 32-query blocks of the workgroup interleave between the groups, so both
+    // groups reach the causal diagonal at nearly the same key tile
+    const int qw0 = i0 + 32 * (2 * (wave & 3) + group);  // first query of this wave
+    const int qi = qw0 + l32;                             // this lane's query
+    // qw0 is uniform across the wave; the buffer descriptors built from it must
+    // be scalar, or every access through them becomes a per-lane loop
+    const int qw0_s = __builtin_amdgcn_readfirstlane(qw0);
 
-  const int nk_all = (N + BN - 1) / BN;
-  const int n_kt = CAUSAL ? min(nk_all, (i0 + kBM - 1) / BN + 1) : nk_all;
-  // tiles holding a key visible to some query of this wave
-  int n_w = CAUSAL ? min(n_kt, (qw0 + 31) / BN + 1) : n_kt;
-  // Without the causal limit the compiler would prove n_w == n_kt, drop the
-  // per-wave tests and merge the slots into blocks it schedules with more
-  // values live than fit in registers; keep the tests in place.
-  asm volatile("" : "+v"(n_w));
-
-  // LOCAL (with CAUSAL): query i sees keys lo_i .. i, lo_i = max(document start,
-  // i - window + 1).  Whole tiles before a wave's smallest lo_i are skipped (tw0),
-  // the workgroup loads from the smallest over its waves (t0), and tiles reaching
-  // below a wave's largest lo_i are masked element by element.
-  int lo_i = 0, lo_max_w = 0, tw0 = 0, t0 = 0;
-  if constexpr (LOCAL) {
-    const int qc = min(qi, N - 1);
-    int lo = doc_start ? doc_start[(size_t)(bh / H) * N + qc] : 0;
-    lo = min(max(lo, 0), qc);
-    if (window > 0) lo = max(lo, qc - window + 1);
-    lo_i = lo;
-    int mn = lo, mx = lo;
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      mn = min(mn, __shfl_xor(mn, off));
-      mx = max(mx, __shfl_xor(mx, off));
+    // ---- Q^T fragments: B operand, lane = query, 8 consecutive head dims -------------
+    v8 qf[NK];
+    {
+      const auto rq = make_rsrc(Q + base + (size_t)qw0_s * D, (int64_t)(N - qw0_s) * ROW_BYTES);
+      const int off = l32 * ROW_BYTES + 16 * hf;
+  #pragma unroll
+      for (int kb = 0; kb < NK; ++kb)
+        qf[kb] = __builtin_bit_cast(v8, __builtin_amdgcn_raw_buffer_load_b128(rq, off + 32 * kb, 0, 0));
     }
-    lo_max_w = mx;
-    tw0 = __builtin_amdgcn_readfirstlane(mn) / BN;
-    __shared__ int wave_first[kThreads / 64];
-    if (lane == 0) wave_first[wave] = tw0;
-    __syncthreads();
-    t0 = wave_first[0];
-#pragma unroll
-    for (int w = 1; w < kThreads / 64; ++w) t0 = min(t0, wave_first[w]);
-  }
-  // tile t holds keys this wave computes with
-  auto act = [&](int t) { return (!LOCAL || t >= tw0) && t < n_w; };
 
-  // The workgroup walks a list of key tiles: position i holds tile t0 + i for the
-  // dense and sliding-window kernels; for block-sparse, the tiles of the key
-  // blocks listed for this query block (ascending, as the pattern lists them).
-  // Causal masking and the key count N apply on top.
-  constexpr int kTilesPerBlock = kSparseKBlock / BN;
-  const int nkb = (N + kSparseKBlock - 1) / kSparseKBlock;  // key blocks
-  int n_list = n_kt - t0, p0 = 0;
-  if constexpr (SPARSE) {
-    static_assert(kBM == kSparseQBlock && kSparseKBlock % BN == 0, "pattern blocks");
-    // the row's range, clamped into [0, nnz]
-    p0 = min(max(blk_ptr[mt], 0), nnz);
-    n_list = (min(max(blk_ptr[mt + 1], p0), nnz) - p0) * kTilesPerBlock;
-  }
-  auto tile_of = [&](int i) -> int {
-    if constexpr (SPARSE) {
-      // a block index outside [0, nkb) maps past the last key: no load, no compute
-      const unsigned b = (unsigned)blk_idx[p0 + i / kTilesPerBlock];
-      return (int)min(b, (unsigned)nkb) * kTilesPerBlock + i % kTilesPerBlock;
-    } else {
-      return t0 + i;
-    }
-  };
-  // last key a tile may start at and still hold a key this wave computes with;
-  // opaque to the compiler for the reason n_w is
-  int j0_max = CAUSAL ? min(qw0 + 31, N - 1) : N - 1;
-  if constexpr (SPARSE) asm volatile("" : "+v"(j0_max));
-  // list position i holds keys this wave computes with
-  auto act_at = [&](int i) {
-    if constexpr (SPARSE) {
-      return tile_of(i) * BN <= j0_max;
-    } else {
-      return act(t0 + i);
-    }
-  };
+    f32x16 o[ND];
+  #pragma unroll
+    for (int db = 0; db < ND; ++db) o[db] = f32x16{};
+    f32x16 s[NH];
+    // The row sum of P runs on the matrix unit: with a block of ones as the A
+    // operand, every row of the accumulator receives the sum over the step's keys
+    // of each query's P.  One more MFMA per 16-key step; on the vector ALU the sum
+    // of the 16-bit P takes two-term dot products, which wait for the matrix unit
+    // while the other wave of the SIMD keeps it busy (measured slower at both
+    // head dims).
+    f32x16 lacc = f32x16{};
+    const v8 ones = __builtin_bit_cast(
+        v8, u32x4{kOnePair<T>, kOnePair<T>, kOnePair<T>, kOnePair<T>});
+    v8 pf[NH][2];  // P^T as 16-bit B operands: [32-key block][16-key step]
+    float m_run = kNegInf;
 
-  // ---- loader: global -> LDS directly, no registers ------------------------------------
-  // A wave-wide 16-byte-per-lane buffer load with the LDS flag writes lane i's
-  // 16 bytes at (LDS base + 16 i): each of the wave's NI loads fills RPI whole
-  // rows, and each lane fetches the global chunk that its LDS slot holds under
-  // the swizzle.  Rows past N fall outside the buffer and land as zeros.
-  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
-  int kgoff[NI], vgoff[NI];
-#pragma unroll
-  for (int j = 0; j < NI; ++j) {
-    const int row = ((LG ? wave & 3 : wave) * NI + j) * RPI + lane / CPR;
-    const int p = lane % CPR;
-    kgoff[j] = row * ROW_BYTES + (p ^ kswz<D>(row)) * 16;
-    vgoff[j] = row * ROW_BYTES + (p ^ vswz<D>(row)) * 16;
-  }
-  // valid = false gives an empty buffer: the loads then read nothing and write
-  // zeros into the stage
-  auto load_k = [&](int t, auto st, bool valid = true) __attribute__((always_inline)) {
-    const auto r = make_rsrc(Kh + (size_t)t * BN * D, valid ? (int64_t)(N - t * BN) * ROW_BYTES : 0);
-#pragma unroll
-    for (int j = 0; j < NI; ++j)
-      load16_to_lds(r, kbuf(st) + ((LG ? wave_s & 3 : wave_s) * NI + j) * 1024, kgoff[j]);
-  };
-  auto load_v = [&](int t, auto st, bool valid = true) __attribute__((always_inline)) {
-    const auto r = make_rsrc(Vh + (size_t)t * BN * D, valid ? (int64_t)(N - t * BN) * ROW_BYTES : 0);
-#pragma unroll
-    for (int j = 0; j < NI; ++j)
-      load16_to_lds(r, vbuf(st) + ((LG ? wave_s & 3 : wave_s) * NI + j) * 1024, vgoff[j]);
-  };
-  // direct loads write LDS behind the compiler's back: wait for them explicitly
-  auto loads_landed = [&]() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
+    const int nk_all = (N + BN - 1) / BN;
+    const int n_kt = CAUSAL ? min(nk_all, (i0 + kBM - 1) / BN + 1) : nk_all;
+    // tiles holding a key visible to some query of this wave
+    int n_w = CAUSAL ? min(n_kt, (qw0 + 31) / BN + 1) : n_kt;
+    // Without the causal limit the compiler would prove n_w == n_kt, drop the
+    // per-wave tests and merge the slots into blocks it schedules with more
+    // values live than fit in registers; keep the tests in place.
+    asm volatile("" : "+v"(n_w));
 
-  // ---- operand read offsets -------------------------------------------------------------
-  // K (A operand of S^T = K Q^T): row l32 (+32 for the second key half), logical
-  // chunk 2 kb + hf.  Rows 32 apart share a swizzle.
-  int kroff[NK];
-#pragma unroll
-  for (int kb = 0; kb < NK; ++kb) kroff[kb] = l32 * ROW_BYTES + ((2 * kb + hf) ^ kswz<D>(l32)) * 16;
-  // V^T (A operand of O^T = V^T P^T) through ds_read_b64_tr_b16: within each
-  // group of 16 lanes, the lane at position q supplies the address of row
-  // R + q/4, head dims C + 4 (q % 4) .. +3, and receives V[R + k][C + q] for
-  // k = 0..3.  With R = 32 kh + 16 kb + 4 hf and C = 32 db + 16 ((lane >> 4) & 1)
-  // the lane gets its head dim (32 db + lane % 32) at the keys of B-operand
-  // positions 8 hf .. 8 hf + 3; a second read 8 rows further gives 8 hf + 4 ..
-  // 8 hf + 7 (the P^T key permutation).  Row steps of 4 keep the swizzle.
-  int vroff[ND];
-  {
-    const int q = lane & 15;
-    const int row = 4 * hf + (q >> 2);
-    const int col = 16 * ((lane >> 4) & 1) + 4 * (q & 3);
-#pragma unroll
-    for (int db = 0; db < ND; ++db)
-      vroff[db] = row * ROW_BYTES + (((col + 32 * db) >> 3) ^ vswz<D>(row)) * 16 + (col & 7) * 2;
-  }
-
-  // ---- the three pieces of a tile --------------------------------------------------------
-  // QK: S^T = K Q^T, one accumulator per 32-key block, from K stage st.
-  auto qk = [&](auto st) __attribute__((always_inline)) {
-    const unsigned char* Kt = kbuf(st);
-#pragma unroll
-    for (int kh = 0; kh < NH; ++kh) s[kh] = f32x16{};
-#pragma unroll
-    for (int kb = 0; kb < NK; ++kb) {
-#pragma unroll
-      for (int kh = 0; kh < NH; ++kh) {
-        const v8 kf = __builtin_bit_cast(
-            v8, *reinterpret_cast<const u32x4*>(Kt + kroff[kb] + kh * 32 * ROW_BYTES));
-        s[kh] = Mma<T>::run(kf, qf[kb], s[kh]);
+    // LOCAL (with CAUSAL): query i sees keys lo_i .. i, lo_i = max(document start,
+    // i - window + 1).  Whole tiles before a wave's smallest lo_i are skipped (tw0),
+    // the workgroup loads from the smallest over its waves (t0), and tiles reaching
+    // below a wave's largest lo_i are masked element by element.
+    int lo_i = 0, lo_max_w = 0, tw0 = 0, t0 = 0;
+    if constexpr (LOCAL) {
+      const int qc = min(qi, N - 1);
+      int lo = doc_start ? doc_start[(size_t)(bh / H) * N + qc] : 0;
+      lo = min(max(lo, 0), qc);
+      if (window > 0) lo = max(lo, qc - window + 1);
+      lo_i = lo;
+      int mn = lo, mx = lo;
+  #pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) {
+        mn = min(mn, __shfl_xor(mn, off));
+        mx = max(mx, __shfl_xor(mx, off));
       }
+      lo_max_w = mx;
+      tw0 = __builtin_amdgcn_readfirstlane(mn) / BN;
+      __shared__ int wave_first[kThreads / 64];
+      if (lane == 0) wave_first[wave] = tw0;
+      __syncthreads();
+      t0 = wave_first[0];
+  #pragma unroll
+      for (int w = 1; w < kThreads / 64; ++w) t0 = min(t0, wave_first[w]);
     }
-  };
-  // SM(t): online softmax of S(t): m, l and O rescaled by 2^(m_old - m_new),
-  // P = 2^(c S - m_new) packed to 16 bits, with m the trailing reference.
-  auto sm = [&](int t) __attribute__((always_inline)) {
-    const int j0 = t * BN;
-    // keys past N, and keys after the query when causal (wave-uniform test)
-    if ((j0 + BN > N) || (CAUSAL && j0 + BN - 1 > qw0) || (LOCAL && j0 < lo_max_w)) {
-#pragma unroll
+    // tile t holds keys this wave computes with
+    auto act = [&](int t) { return (!LOCAL || t >= tw0) && t < n_w; };
+
+    // The workgroup walks a list of key tiles: position i holds tile t0 + i for the
+    // dense and sliding-window kernels; for block-sparse, the tiles of the key
+    // blocks listed for this query block (ascending, as the pattern lists them).
+    // Causal masking and the key count N apply on top.
+    constexpr int kTilesPerBlock = kSparseKBlock / BN;
+    const int nkb = (N + kSparseKBlock - 1) / kSparseKBlock;  // key blocks
+    int n_list = n_kt - t0, p0 = 0;
+    if constexpr (SPARSE) {
+      static_assert(kBM == kSparseQBlock && kSparseKBlock % BN == 0, "pattern blocks");
+      // the row's range, clamped into [0, nnz]
+      p0 = min(max(blk_ptr[mt], 0), nnz);
+      n_list = (min(max(blk_ptr[mt + 1], p0), nnz) - p0) * kTilesPerBlock;
+    }
+    auto tile_of = [&](int i) -> int {
+      if constexpr (SPARSE) {
+        // a block index outside [0, nkb) maps past the last key: no load, no compute
+        const unsigned b = (unsigned)blk_idx[p0 + i / kTilesPerBlock];
+        return (int)min(b, (unsigned)nkb) * kTilesPerBlock + i % kTilesPerBlock;
+      } else {
+        return t0 + i;
+      }
+    };
+    // last key a tile may start at and still hold a key this wave computes with;
+    // opaque to the compiler for the reason n_w is
+    int j0_max = CAUSAL ? min(qw0 + 31, N - 1) : N - 1;
+    if constexpr (SPARSE) asm volatile("" : "+v"(j0_max));
+    // list position i holds keys this wave computes with
+    auto act_at = [&](int i) {
+      if constexpr (SPARSE) {
+        return tile_of(i) * BN <= j0_max;
+      } else {
+        return act(t0 + i);
+      }
+    };
+
+    // ---- loader: global -> LDS directly, no registers ------------------------------------
+    // A wave-wide 16-byte-per-lane buffer load with the LDS flag writes lane i's
+    // 16 bytes at (LDS base + 16 i): each of the wave's NI loads fills RPI whole
+    // rows, and each lane fetches the global chunk that its LDS slot holds under
+    // the swizzle.  Rows past N fall outside the buffer and land as zeros.
+    const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+    int kgoff[NI], vgoff[NI];
+  #pragma unroll
+    for (int j = 0; j < NI; ++j) {
+      const int row = ((LG ? wave & 3 : wave) * NI + j) * RPI + lane / CPR;
+      const int p = lane % CPR;
+      kgoff[j] = row * ROW_BYTES + (p ^ kswz<D>(row)) * 16;
+      vgoff[j] = row * ROW_BYTES + (p ^ vswz<D>(row)) * 16;
+    }
+    // valid = false gives an empty buffer: the loads then read nothing and write
+    // zeros into the stage
+    auto load_k = [&](int t, auto st, bool valid = true) __attribute__((always_inline)) {
+      const auto r = make_rsrc(Kh + (size_t)t * BN * D, valid ? (int64_t)(N - t * BN) * ROW_BYTES : 0);
+  #pragma unroll
+      for (int j = 0; j < NI; ++j)
+        load16_to_lds(r, kbuf(st) + ((LG ? wave_s & 3 : wave_s) * NI + j) * 1024, kgoff[j]);
+    };
+    auto load_v = [&](int t, auto st, bool valid = true) __attribute__((always_inline)) {
+      const auto r = make_rsrc(Vh + (size_t)t * BN * D, valid ? (int64_t)(N - t * BN) * ROW_BYTES : 0);
+  #pragma unroll
+      for (int j = 0; j < NI; ++j)
+        load16_to_lds(r, vbuf(st) + ((LG ? wave_s & 3 : wave_s) * NI + j) * 1024, vgoff[j]);
+    };
+    // direct loads write LDS behind the compiler's back: wait for them explicitly
+    auto loads_landed = [&]() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
+
+    // ---- operand read offsets -------------------------------------------------------------
+    // K (A operand of S^T = K Q^T): row l32 (+32 for the second key half), logical
+    // chunk 2 kb + hf.  Rows 32 apart share a swizzle.
+    int kroff[NK];
+  #pragma unroll
+    for (int kb = 0; kb < NK; ++kb) kroff[kb] = l32 * ROW_BYTES + ((2 * kb + hf) ^ kswz<D>(l32)) * 16;
+    // V^T (A operand of O^T = V^T P^T) through ds_read_b64_tr_b16: within each
+    // group of 16 lanes, the lane at position q supplies the address of row
+    // R + q/4, head dims C + 4 (q % 4) .. +3, and receives V[R + k][C + q] for
+    // k = 0..3.  With R = 32 kh + 16 kb + 4 hf and C = 32 db + 16 ((lane >> 4) & 1)
+    // the lane gets its head dim (32 db + lane % 32) at the keys of B-operand
+    // positions 8 hf .. 8 hf + 3; a second read 8 rows further gives 8 hf + 4 ..
+    // 8 hf + 7 (the P^T key permutation).  Row steps of 4 keep the swizzle.
+    int vroff[ND];
+    {
+      const int q = lane & 15;
+      const int row = 4 * hf + (q >> 2);
+      const int col = 16 * ((lane >> 4) & 1) + 4 * (q & 3);
+  #pragma unroll
+      for (int db = 0; db < ND; ++db)
+        vroff[db] = row * ROW_BYTES + (((col + 32 * db) >> 3) ^ vswz<D>(row)) * 16 + (col & 7) * 2;
+    }
+
+    // ---- the three pieces of a tile --------------------------------------------------------
+    // QK: S^T = K Q^T, one accumulator per 32-key block, from K stage st.
+    auto qk = [&](auto st) __attribute__((always_inline)) {
+      const unsigned char* Kt = kbuf(st);
+  #pragma unroll
+      for (int kh = 0; kh < NH; ++kh) s[kh] = f32x16{};
+  #pragma unroll
+      for (int kb = 0; kb < NK; ++kb) {
+  #pragma unroll
+        for (int kh = 0; kh < NH; ++kh) {
+          const v8 kf = __builtin_bit_cast(
+              v8, *reinterpret_cast<const u32x4*>(Kt + kroff[kb] + kh * 32 * ROW_BYTES));
+          s[kh] = Mma<T>::run(kf, qf[kb], s[kh]);
+        }
+      }
+    };
+    // SM(t): online softmax of S(t): m, l and O rescaled by 2^(m_old - m_new),
+    // P = 2^(c S - m_new) packed to 16 bits, with m the trailing reference.
+    auto sm = [&](int t) __attribute__((always_inline)) {
+      const int j0 = t * BN;
+      // keys past N, and keys after the query when causal (wave-uniform test)
+      if ((j0 + BN > N) || (CAUSAL && j0 + BN - 1 > qw0) || (LOCAL && j0 < lo_max_w)) {
+  #pragma unroll
+        for (int kh = 0; kh < NH; ++kh) {
+  #pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = j0 + 32 * kh + 8 * (r >> 2) + 4 * hf + (r & 3);
+            if (key >= N || (CAUSAL && key > qi) || (LOCAL && key < lo_i)) s[kh][r] = kNegInf;
+          }
+        }
+      }
+      float mx = kNegInf;
+  #pragma unroll
+      for (int kh = 0; kh < NH; ++kh)
+  #pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kh][r]);
+      mx = max_halves(mx);
+      const float m_cand = fmaxf(m_run, mx * c);
+      const float m_new = (m_cand > m_run + kSlack) ? m_cand : m_run;  // -inf moves to any finite max
+      const float m_sub = (m_new == kNegInf) ? 0.f : m_new;  // a fully masked row stays empty
+      const float alpha = exp2_fast(m_run - m_sub);
+  #pragma unroll
       for (int kh = 0; kh < NH; ++kh) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = j0 + 32 * kh + 8 * (r >> 2) + 4 * hf + (r & 3);
-          if (key >= N || (CAUSAL && key > qi) || (LOCAL && key < lo_i)) s[kh][r] = kNegInf;
+  #pragma unroll
+        for (int r = 0; r < 16; ++r) pf[kh][r >> 3][r & 7] = (T)exp2_fast(fmaf(s[kh][r], c, -m_sub));
+      }
+      m_run = m_new;
+      if (__any(alpha != 1.f)) {  // wave-uniform; skipped while no row's reference moves
+  #pragma unroll
+        for (int db = 0; db < ND; ++db) o[db] *= alpha;
+        lacc *= alpha;
+      }
+    };
+    // PV: O^T += V^T P^T, from V stage st.
+    auto pv = [&](auto st) __attribute__((always_inline)) {
+      const unsigned char* Vt = vbuf(st);
+  #pragma unroll
+      for (int kh = 0; kh < NH; ++kh) {
+  #pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+  #pragma unroll
+          for (int db = 0; db < ND; ++db) {  // ND independent accumulators in flight
+            const unsigned char* pa = Vt + vroff[db] + (32 * kh + 16 * kb) * ROW_BYTES;
+            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)pa);
+            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(pa + 8 * ROW_BYTES));
+            const v8 vf = __builtin_bit_cast(v8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+            o[db] = Mma<T>::run(vf, pf[kh][kb], o[db]);
+          }
+          lacc = Mma<T>::run(ones, pf[kh][kb], lacc);
+        }
+      }
+    };
+
+    // PV(tp) then QK(tq) in one block, with the LDS operand reads running a fixed
+    // distance ahead of the MFMAs that consume them: enough reads in flight to
+    // cover LDS latency, few enough registers to avoid spilling.  nld (a
+    // compile-time count) direct loads issued by loads() are spread evenly
+    // between the MFMAs.
+    auto pv_qk = [&](auto stp, auto stq, auto nld, auto&& loads) __attribute__((always_inline)) {
+      constexpr int NL = decltype(nld)::value;
+      loads();
+      pv(stp);
+      qk(stq);
+      // PV MFMAs take two transposed reads each, QK MFMAs one read
+      constexpr int kAhead = 4;               // MFMAs whose operands are read ahead
+      // (the row-sum MFMA that ends each 16-key step reads nothing)
+      constexpr int kStep = ND + 1;  // PV MFMAs per 16-key step
+      constexpr int kPv = 2 * NH * kStep, kQk = NH * NK;
+  #pragma unroll
+      for (int j = 0; j < kAhead; ++j)
+        if (j % kStep != ND) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS reads
+      constexpr int kEvery = NL ? (kPv + kQk) / (NL + 1) : 1;
+  #pragma unroll
+      for (int i = 0; i < kPv + kQk; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+        if (NL && i % kEvery == kEvery - 1 && i / kEvery < NL)
+          __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one direct load
+        const int j = i + kAhead;                           // operand reads for MFMA j
+        if (j < kPv) {
+          if (j % kStep != ND) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        } else if (j < kPv + kQk) {
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+      }
+    };
+
+    // The tile at list position i, in stage S = i & 1: slot X, the barrier, slot Y.
+    auto tile = [&](int i, auto st) __attribute__((always_inline)) {
+      constexpr int S = decltype(st)::value;
+      const StageTag<S> cur;
+      const StageTag<S ^ 1> other;
+      const bool a_cur = act_at(i);
+      // ---- slot X
+      if (group == 0) {
+        if (a_cur) sm(tile_of(i));
+      } else {
+        __builtin_amdgcn_s_setprio(1);
+        const bool a_prev = i > 0 && act_at(i - 1);
+        if (a_prev && a_cur) {
+          pv_qk(other, cur, std::integral_constant<int, 0>{}, [] {});
+        } else {
+          if (a_prev) pv(other);
+          if (a_cur) qk(cur);
+        }
+        __builtin_amdgcn_s_setprio(0);
+      }
+      loads_landed();  // K of position i + 1, V of position i
+      __syncthreads();
+      // ---- slot Y
+      if (group == 0) {
+        __builtin_amdgcn_s_setprio(1);
+        const bool a_next = i + 1 < n_list && act_at(i + 1);
+        // K(i + 2) into the stage K(i) leaves, V(i + 1) into the one V(i - 1) left;
+        // past the end of the list the loads are empty, and the zeros they write
+        // land in stages that no later read uses.  Unconditional loads keep the
+        // block straight, so the schedule can spread them.
+        const bool k_ok = i + 2 < n_list, v_ok = i + 1 < n_list;
+        const int tk = k_ok ? tile_of(i + 2) : 0, tv = v_ok ? tile_of(i + 1) : 0;
+        auto loads = [&]() __attribute__((always_inline)) {
+          load_k(tk, cur, k_ok);
+          load_v(tv, other, v_ok);
+        };
+        if (a_cur && a_next) {
+          pv_qk(cur, other, std::integral_constant<int, 2 * NI>{}, loads);
+        } else {
+          loads();
+          if (a_cur) pv(cur);
+          if (a_next) qk(other);
+        }
+        __builtin_amdgcn_s_setprio(0);
+      } else {
+        if (a_cur) sm(tile_of(i));
+      }
+    };
+
+    // ---- slot schedule ----------------------------------------------------------------
+    // Each tile t takes two slots:
+    //   slot X(t): group 0 runs SM(t)          group 1 runs PV(t-1), QK(t)
+    //   slot Y(t): group 0 runs PV(t), QK(t+1) group 1 runs SM(t)
+    // so on every SIMD one wave keeps the matrix unit busy while the other runs
+    // the vector-ALU softmax.  K(t+1) and V(t) are read from Y(t) to X(t+1); group
+    // 0 issues their loads between its MFMAs in Y(t-1) (into the stages of K(t-1)
+    // and V(t-1), last read in X(t-1)), they land during Y(t-1) and X(t), and the
+    // workgroup barrier that ends X(t) publishes them.  That barrier is the only one per tile: no LDS stage changes
+    // hands between Y(t) and X(t+1), and meeting once per tile keeps the two
+    // groups in opposite phases.  The dense kernel starts at tile t0 = 0; the
+    // LOCAL one at the workgroup's first visible tile, each wave computing from
+    // its own first tile tw0.
+    const bool loader = !LG || group == 0;
+    if (loader && n_list > 0) load_k(tile_of(0), StageTag<0>{});
+    loads_landed();
+    __syncthreads();
+    // Retire the Q loads here.  Left pending, they would make the first MFMA that
+    // reads Q wait on the vector-memory counter, which then also counts the tile
+    // loads in flight.
+  #pragma unroll
+    for (int kb = 0; kb < NK; ++kb) asm volatile("" ::"v"(qf[kb]));
+    // slot Y(t0 - 1): load K(t0+1), V(t0); group 0 computes S(t0)
+    if (loader && 1 < n_list) load_k(tile_of(1), StageTag<1>{});
+    if (loader && n_list > 0) load_v(tile_of(0), StageTag<0>{});
+    if (group == 0 && n_list > 0 && act_at(0)) {
+      __builtin_amdgcn_s_setprio(1);
+      qk(StageTag<0>{});
+      __builtin_amdgcn_s_setprio(0);
+    }
+    __syncthreads();
+    for (int i = 0; i < n_list; i += 2) {
+      tile(i, StageTag<0>{});
+      if (i + 1 < n_list) tile(i + 1, StageTag<1>{});
+    }
+    // slot X after the last tile: group 1 finishes the last PV
+    if (group == 1 && n_list > 0 && act_at(n_list - 1)) {
+      if (((n_list - 1) & 1) == 0) pv(StageTag<0>{}); else pv(StageTag<1>{});
+    }
+
+    // ---- epilogue: O / l, logsumexp --------------------------------------------------
+    const float l_tot = lacc[0];
+    // a block-sparse row can see no key at all: O = 0 and logsumexp -inf there
+    const float inv = (SPARSE && l_tot == 0.f) ? 0.f : 1.f / l_tot;
+    {
+      // rows past N fall outside the buffer and are dropped
+      const auto ro = make_rsrc(O + base + (size_t)qw0_s * D, (int64_t)(N - qw0_s) * ROW_BYTES);
+      const int off = l32 * ROW_BYTES + 8 * hf;
+  #pragma unroll
+      for (int db = 0; db < ND; ++db) {
+  #pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const u32x2 w = u32x2{pack2<T>(o[db][4 * g] * inv, o[db][4 * g + 1] * inv),
+                                pack2<T>(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv)};
+          __builtin_amdgcn_raw_buffer_store_b64(w, ro, off + (db * 32 + 8 * g) * 2, 0, 0);
         }
       }
     }
-    float mx = kNegInf;
-#pragma unroll
-    for (int kh = 0; kh < NH; ++kh)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kh][r]);
-    mx = max_halves(mx);
-    const float m_cand = fmaxf(m_run, mx * c);
-    const float m_new = (m_cand > m_run + kSlack) ? m_cand : m_run;  // -inf moves to any finite max
-    const float m_sub = (m_new == kNegInf) ? 0.f : m_new;  // a fully masked row stays empty
-    const float alpha = exp2_fast(m_run - m_sub);
-#pragma unroll
-    for (int kh = 0; kh < NH; ++kh) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) pf[kh][r >> 3][r & 7] = (T)exp2_fast(fmaf(s[kh][r], c, -m_sub));
-    }
-    m_run = m_new;
-    if (__any(alpha != 1.f)) {  // wave-uniform; skipped while no row's reference moves
-#pragma unroll
-      for (int db = 0; db < ND; ++db) o[db] *= alpha;
-      lacc *= alpha;
-    }
-  };
-  // PV: O^T += V^T P^T, from V stage st.
-  auto pv = [&](auto st) __attribute__((always_inline)) {
-    const unsigned char* Vt = vbuf(st);
-#pragma unroll
-    for (int kh = 0; kh < NH; ++kh) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int db = 0; db < ND; ++db) {  // ND independent accumulators in flight
-          const unsigned char* pa = Vt + vroff[db] + (32 * kh + 16 * kb) * ROW_BYTES;
-          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)pa);
-          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(pa + 8 * ROW_BYTES));
-          const v8 vf = __builtin_bit_cast(v8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-          o[db] = Mma<T>::run(vf, pf[kh][kb], o[db]);
-        }
-        lacc = Mma<T>::run(ones, pf[kh][kb], lacc);
-      }
-    }
+    if (LSE != nullptr && hf == 0 && qi < N)
+      LSE[(size_t)bh * N + qi] = (SPARSE && l_tot == 0.f) ? kNegInf : (m_run + log2f(l_tot)) * kLn2;
   };
 
-  // PV(tp) then QK(tq) in one block, with the LDS operand reads running a fixed
-  // distance ahead of the MFMAs that consume them: enough reads in flight to
-  // cover LDS latency, few enough registers to avoid spilling.  nld (a
-  // compile-time count) direct loads issued by loads() are spread evenly
-  // between the MFMAs.
-  auto pv_qk = [&](auto stp, auto stq, auto nld, auto&& loads) __attribute__((always_inline)) {
-    constexpr int NL = decltype(nld)::value;
-    loads();
-    pv(stp);
-    qk(stq);
-    // PV MFMAs take two transposed reads each, QK MFMAs one read
-    constexpr int kAhead = 4;               // MFMAs whose operands are read ahead
-    // (the row-sum MFMA that ends each 16-key step reads nothing)
-    constexpr int kStep = ND + 1;  // PV MFMAs per 16-key step
-    constexpr int kPv = 2 * NH * kStep, kQk = NH * NK;
-#pragma unroll
-    for (int j = 0; j < kAhead; ++j)
-      if (j % kStep != ND) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS reads
-    constexpr int kEvery = NL ? (kPv + kQk) / (NL + 1) : 1;
-#pragma unroll
-    for (int i = 0; i < kPv + kQk; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-      if (NL && i % kEvery == kEvery - 1 && i / kEvery < NL)
-        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one direct load
-      const int j = i + kAhead;                           // operand reads for MFMA j
-      if (j < kPv) {
-        if (j % kStep != ND) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      } else if (j < kPv + kQk) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      }
-    }
-  };
-
-  // The tile at list position i, in stage S = i & 1: slot X, the barrier, slot Y.
-  auto tile = [&](int i, auto st) __attribute__((always_inline)) {
-    constexpr int S = decltype(st)::value;
-    const StageTag<S> cur;
-    const StageTag<S ^ 1> other;
-    const bool a_cur = act_at(i);
-    // ---- slot X
-    if (group == 0) {
-      if (a_cur) sm(tile_of(i));
-    } else {
-      __builtin_amdgcn_s_setprio(1);
-      const bool a_prev = i > 0 && act_at(i - 1);
-      if (a_prev && a_cur) {
-        pv_qk(other, cur, std::integral_constant<int, 0>{}, [] {});
-      } else {
-        if (a_prev) pv(other);
-        if (a_cur) qk(cur);
-      }
-      __builtin_amdgcn_s_setprio(0);
-    }
-    loads_landed();  // K of position i + 1, V of position i
-    __syncthreads();
-    // ---- slot Y
-    if (group == 0) {
-      __builtin_amdgcn_s_setprio(1);
-      const bool a_next = i + 1 < n_list && act_at(i + 1);
-      // K(i + 2) into the stage K(i) leaves, V(i + 1) into the one V(i - 1) left;
-      // past the end of the list the loads are empty, and the zeros they write
-      // land in stages that no later read uses.  Unconditional loads keep the
-      // block straight, so the schedule can spread them.
-      const bool k_ok = i + 2 < n_list, v_ok = i + 1 < n_list;
-      const int tk = k_ok ? tile_of(i + 2) : 0, tv = v_ok ? tile_of(i + 1) : 0;
-      auto loads = [&]() __attribute__((always_inline)) {
-        load_k(tk, cur, k_ok);
-        load_v(tv, other, v_ok);
-      };
-      if (a_cur && a_next) {
-        pv_qk(cur, other, std::integral_constant<int, 2 * NI>{}, loads);
-      } else {
-        loads();
-        if (a_cur) pv(cur);
-        if (a_next) qk(other);
-      }
-      __builtin_amdgcn_s_setprio(0);
-    } else {
-      if (a_cur) sm(tile_of(i));
-    }
-  };
-
-  // ---- slot schedule ----------------------------------------------------------------
-  // Each tile t takes two slots:
-  //   slot X(t): group 0 runs SM(t)          group 1 runs PV(t-1), QK(t)
-  //   slot Y(t): group 0 runs PV(t), QK(t+1) group 1 runs SM(t)
-  // so on every SIMD one wave keeps the matrix unit busy while the other runs
-  // the vector-ALU softmax.  K(t+1) and V(t) are read from Y(t) to X(t+1); group
-  // 0 issues their loads between its MFMAs in Y(t-1) (into the stages of K(t-1)
-  // and V(t-1), last read in X(t-1)), they land during Y(t-1) and X(t), and the
-  // workgroup barrier that ends X(t) publishes them.  That barrier is the only one per tile: no LDS stage changes
-  // hands between Y(t) and X(t+1), and meeting once per tile keeps the two
-  // groups in opposite phases.  The dense kernel starts at tile t0 = 0; the
-  // LOCAL one at the workgroup's first visible tile, each wave computing from
-  // its own first tile tw0.
-  const bool loader = !LG || group == 0;
-  if (loader && n_list > 0) load_k(tile_of(0), StageTag<0>{});
-  loads_landed();
-  __syncthreads();
-  // Retire the Q loads here.  Left pending, they would make the first MFMA that
-  // reads Q wait on the vector-memory counter, which then also counts the tile
-  // loads in flight.
-#pragma unroll
-  for (int kb = 0; kb < NK; ++kb) asm volatile("" ::"v"(qf[kb]));
-  // slot Y(t0 - 1): load K(t0+1), V(t0); group 0 computes S(t0)
-  if (loader && 1 < n_list) load_k(tile_of(1), StageTag<1>{});
-  if (loader && n_list > 0) load_v(tile_of(0), StageTag<0>{});
-  if (group == 0 && n_list > 0 && act_at(0)) {
-    __builtin_amdgcn_s_setprio(1);
-    qk(StageTag<0>{});
-    __builtin_amdgcn_s_setprio(0);
+  block(mt_a);
+  if (paired && mt_b != mt_a) {
+    __syncthreads();  // the first block's LDS stages are read no more
+    block(mt_b);
   }
-  __syncthreads();
-  for (int i = 0; i < n_list; i += 2) {
-    tile(i, StageTag<0>{});
-    if (i + 1 < n_list) tile(i + 1, StageTag<1>{});
-  }
-  // slot X after the last tile: group 1 finishes the last PV
-  if (group == 1 && n_list > 0 && act_at(n_list - 1)) {
-    if (((n_list - 1) & 1) == 0) pv(StageTag<0>{}); else pv(StageTag<1>{});
-  }
-
-  // ---- epilogue: O / l, logsumexp --------------------------------------------------
-  const float l_tot = lacc[0];
-  // a block-sparse row can see no key at all: O = 0 and logsumexp -inf there
-  const float inv = (SPARSE && l_tot == 0.f) ? 0.f : 1.f / l_tot;
-  {
-    // rows past N fall outside the buffer and are dropped
-    const auto ro = make_rsrc(O + base + (size_t)qw0_s * D, (int64_t)(N - qw0_s) * ROW_BYTES);
-    const int off = l32 * ROW_BYTES + 8 * hf;
-#pragma unroll
-    for (int db = 0; db < ND; ++db) {
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const u32x2 w = u32x2{pack2<T>(o[db][4 * g] * inv, o[db][4 * g + 1] * inv),
-                              pack2<T>(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv)};
-        __builtin_amdgcn_raw_buffer_store_b64(w, ro, off + (db * 32 + 8 * g) * 2, 0, 0);
-      }
-    }
-  }
-  if (LSE != nullptr && hf == 0 && qi < N)
-    LSE[(size_t)bh * N + qi] = (SPARSE && l_tot == 0.f) ? kNegInf : (m_run + log2f(l_tot)) * kLn2;
 }
 
 // ------------------------------------------------------------------------------------
@@ -664,7 +691,9 @@ hipError_t launch_attn_fwd(Elem elem, const void* q, const void* k, const void* 
   int BH = B * H;
   int n_mtiles = (N + rows_per_block - 1) / rows_per_block;
   float c = scale * kLog2e;
-  const int grid = BH * n_mtiles;
+  // causal: two query blocks of unequal length per workgroup (see the kernel)
+  int pairs = (causal && elem != Elem::f32) ? 1 : 0;
+  const int grid = BH * (pairs ? (n_mtiles + 1) / 2 : n_mtiles);
   if (elem == Elem::f32) {
     void* args[] = {(void*)&q, (void*)&k, (void*)&v, (void*)&o, (void*)&lse,
                     (void*)&BH, (void*)&N, (void*)&n_mtiles, (void*)&c};
@@ -679,7 +708,7 @@ hipError_t launch_attn_fwd(Elem elem, const void* q, const void* k, const void* 
   void* args[] = {(void*)&q, (void*)&k, (void*)&v, (void*)&o, (void*)&lse, (void*)&BH,
                   (void*)&N, (void*)&n_mtiles, (void*)&c, (void*)&xcd_groups, (void*)&H,
                   (void*)&doc_start, (void*)&window, (void*)&blk_ptr, (void*)&blk_idx,
-                  (void*)&nnz};
+                  (void*)&nnz, (void*)&pairs};
   return hipLaunchKernel(fn, dim3(grid), dim3(threads), args, 0, stream);
 }
 
@@ -696,10 +725,11 @@ hipError_t launch_attn_fwd_local(Elem elem, const void* q, const void* k, const 
   const int* blk_ptr = nullptr;
   const int* blk_idx = nullptr;
   int nnz = 0;
+  int pairs = 0;
   void* args[] = {(void*)&q, (void*)&k, (void*)&v, (void*)&o, (void*)&lse, (void*)&BH,
                   (void*)&N, (void*)&n_mtiles, (void*)&c, (void*)&xcd_groups, (void*)&H,
                   (void*)&doc_start, (void*)&window, (void*)&blk_ptr, (void*)&blk_idx,
-                  (void*)&nnz};
+                  (void*)&nnz, (void*)&pairs};
   return hipLaunchKernel(fn, dim3(grid), dim3(threads), args, 0, stream);
 }
 
@@ -716,10 +746,11 @@ hipError_t launch_attn_fwd_blocksparse(Elem elem, const void* q, const void* k, 
   int xcd_groups = (BH % 8 == 0) ? 1 : 0;
   const int* doc_start = nullptr;
   int window = 0;
+  int pairs = 0;
   void* args[] = {(void*)&q, (void*)&k, (void*)&v, (void*)&o, (void*)&lse, (void*)&BH,
                   (void*)&N, (void*)&n_mtiles, (void*)&c, (void*)&xcd_groups, (void*)&H,
                   (void*)&doc_start, (void*)&window, (void*)&blk_ptr, (void*)&blk_idx,
-                  (void*)&nnz};
+                  (void*)&nnz, (void*)&pairs};
   return hipLaunchKernel(fn, dim3(grid), dim3(threads), args, 0, stream);
 }
 

@@ -171,6 +171,22 @@ def test_edge_shapes(orc, dtype, d, causal, N):
                          causal, o, lse)
 
 
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f16", 64), ("bf16", 64), ("f16", 128)])
+@pytest.mark.parametrize("B,H", [(2, 4), (1, 3)])
+@pytest.mark.parametrize("N", [700, 1025])
+def test_causal_block_pairs(orc, dtype, d, B, H, N):
+    """Causal 16-bit launches give each workgroup two query blocks of one head,
+    one from each end of the sequence.  N = 700 and 1025 give an odd number of
+    256-row blocks (3 and 5, the middle one alone, the last ragged); B*H = 8
+    takes the XCD-grouped workgroup order, B*H = 3 the plain one."""
+    say(f"[attention causal pairs] dtype={dtype} d={d} B={B} H={H} N={N}")
+    q, k, v = workloads.random_attn(B, H, N, d, dtype, seed=N * 3 + d + H)
+    scale = 1.0 / np.sqrt(d)
+    o, lse = run_gpu(q, k, v, dtype, scale, True)
+    check_against_oracle(orc, f"pairs {dtype} d{d} B{B}H{H} N{N}", q, k, v, dtype, scale, True,
+                         o, lse)
+
+
 def large_score_inputs(dtype, d):
     """Q x 10 over iid N(0, 1) inputs, [1, 2, 777, d] storage arrays."""
     q, k, v = workloads.random_attn(1, 2, 777, d, "f32", seed=99 if d == 128 else 199)
