@@ -173,109 +173,121 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dq(
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hf = lane >> 5;
   const int wave_s = __builtin_amdgcn_readfirstlane(wave);
-  int bh, qb;
-  block_of(BH, n_qblocks, xcd_groups, true, &bh, &qb);
-  const int i0 = qb * kQB;
-  const size_t base = (size_t)bh * (size_t)N * D;
-  const int qw0 = i0 + 32 * wave;  // first query of this wave
-  const int qw0_s = __builtin_amdgcn_readfirstlane(qw0);
-  const int qi = qw0 + l32;
+  // causal: blocks qb and n_qblocks - 1 - qb, one after the other, so that every
+  // workgroup visits as many key tiles as any other
+  int bh, qb_a, qb_b = 0;
+  block_of(BH, CAUSAL ? (n_qblocks + 1) >> 1 : n_qblocks, xcd_groups, true, &bh, &qb_b);
+  qb_a = CAUSAL ? n_qblocks - 1 - qb_b : qb_b;
 
-  // Q^T and dO^T as B operands: lane = query, 8 consecutive head dims per step;
-  // D_i = <dO_i, O_i> from the same rows (each lane half holds half the dims)
-  v8 qf[NK], dof[NK];
-  float Di;
-  {
-    const int64_t bytes = (int64_t)(N - qw0_s) * ROW_BYTES;
-    const auto rq = make_rsrc(Q + base + (size_t)qw0_s * D, bytes);
-    const auto rdo = make_rsrc(dO + base + (size_t)qw0_s * D, bytes);
-    const auto ro = make_rsrc(O + base + (size_t)qw0_s * D, bytes);
-    const int off = l32 * ROW_BYTES + 16 * hf;
-    float acc = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < NK; ++kb) {
-      qf[kb] = __builtin_bit_cast(v8, __builtin_amdgcn_raw_buffer_load_b128(rq, off + 32 * kb, 0, 0));
-      dof[kb] = __builtin_bit_cast(v8, __builtin_amdgcn_raw_buffer_load_b128(rdo, off + 32 * kb, 0, 0));
-      const v8 of = __builtin_bit_cast(v8, __builtin_amdgcn_raw_buffer_load_b128(ro, off + 32 * kb, 0, 0));
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc = fmaf((float)dof[kb][e], (float)of[e], acc);
-    }
-    Di = sum_halves(acc);
-  }
-  const float lse2 = qi < N ? LSE[(size_t)bh * N + qi] * kLog2e : 0.f;
-  if (hf == 0 && qi < N) Dws[(size_t)bh * N + qi] = Di;
+  auto block = [&](const int qb) __attribute__((always_inline)) {
+    const int i0 = qb * kQB;
+    const size_t base = (size_t)bh * (size_t)N * D;
+    const int qw0 = i0 + 32 * wave;  // first query of this wave
+    const int qw0_s = __builtin_amdgcn_readfirstlane(qw0);
+    const int qi = qw0 + l32;
 
-  f32x16 dq[ND];
-#pragma unroll
-  for (int db = 0; db < ND; ++db) dq[db] = f32x16{};
-
-  const int nk_all = (N + kKT - 1) / kKT;
-  const int n_kt = CAUSAL ? min(nk_all, (i0 + kQB - 1) / kKT + 1) : nk_all;
-  const int n_w = CAUSAL ? min(n_kt, (qw0 + 31) / kKT + 1) : n_kt;  // this wave's last tile + 1
-
-  // K and V rows (A operands, rows = keys) through 16-byte reads
-  int kroff[NK];
-#pragma unroll
-  for (int kb = 0; kb < NK; ++kb) kroff[kb] = l32 * ROW_BYTES + ((2 * kb + hf) ^ kswz<D>(l32)) * 16;
-  const TrOffsets<D> tro(lane);
-  const uint16_t* Kh = K + base;
-  const uint16_t* Vh = V + base;
-  auto load_kv = [&](int t, auto st) __attribute__((always_inline)) {
-    const int64_t bytes = (int64_t)(N - t * kKT) * ROW_BYTES;
-    load_tile<D, kKT>(make_rsrc(Kh + (size_t)t * kKT * D, bytes), kbuf(st), wave_s, lane);
-    load_tile<D, kKT>(make_rsrc(Vh + (size_t)t * kKT * D, bytes), vbuf(st), wave_s, lane);
-  };
-
-  // key tile t from stage st; the next tile loads into the other stage, whose
-  // reads (tile t - 1) ended at the previous barrier
-  auto tile = [&](int t, auto st) __attribute__((always_inline)) {
-    if (t + 1 < n_kt) load_kv(t + 1, StageTag<decltype(st)::value ^ 1>{});
-    if (t < n_w) {
-      const unsigned char* Kt = kbuf(st);
-      const unsigned char* Vt = vbuf(st);
-      const int j0 = t * kKT;
-      const bool masked = (j0 + kKT > N) || (CAUSAL && j0 + kKT - 1 > qw0);
-#pragma unroll
-      for (int kh = 0; kh < kKT / 32; ++kh) {
-        f32x16 s = f32x16{}, dp = f32x16{};
-#pragma unroll
-        for (int kb = 0; kb < NK; ++kb) {
-          const int o = kroff[kb] + kh * 32 * ROW_BYTES;
-          const v8 kf = __builtin_bit_cast(v8, *reinterpret_cast<const u32x4*>(Kt + o));
-          const v8 vf = __builtin_bit_cast(v8, *reinterpret_cast<const u32x4*>(Vt + o));
-          s = Mma<T>::run(kf, qf[kb], s);
-          dp = Mma<T>::run(vf, dof[kb], dp);
-        }
-        v8 dsf[2];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = exp2_fast(fmaf(s[r], c, -lse2));
-          float ds = p * (dp[r] - Di);
-          if (masked) {
-            const int key = j0 + 32 * kh + 8 * (r >> 2) + 4 * hf + (r & 3);
-            if (key >= N || (CAUSAL && key > qi)) ds = 0.f;
-          }
-          dsf[r >> 3][r & 7] = (T)ds;
-        }
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int db = 0; db < ND; ++db)
-            dq[db] = Mma<T>::run(read_tr<T, D>(Kt, tro, db, 32 * kh + 16 * kb), dsf[kb], dq[db]);
+    // Q^T and dO^T as B operands: lane = query, 8 consecutive head dims per step;
+    // D_i = <dO_i, O_i> from the same rows (each lane half holds half the dims)
+    v8 qf[NK], dof[NK];
+    float Di;
+    {
+      const int64_t bytes = (int64_t)(N - qw0_s) * ROW_BYTES;
+      const auto rq = make_rsrc(Q + base + (size_t)qw0_s * D, bytes);
+      const auto rdo = make_rsrc(dO + base + (size_t)qw0_s * D, bytes);
+      const auto ro = make_rsrc(O + base + (size_t)qw0_s * D, bytes);
+      const int off = l32 * ROW_BYTES + 16 * hf;
+      float acc = 0.f;
+  #pragma unroll
+      for (int kb = 0; kb < NK; ++kb) {
+        qf[kb] = __builtin_bit_cast(v8, __builtin_amdgcn_raw_buffer_load_b128(rq, off + 32 * kb, 0, 0));
+        dof[kb] = __builtin_bit_cast(v8, __builtin_amdgcn_raw_buffer_load_b128(rdo, off + 32 * kb, 0, 0));
+        const v8 of = __builtin_bit_cast(v8, __builtin_amdgcn_raw_buffer_load_b128(ro, off + 32 * kb, 0, 0));
+  #pragma unroll
+        for (int e = 0; e < 8; ++e) acc = fmaf((float)dof[kb][e], (float)of[e], acc);
       }
+      Di = sum_halves(acc);
     }
-    vmem_landed();  // tile t + 1
+    const float lse2 = qi < N ? LSE[(size_t)bh * N + qi] * kLog2e : 0.f;
+    if (hf == 0 && qi < N) Dws[(size_t)bh * N + qi] = Di;
+
+    f32x16 dq[ND];
+  #pragma unroll
+    for (int db = 0; db < ND; ++db) dq[db] = f32x16{};
+
+    const int nk_all = (N + kKT - 1) / kKT;
+    const int n_kt = CAUSAL ? min(nk_all, (i0 + kQB - 1) / kKT + 1) : nk_all;
+    const int n_w = CAUSAL ? min(n_kt, (qw0 + 31) / kKT + 1) : n_kt;  // this wave's last tile + 1
+
+    // K and V rows (A operands, rows = keys) through 16-byte reads
+    int kroff[NK];
+  #pragma unroll
+    for (int kb = 0; kb < NK; ++kb) kroff[kb] = l32 * ROW_BYTES + ((2 * kb + hf) ^ kswz<D>(l32)) * 16;
+    const TrOffsets<D> tro(lane);
+    const uint16_t* Kh = K + base;
+    const uint16_t* Vh = V + base;
+    auto load_kv = [&](int t, auto st) __attribute__((always_inline)) {
+      const int64_t bytes = (int64_t)(N - t * kKT) * ROW_BYTES;
+      load_tile<D, kKT>(make_rsrc(Kh + (size_t)t * kKT * D, bytes), kbuf(st), wave_s, lane);
+      load_tile<D, kKT>(make_rsrc(Vh + (size_t)t * kKT * D, bytes), vbuf(st), wave_s, lane);
+    };
+
+    // key tile t from stage st; the next tile loads into the other stage, whose
+    // reads (tile t - 1) ended at the previous barrier
+    auto tile = [&](int t, auto st) __attribute__((always_inline)) {
+      if (t + 1 < n_kt) load_kv(t + 1, StageTag<decltype(st)::value ^ 1>{});
+      if (t < n_w) {
+        const unsigned char* Kt = kbuf(st);
+        const unsigned char* Vt = vbuf(st);
+        const int j0 = t * kKT;
+        const bool masked = (j0 + kKT > N) || (CAUSAL && j0 + kKT - 1 > qw0);
+  #pragma unroll
+        for (int kh = 0; kh < kKT / 32; ++kh) {
+          f32x16 s = f32x16{}, dp = f32x16{};
+  #pragma unroll
+          for (int kb = 0; kb < NK; ++kb) {
+            const int o = kroff[kb] + kh * 32 * ROW_BYTES;
+            const v8 kf = __builtin_bit_cast(v8, *reinterpret_cast<const u32x4*>(Kt + o));
+            const v8 vf = __builtin_bit_cast(v8, *reinterpret_cast<const u32x4*>(Vt + o));
+            s = Mma<T>::run(kf, qf[kb], s);
+            dp = Mma<T>::run(vf, dof[kb], dp);
+          }
+          v8 dsf[2];
+  #pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float p = exp2_fast(fmaf(s[r], c, -lse2));
+            float ds = p * (dp[r] - Di);
+            if (masked) {
+              const int key = j0 + 32 * kh + 8 * (r >> 2) + 4 * hf + (r & 3);
+              if (key >= N || (CAUSAL && key > qi)) ds = 0.f;
+            }
+            dsf[r >> 3][r & 7] = (T)ds;
+          }
+  #pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+  #pragma unroll
+            for (int db = 0; db < ND; ++db)
+              dq[db] = Mma<T>::run(read_tr<T, D>(Kt, tro, db, 32 * kh + 16 * kb), dsf[kb], dq[db]);
+        }
+      }
+      vmem_landed();  // tile t + 1
+      __syncthreads();
+    };
+
+    load_kv(0, StageTag<0>{});
+    vmem_landed();
     __syncthreads();
+    for (int t = 0; t < n_kt; t += 2) {
+      tile(t, StageTag<0>{});
+      if (t + 1 < n_kt) tile(t + 1, StageTag<1>{});
+    }
+    store_rows<T, D>(dq, make_rsrc(dQ + base + (size_t)qw0_s * D, (int64_t)(N - qw0_s) * ROW_BYTES), lane, scale);
   };
 
-  load_kv(0, StageTag<0>{});
-  vmem_landed();
-  __syncthreads();
-  for (int t = 0; t < n_kt; t += 2) {
-    tile(t, StageTag<0>{});
-    if (t + 1 < n_kt) tile(t + 1, StageTag<1>{});
+  block(qb_a);
+  if (CAUSAL && qb_b != qb_a) {
+    __syncthreads();  // the first block's tiles are read no more
+    block(qb_b);
   }
-  store_rows<T, D>(dq, make_rsrc(dQ + base + (size_t)qw0_s * D, (int64_t)(N - qw0_s) * ROW_BYTES), lane, scale);
 }
 
 // ------------------------------------------------------------------------------------
@@ -328,6 +340,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dkdv(
   // wave-uniform indices in scalar registers: the accumulators leave few vector ones
   const int kg = wave_s & 3;   // 32-key group of this wave
   const int qh = wave_s >> 2;  // which 32 queries of each tile
+  // (key blocks are not paired the way dQ pairs its query blocks: at
+  // B8 H32 N8192 d128 causal that measured no faster here)
   int bh, kbk;
   block_of(BH, n_kblocks, xcd_groups, false, &bh, &kbk);
   const int k0 = kbk * kKB;
@@ -487,10 +501,11 @@ hipError_t launch_attn_bwd(Elem elem, const void* q, const void* k, const void* 
   float c = scale * kLog2e;
   int xcd_groups = (BH % 8 == 0) ? 1 : 0;
   int n_qblocks = (N + kQB - 1) / kQB;
+  const int dq_grid = BH * (causal ? (n_qblocks + 1) / 2 : n_qblocks);  // causal: paired blocks
   void* a1[] = {(void*)&q, (void*)&k, (void*)&v, (void*)&o, (void*)&dout, (void*)&lse, (void*)&dq,
                 (void*)&workspace, (void*)&BH, (void*)&N, (void*)&n_qblocks, (void*)&c, (void*)&scale,
                 (void*)&xcd_groups};
-  hipError_t e = hipLaunchKernel(fdq, dim3(BH * n_qblocks), dim3(kThreads), a1, 0, stream);
+  hipError_t e = hipLaunchKernel(fdq, dim3(dq_grid), dim3(kThreads), a1, 0, stream);
   if (e != hipSuccess) return e;
   int n_kblocks = (N + kKB - 1) / kKB;
   const float* dws = workspace;

@@ -118,282 +118,299 @@ __device__ __forceinline__ void fp8_forward(
   const int l32 = lane & 31, hf = lane >> 5;
   const int group = wave >> 2;
 
-  // ---- which (batch*head, query block) this workgroup owns (as the bf16 kernel)
-  int id = blockIdx.x, bh, mt;
+  // ---- which (batch*head, query blocks) this workgroup owns (as the bf16 kernel:
+  // causal workgroups take blocks mt and n_mtiles - 1 - mt, which together hold
+  // as many key tiles as any other pair)
+  int id = blockIdx.x, bh, mt_a, mt_b = 0;
+  const int n_units = CAUSAL ? (n_mtiles + 1) >> 1 : n_mtiles;
   if (xcd_groups) {
     const int per = gridDim.x >> 3;
     id = (id & 7) * per + (id >> 3);
-    bh = id / n_mtiles;
-    mt = n_mtiles - 1 - (id - bh * n_mtiles);
+    bh = id / n_units;
+    mt_a = n_units - 1 - (id - bh * n_units);
   } else {
     bh = id % BH;
-    mt = n_mtiles - 1 - id / BH;
+    mt_a = n_units - 1 - id / BH;
   }
-  const int i0 = mt * kBM;
-  const size_t base = (size_t)bh * (size_t)N * kD;  // bytes = elements
-  const uint8_t* Kh = K + base;
-  const uint8_t* Vh = V + base;
-  const int qw0 = i0 + 32 * (2 * (wave & 3) + group);
-  const int qi = qw0 + l32;
-  const int qw0_s = __builtin_amdgcn_readfirstlane(qw0);
-
-  // ---- Q^T fragments: lane = query, 32 consecutive head dims per 64-deep step
-  i32x8 qf[NK];
-  {
-    const auto rq = make_rsrc(Q + base + (size_t)qw0_s * kD, (int64_t)(N - qw0_s) * ROW_BYTES);
-    const int off = l32 * ROW_BYTES + 32 * hf;
-#pragma unroll
-    for (int kb = 0; kb < NK; ++kb) {
-      const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(rq, off + 64 * kb, 0, 0);
-      const u32x4 b = __builtin_amdgcn_raw_buffer_load_b128(rq, off + 64 * kb + 16, 0, 0);
-      qf[kb] = i32x8{(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)b[0], (int)b[1], (int)b[2], (int)b[3]};
-    }
+  if (CAUSAL) {
+    mt_b = mt_a;
+    mt_a = n_mtiles - 1 - mt_b;
   }
 
-  f32x16 o[ND];
-#pragma unroll
-  for (int db = 0; db < ND; ++db) o[db] = f32x16{};
-  f32x16 s[NH];
-  // row sums of the rounded P on the matrix unit: a V^T block whose row 0 is all
-  // ones, so element 0 of the lane-half-0 accumulator is l for the lane's query
-  // (the other 31 rows are zero and stay zero)
-  f32x16 lacc = f32x16{};
-  const int one8 = l32 == 0 ? 0x38383838 : 0;  // E4M3 1.0 in every byte of row 0
-  const i32x8 ones = {one8, one8, one8, one8, one8, one8, one8, one8};
-  i32x8 pf;  // P^T (2^7 P in E4M3) as the B operand: bytes 8 i .. 8 i + 7 = keys 16 i + 8 hf + 0..7
-  float m_run = kNegInf;
+  // one query block; inlined once per block of the pair
+  auto block = [&](const int mt) __attribute__((always_inline)) {
+    const int i0 = mt * kBM;
+    const size_t base = (size_t)bh * (size_t)N * kD;  // bytes = elements
+    const uint8_t* Kh = K + base;
+    const uint8_t* Vh = V + base;
+    const int qw0 = i0 + 32 * (2 * (wave & 3) + group);
+    const int qi = qw0 + l32;
+    const int qw0_s = __builtin_amdgcn_readfirstlane(qw0);
 
-  const int nk_all = (N + kBN - 1) / kBN;
-  const int n_kt = CAUSAL ? min(nk_all, (i0 + kBM - 1) / kBN + 1) : nk_all;
-  int n_w = CAUSAL ? min(n_kt, (qw0 + 31) / kBN + 1) : n_kt;
-  asm volatile("" : "+v"(n_w));
-  auto act = [&](int t) { return t < n_w; };
-
-  // ---- loader: global -> LDS directly, by the four group-0 waves (2 KiB each per tile)
-  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
-  int kgoff[NI], vgoff[NI];
-#pragma unroll
-  for (int j = 0; j < NI; ++j) {
-    const int row = ((wave & 3) * NI + j) * RPI + lane / CPR;
-    const int p = lane % CPR;
-    kgoff[j] = row * ROW_BYTES + (p ^ kswz8<kD>(row)) * 16;
-    vgoff[j] = row * ROW_BYTES + (p ^ vswz8<kD>(row)) * 16;
-  }
-  auto load_k = [&](int t, auto st) __attribute__((always_inline)) {
-    const auto r = make_rsrc(Kh + (size_t)t * kBN * kD, (int64_t)(N - t * kBN) * ROW_BYTES);
-#pragma unroll
-    for (int j = 0; j < NI; ++j) load16_to_lds(r, kbuf(st) + ((wave_s & 3) * NI + j) * 1024, kgoff[j]);
-  };
-  auto load_v = [&](int t, auto st) __attribute__((always_inline)) {
-    const auto r = make_rsrc(Vh + (size_t)t * kBN * kD, (int64_t)(N - t * kBN) * ROW_BYTES);
-#pragma unroll
-    for (int j = 0; j < NI; ++j) load16_to_lds(r, vbuf(st) + ((wave_s & 3) * NI + j) * 1024, vgoff[j]);
-  };
-  auto loads_landed = [&]() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
-
-  // ---- operand read offsets
-  // K: row l32 (+32 per key block), logical chunks 4 kb + 2 hf and 4 kb + 2 hf + 1
-  int kroff[NK][2];
-#pragma unroll
-  for (int kb = 0; kb < NK; ++kb)
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-      kroff[kb][h] = l32 * ROW_BYTES + ((4 * kb + 2 * hf + h) ^ kswz8<kD>(l32)) * 16;
-  // V^T: read i of head-dim block db takes rows 16 i + 8 hf + (q >> 1), bytes
-  // 32 db + 16 ((lane >> 4) & 1) + 8 (q & 1) (q = lane % 16); rows 16 i apart share
-  // the swizzle, so one offset per db serves all four reads
-  int vroff[ND];
-  {
-    const int q = lane & 15;
-    const int row = 8 * hf + (q >> 1);
-#pragma unroll
-    for (int db = 0; db < ND; ++db)
-      vroff[db] = row * ROW_BYTES + ((2 * db + ((lane >> 4) & 1)) ^ vswz8<kD>(row)) * 16 + 8 * (q & 1);
-  }
-
-  auto qk = [&](auto st) __attribute__((always_inline)) {
-    const unsigned char* Kt = kbuf(st);
-#pragma unroll
-    for (int kh = 0; kh < NH; ++kh) s[kh] = f32x16{};
-#pragma unroll
-    for (int kb = 0; kb < NK; ++kb) {
-#pragma unroll
-      for (int kh = 0; kh < NH; ++kh) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(Kt + kroff[kb][0] + kh * 32 * ROW_BYTES);
-        const u32x4 b = *reinterpret_cast<const u32x4*>(Kt + kroff[kb][1] + kh * 32 * ROW_BYTES);
-        const i32x8 kf = {(int)a[0], (int)a[1], (int)a[2], (int)a[3],
-                          (int)b[0], (int)b[1], (int)b[2], (int)b[3]};
-        s[kh] = mma_fp8(kf, qf[kb], s[kh]);
+    // ---- Q^T fragments: lane = query, 32 consecutive head dims per 64-deep step
+    i32x8 qf[NK];
+    {
+      const auto rq = make_rsrc(Q + base + (size_t)qw0_s * kD, (int64_t)(N - qw0_s) * ROW_BYTES);
+      const int off = l32 * ROW_BYTES + 32 * hf;
+  #pragma unroll
+      for (int kb = 0; kb < NK; ++kb) {
+        const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(rq, off + 64 * kb, 0, 0);
+        const u32x4 b = __builtin_amdgcn_raw_buffer_load_b128(rq, off + 64 * kb + 16, 0, 0);
+        qf[kb] = i32x8{(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)b[0], (int)b[1], (int)b[2], (int)b[3]};
       }
     }
-    mfma_settle();
-  };
-  auto sm = [&](int t) __attribute__((always_inline)) {
-    const int j0 = t * kBN;
-    if ((j0 + kBN > N) || (CAUSAL && j0 + kBN - 1 > qw0)) {
-#pragma unroll
+
+    f32x16 o[ND];
+  #pragma unroll
+    for (int db = 0; db < ND; ++db) o[db] = f32x16{};
+    f32x16 s[NH];
+    // row sums of the rounded P on the matrix unit: a V^T block whose row 0 is all
+    // ones, so element 0 of the lane-half-0 accumulator is l for the lane's query
+    // (the other 31 rows are zero and stay zero)
+    f32x16 lacc = f32x16{};
+    const int one8 = l32 == 0 ? 0x38383838 : 0;  // E4M3 1.0 in every byte of row 0
+    const i32x8 ones = {one8, one8, one8, one8, one8, one8, one8, one8};
+    i32x8 pf;  // P^T (2^7 P in E4M3) as the B operand: bytes 8 i .. 8 i + 7 = keys 16 i + 8 hf + 0..7
+    float m_run = kNegInf;
+
+    const int nk_all = (N + kBN - 1) / kBN;
+    const int n_kt = CAUSAL ? min(nk_all, (i0 + kBM - 1) / kBN + 1) : nk_all;
+    int n_w = CAUSAL ? min(n_kt, (qw0 + 31) / kBN + 1) : n_kt;
+    asm volatile("" : "+v"(n_w));
+    auto act = [&](int t) { return t < n_w; };
+
+    // ---- loader: global -> LDS directly, by the four group-0 waves (2 KiB each per tile)
+    const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+    int kgoff[NI], vgoff[NI];
+  #pragma unroll
+    for (int j = 0; j < NI; ++j) {
+      const int row = ((wave & 3) * NI + j) * RPI + lane / CPR;
+      const int p = lane % CPR;
+      kgoff[j] = row * ROW_BYTES + (p ^ kswz8<kD>(row)) * 16;
+      vgoff[j] = row * ROW_BYTES + (p ^ vswz8<kD>(row)) * 16;
+    }
+    auto load_k = [&](int t, auto st) __attribute__((always_inline)) {
+      const auto r = make_rsrc(Kh + (size_t)t * kBN * kD, (int64_t)(N - t * kBN) * ROW_BYTES);
+  #pragma unroll
+      for (int j = 0; j < NI; ++j) load16_to_lds(r, kbuf(st) + ((wave_s & 3) * NI + j) * 1024, kgoff[j]);
+    };
+    auto load_v = [&](int t, auto st) __attribute__((always_inline)) {
+      const auto r = make_rsrc(Vh + (size_t)t * kBN * kD, (int64_t)(N - t * kBN) * ROW_BYTES);
+  #pragma unroll
+      for (int j = 0; j < NI; ++j) load16_to_lds(r, vbuf(st) + ((wave_s & 3) * NI + j) * 1024, vgoff[j]);
+    };
+    auto loads_landed = [&]() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
+
+    // ---- operand read offsets
+    // K: row l32 (+32 per key block), logical chunks 4 kb + 2 hf and 4 kb + 2 hf + 1
+    int kroff[NK][2];
+  #pragma unroll
+    for (int kb = 0; kb < NK; ++kb)
+  #pragma unroll
+      for (int h = 0; h < 2; ++h)
+        kroff[kb][h] = l32 * ROW_BYTES + ((4 * kb + 2 * hf + h) ^ kswz8<kD>(l32)) * 16;
+    // V^T: read i of head-dim block db takes rows 16 i + 8 hf + (q >> 1), bytes
+    // 32 db + 16 ((lane >> 4) & 1) + 8 (q & 1) (q = lane % 16); rows 16 i apart share
+    // the swizzle, so one offset per db serves all four reads
+    int vroff[ND];
+    {
+      const int q = lane & 15;
+      const int row = 8 * hf + (q >> 1);
+  #pragma unroll
+      for (int db = 0; db < ND; ++db)
+        vroff[db] = row * ROW_BYTES + ((2 * db + ((lane >> 4) & 1)) ^ vswz8<kD>(row)) * 16 + 8 * (q & 1);
+    }
+
+    auto qk = [&](auto st) __attribute__((always_inline)) {
+      const unsigned char* Kt = kbuf(st);
+  #pragma unroll
+      for (int kh = 0; kh < NH; ++kh) s[kh] = f32x16{};
+  #pragma unroll
+      for (int kb = 0; kb < NK; ++kb) {
+  #pragma unroll
+        for (int kh = 0; kh < NH; ++kh) {
+          const u32x4 a = *reinterpret_cast<const u32x4*>(Kt + kroff[kb][0] + kh * 32 * ROW_BYTES);
+          const u32x4 b = *reinterpret_cast<const u32x4*>(Kt + kroff[kb][1] + kh * 32 * ROW_BYTES);
+          const i32x8 kf = {(int)a[0], (int)a[1], (int)a[2], (int)a[3],
+                            (int)b[0], (int)b[1], (int)b[2], (int)b[3]};
+          s[kh] = mma_fp8(kf, qf[kb], s[kh]);
+        }
+      }
+      mfma_settle();
+    };
+    auto sm = [&](int t) __attribute__((always_inline)) {
+      const int j0 = t * kBN;
+      if ((j0 + kBN > N) || (CAUSAL && j0 + kBN - 1 > qw0)) {
+  #pragma unroll
+        for (int kh = 0; kh < NH; ++kh) {
+  #pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = j0 + 32 * kh + 8 * (r >> 2) + 4 * hf + (r & 3);
+            if (key >= N || (CAUSAL && key > qi)) s[kh][r] = kNegInf;
+          }
+        }
+      }
+      float mx = kNegInf;
+  #pragma unroll
+      for (int kh = 0; kh < NH; ++kh)
+  #pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kh][r]);
+      mx = max_halves(mx);
+      const float m_cand = fmaxf(m_run, mx * c);
+      const float m_new = (m_cand > m_run + kSlack) ? m_cand : m_run;  // -inf moves to any finite max
+      const float m_sub = (m_new == kNegInf) ? 0.f : m_new;  // a fully masked row stays empty
+      const float alpha = exp2_fast(m_run - m_sub);
+      const float shift = kPScale - m_sub;
+      // 2^7 P rounded to E4M3: word g of block kh holds keys 32 kh + 8 g + 4 hf + 0..3
+      unsigned w[NH][4];
+  #pragma unroll
       for (int kh = 0; kh < NH; ++kh) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = j0 + 32 * kh + 8 * (r >> 2) + 4 * hf + (r & 3);
-          if (key >= N || (CAUSAL && key > qi)) s[kh][r] = kNegInf;
+  #pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const float p0 = exp2_fast(fmaf(s[kh][4 * g], c, shift));
+          const float p1 = exp2_fast(fmaf(s[kh][4 * g + 1], c, shift));
+          const float p2 = exp2_fast(fmaf(s[kh][4 * g + 2], c, shift));
+          const float p3 = exp2_fast(fmaf(s[kh][4 * g + 3], c, shift));
+          int x = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
+          x = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, x, true);
+          w[kh][g] = (unsigned)x;
+        }
+      }
+      m_run = m_new;
+      // runs of 4 keys -> runs of 8: swap word 2j + 1 of the low half with word 2j
+      // of the high half
+  #pragma unroll
+      for (int kh = 0; kh < NH; ++kh) {
+  #pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const auto r = __builtin_amdgcn_permlane32_swap(w[kh][2 * j], w[kh][2 * j + 1], false, false);
+          pf[4 * kh + 2 * j] = (int)r[0];
+          pf[4 * kh + 2 * j + 1] = (int)r[1];
+        }
+      }
+      if (__any(alpha != 1.f)) {
+  #pragma unroll
+        for (int db = 0; db < ND; ++db) o[db] *= alpha;
+        lacc[0] *= alpha;
+      }
+    };
+    auto pv_chain = [&](auto st) __attribute__((always_inline)) {
+      const unsigned char* Vt = vbuf(st);
+  #pragma unroll
+      for (int db = 0; db < ND; ++db) {
+        i32x2 r[4];
+  #pragma unroll
+        for (int i = 0; i < 4; ++i)
+          r[i] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(Vt + vroff[db] + 16 * i * ROW_BYTES));
+        const i32x8 vf = {r[0][0], r[0][1], r[1][0], r[1][1], r[2][0], r[2][1], r[3][0], r[3][1]};
+        o[db] = mma_fp8(vf, pf, o[db]);
+      }
+      lacc = mma_fp8(ones, pf, lacc);  // l += sum of the rounded P
+    };
+    auto pv = [&](auto st) __attribute__((always_inline)) {
+      pv_chain(st);
+      mfma_settle();
+    };
+    auto pv_qk = [&](auto stp, auto stq) __attribute__((always_inline)) {
+      pv_chain(stp);
+      qk(stq);
+      constexpr int kAhead = 2;  // MFMAs whose operands are read ahead
+      constexpr int kPv = ND + 1, kQk = NH * NK;
+      __builtin_amdgcn_sched_group_barrier(0x100, 4 * kAhead, 0);  // DS reads
+  #pragma unroll
+      for (int i = 0; i < kPv + kQk; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+        const int j = i + kAhead;
+        if (j < kPv - 1) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+        else if (j < kPv + kQk) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+    };
+
+    // One tile t in stage S = t & 1: slot X(t), the barrier, slot Y(t) (the bf16
+    // kernel's schedule: group 0 runs SM(t) then PV(t), QK(t+1); group 1 runs
+    // PV(t-1), QK(t) then SM(t)).
+    auto tile = [&](int t, auto st) __attribute__((always_inline)) {
+      constexpr int S = decltype(st)::value;
+      const StageTag<S> cur;
+      const StageTag<S ^ 1> other;
+      if (group == 0) {
+        if (act(t)) sm(t);
+      } else {
+        __builtin_amdgcn_s_setprio(1);
+        if (t > 0 && act(t - 1) && act(t)) {
+          pv_qk(other, cur);
+        } else {
+          if (t > 0 && act(t - 1)) pv(other);
+          if (act(t)) qk(cur);
+        }
+        __builtin_amdgcn_s_setprio(0);
+      }
+      loads_landed();
+      __syncthreads();
+      if (group == 0) {
+        if (t + 2 < n_kt) load_k(t + 2, cur);
+        if (t + 1 < n_kt) load_v(t + 1, other);
+        __builtin_amdgcn_s_setprio(1);
+        if (act(t) && act(t + 1)) {
+          pv_qk(cur, other);
+        } else {
+          if (act(t)) pv(cur);
+          if (act(t + 1)) qk(other);
+        }
+        __builtin_amdgcn_s_setprio(0);
+      } else {
+        if (act(t)) sm(t);
+      }
+    };
+
+    if (group == 0) load_k(0, StageTag<0>{});
+    loads_landed();
+    __syncthreads();
+  #pragma unroll
+    for (int kb = 0; kb < NK; ++kb) asm volatile("" ::"v"(qf[kb]));
+    if (group == 0) {
+      if (1 < n_kt) load_k(1, StageTag<1>{});
+      load_v(0, StageTag<0>{});
+    }
+    if (group == 0 && act(0)) {
+      __builtin_amdgcn_s_setprio(1);
+      qk(StageTag<0>{});
+      __builtin_amdgcn_s_setprio(0);
+    }
+    __syncthreads();
+    for (int t = 0; t < n_kt; t += 2) {
+      tile(t, StageTag<0>{});
+      if (t + 1 < n_kt) tile(t + 1, StageTag<1>{});
+    }
+    if (group == 1 && act(n_kt - 1)) {
+      if (((n_kt - 1) & 1) == 0) pv(StageTag<0>{}); else pv(StageTag<1>{});
+    }
+
+    // ---- epilogue: O = v_descale * O / l in bf16, logsumexp = ln 2 (m + log2(l / 2^7))
+    const float l_tot = sum_halves(lacc[0]);  // the high half's element 0 is row 4: zero
+    const float inv = v_descale / l_tot;
+    {
+      const auto ro = make_rsrc(O + (size_t)bh * N * kD + (size_t)qw0_s * kD, (int64_t)(N - qw0_s) * kD * 2);
+      const int off = l32 * kD * 2 + 8 * hf;
+  #pragma unroll
+      for (int db = 0; db < ND; ++db) {
+  #pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const u32x2 wv = u32x2{pack2<__bf16>(o[db][4 * g] * inv, o[db][4 * g + 1] * inv),
+                                 pack2<__bf16>(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv)};
+          __builtin_amdgcn_raw_buffer_store_b64(wv, ro, off + (db * 32 + 8 * g) * 2, 0, 0);
         }
       }
     }
-    float mx = kNegInf;
-#pragma unroll
-    for (int kh = 0; kh < NH; ++kh)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kh][r]);
-    mx = max_halves(mx);
-    const float m_cand = fmaxf(m_run, mx * c);
-    const float m_new = (m_cand > m_run + kSlack) ? m_cand : m_run;  // -inf moves to any finite max
-    const float m_sub = (m_new == kNegInf) ? 0.f : m_new;  // a fully masked row stays empty
-    const float alpha = exp2_fast(m_run - m_sub);
-    const float shift = kPScale - m_sub;
-    // 2^7 P rounded to E4M3: word g of block kh holds keys 32 kh + 8 g + 4 hf + 0..3
-    unsigned w[NH][4];
-#pragma unroll
-    for (int kh = 0; kh < NH; ++kh) {
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const float p0 = exp2_fast(fmaf(s[kh][4 * g], c, shift));
-        const float p1 = exp2_fast(fmaf(s[kh][4 * g + 1], c, shift));
-        const float p2 = exp2_fast(fmaf(s[kh][4 * g + 2], c, shift));
-        const float p3 = exp2_fast(fmaf(s[kh][4 * g + 3], c, shift));
-        int x = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
-        x = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, x, true);
-        w[kh][g] = (unsigned)x;
-      }
-    }
-    m_run = m_new;
-    // runs of 4 keys -> runs of 8: swap word 2j + 1 of the low half with word 2j
-    // of the high half
-#pragma unroll
-    for (int kh = 0; kh < NH; ++kh) {
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const auto r = __builtin_amdgcn_permlane32_swap(w[kh][2 * j], w[kh][2 * j + 1], false, false);
-        pf[4 * kh + 2 * j] = (int)r[0];
-        pf[4 * kh + 2 * j + 1] = (int)r[1];
-      }
-    }
-    if (__any(alpha != 1.f)) {
-#pragma unroll
-      for (int db = 0; db < ND; ++db) o[db] *= alpha;
-      lacc[0] *= alpha;
-    }
-  };
-  auto pv_chain = [&](auto st) __attribute__((always_inline)) {
-    const unsigned char* Vt = vbuf(st);
-#pragma unroll
-    for (int db = 0; db < ND; ++db) {
-      i32x2 r[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        r[i] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(Vt + vroff[db] + 16 * i * ROW_BYTES));
-      const i32x8 vf = {r[0][0], r[0][1], r[1][0], r[1][1], r[2][0], r[2][1], r[3][0], r[3][1]};
-      o[db] = mma_fp8(vf, pf, o[db]);
-    }
-    lacc = mma_fp8(ones, pf, lacc);  // l += sum of the rounded P
-  };
-  auto pv = [&](auto st) __attribute__((always_inline)) {
-    pv_chain(st);
-    mfma_settle();
-  };
-  auto pv_qk = [&](auto stp, auto stq) __attribute__((always_inline)) {
-    pv_chain(stp);
-    qk(stq);
-    constexpr int kAhead = 2;  // MFMAs whose operands are read ahead
-    constexpr int kPv = ND + 1, kQk = NH * NK;
-    __builtin_amdgcn_sched_group_barrier(0x100, 4 * kAhead, 0);  // DS reads
-#pragma unroll
-    for (int i = 0; i < kPv + kQk; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-      const int j = i + kAhead;
-      if (j < kPv - 1) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-      else if (j < kPv + kQk) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-    }
+    if (LSE != nullptr && hf == 0 && qi < N)
+      LSE[(size_t)bh * N + qi] = (m_run + log2f(l_tot) - kPScale) * kLn2;
   };
 
-  // One tile t in stage S = t & 1: slot X(t), the barrier, slot Y(t) (the bf16
-  // kernel's schedule: group 0 runs SM(t) then PV(t), QK(t+1); group 1 runs
-  // PV(t-1), QK(t) then SM(t)).
-  auto tile = [&](int t, auto st) __attribute__((always_inline)) {
-    constexpr int S = decltype(st)::value;
-    const StageTag<S> cur;
-    const StageTag<S ^ 1> other;
-    if (group == 0) {
-      if (act(t)) sm(t);
-    } else {
-      __builtin_amdgcn_s_setprio(1);
-      if (t > 0 && act(t - 1) && act(t)) {
-        pv_qk(other, cur);
-      } else {
-        if (t > 0 && act(t - 1)) pv(other);
-        if (act(t)) qk(cur);
-      }
-      __builtin_amdgcn_s_setprio(0);
-    }
-    loads_landed();
-    __syncthreads();
-    if (group == 0) {
-      if (t + 2 < n_kt) load_k(t + 2, cur);
-      if (t + 1 < n_kt) load_v(t + 1, other);
-      __builtin_amdgcn_s_setprio(1);
-      if (act(t) && act(t + 1)) {
-        pv_qk(cur, other);
-      } else {
-        if (act(t)) pv(cur);
-        if (act(t + 1)) qk(other);
-      }
-      __builtin_amdgcn_s_setprio(0);
-    } else {
-      if (act(t)) sm(t);
-    }
-  };
-
-  if (group == 0) load_k(0, StageTag<0>{});
-  loads_landed();
-  __syncthreads();
-#pragma unroll
-  for (int kb = 0; kb < NK; ++kb) asm volatile("" ::"v"(qf[kb]));
-  if (group == 0) {
-    if (1 < n_kt) load_k(1, StageTag<1>{});
-    load_v(0, StageTag<0>{});
+  block(mt_a);
+  if (CAUSAL && mt_b != mt_a) {
+    __syncthreads();  // the first block's LDS stages are read no more
+    block(mt_b);
   }
-  if (group == 0 && act(0)) {
-    __builtin_amdgcn_s_setprio(1);
-    qk(StageTag<0>{});
-    __builtin_amdgcn_s_setprio(0);
-  }
-  __syncthreads();
-  for (int t = 0; t < n_kt; t += 2) {
-    tile(t, StageTag<0>{});
-    if (t + 1 < n_kt) tile(t + 1, StageTag<1>{});
-  }
-  if (group == 1 && act(n_kt - 1)) {
-    if (((n_kt - 1) & 1) == 0) pv(StageTag<0>{}); else pv(StageTag<1>{});
-  }
-
-  // ---- epilogue: O = v_descale * O / l in bf16, logsumexp = ln 2 (m + log2(l / 2^7))
-  const float l_tot = sum_halves(lacc[0]);  // the high half's element 0 is row 4: zero
-  const float inv = v_descale / l_tot;
-  {
-    const auto ro = make_rsrc(O + (size_t)bh * N * kD + (size_t)qw0_s * kD, (int64_t)(N - qw0_s) * kD * 2);
-    const int off = l32 * kD * 2 + 8 * hf;
-#pragma unroll
-    for (int db = 0; db < ND; ++db) {
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const u32x2 wv = u32x2{pack2<__bf16>(o[db][4 * g] * inv, o[db][4 * g + 1] * inv),
-                               pack2<__bf16>(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv)};
-        __builtin_amdgcn_raw_buffer_store_b64(wv, ro, off + (db * 32 + 8 * g) * 2, 0, 0);
-      }
-    }
-  }
-  if (LSE != nullptr && hf == 0 && qi < N)
-    LSE[(size_t)bh * N + qi] = (m_run + log2f(l_tot) - kPScale) * kLn2;
 }
 
 #define FP8_KERNEL_ARGS                                                                         \
@@ -425,10 +442,11 @@ hipError_t launch_attn_fwd_fp8(const void* q, const void* k, const void* v, void
   int n_mtiles = (N + kBM - 1) / kBM;
   float c = scale * q_descale * k_descale * kLog2e;
   int xcd_groups = (BH % 8 == 0) ? 1 : 0;
+  const int grid = BH * (causal ? (n_mtiles + 1) / 2 : n_mtiles);  // causal: paired blocks
   const void* fn = pick_fp8(d, causal);
   void* args[] = {(void*)&q, (void*)&k, (void*)&v, (void*)&o, (void*)&lse, (void*)&BH,
                   (void*)&N, (void*)&n_mtiles, (void*)&c, (void*)&v_descale, (void*)&xcd_groups};
-  return hipLaunchKernel(fn, dim3(BH * n_mtiles), dim3(kThreads), args, 0, stream);
+  return hipLaunchKernel(fn, dim3(grid), dim3(kThreads), args, 0, stream);
 }
 
 hipError_t attn_fwd_fp8_attributes(int d, bool causal, hipFuncAttributes* attr, int* threads,

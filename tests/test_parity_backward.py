@@ -156,6 +156,22 @@ def test_backward_several_tiles(orc, causal, d):
     check(orc, f"bwd bf16 d{d} c{int(causal)} N{N}", q, k, v, g, "bf16", scale, causal, grads, o=o)
 
 
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f16", 64)])
+@pytest.mark.parametrize("B,H", [(2, 4), (1, 3)])
+@pytest.mark.parametrize("N", [700, 1025])
+def test_backward_causal_block_pairs(orc, dtype, d, B, H, N):
+    """Causal dQ workgroups take two 256-query blocks of one head, one from each
+    end of the sequence: odd block counts (3 and 5, ragged last block), with the
+    XCD-grouped order (B*H = 8) and the plain one (B*H = 3)."""
+    say(f"[attention backward causal pairs] dtype={dtype} d={d} B={B} H={H} N={N}")
+    q, k, v = workloads.random_attn(B, H, N, d, dtype, seed=N * 5 + d + H)
+    g = workloads.cast(upstream((B, H, N, d), N + 3 * d + H), dtype)
+    scale = 1.0 / np.sqrt(d)
+    o, lse = oracle_forward(orc, q, k, v, dtype, scale, True)
+    grads = run_bwd(q, k, v, o, g, lse, dtype, scale, True)
+    check(orc, f"bwd pairs {dtype} d{d} B{B}H{H} N{N}", q, k, v, g, dtype, scale, True, grads, o=o)
+
+
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("N", [2, 65, 1000])
 def test_backward_chain(orc, causal, N):

@@ -160,6 +160,20 @@ def test_fp8_edge_shapes(orc, causal, N, d):
     check(orc, f"fp8 d{d} c{int(causal)} N{N}", q8, k8, v8, 1 / np.sqrt(d), desc, causal, o, lse)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("B,H", [(2, 4), (1, 3)])
+@pytest.mark.parametrize("N", [700, 1025])
+def test_fp8_causal_block_pairs(orc, d, B, H, N):
+    """Causal fp8 workgroups take two 256-query blocks of one head, one from each
+    end of the sequence: odd block counts (3 and 5, ragged last block), with the
+    XCD-grouped order (B*H = 8) and the plain one (B*H = 3)."""
+    desc = (1 / 64, 1 / 64, 1 / 64)
+    say(f"[attention fp8 causal pairs] d={d} B={B} H={H} N={N}")
+    q8, k8, v8 = random_fp8(B, H, N, d, seed=N + 11 + d + H, desc=desc)
+    o, lse = run(q8, k8, v8, 1 / np.sqrt(d), desc, True)
+    check(orc, f"fp8 pairs d{d} B{B}H{H} N{N}", q8, k8, v8, 1 / np.sqrt(d), desc, True, o, lse)
+
+
 def test_fp8_workload(orc):
     """The B8 H32 N8192 d128 causal fp8 workload in its full launch; every one of
     the 256 heads checked on its 256 sampled rows (tile and diagonal boundaries
