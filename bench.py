@@ -110,12 +110,19 @@ def _counter_rows(d):
     return rows
 
 
+def attn_workgroups(B: int, H: int, N: int, causal: bool) -> int:
+    """Workgroups of a 16-bit or fp8 forward launch: one per 256-query block, or,
+    causal, one per pair of blocks (mt, n - 1 - mt) of a head."""
+    blocks = -(-N // 256)
+    return B * H * (-(-blocks // 2) if causal else blocks)
+
+
 def _attn_grid() -> int:
     """Threads of the headline attention launch (the benchmark also launches the same
     kernel at other shapes; its dispatches are told apart by grid size)."""
     import workloads
     w = workloads.ATTN[ATTN_WORKLOAD]
-    return w.B * w.H * (-(-w.N // 256)) * 512
+    return attn_workgroups(w.B, w.H, w.N, w.causal) * 512
 
 
 def _is_attn_dispatch(r) -> bool:
@@ -752,7 +759,7 @@ def main():
             "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4),
                          "kernel": f"attn_fwd_mfma<bf16,64,{'causal' if wd.causal else 'dense'}>",
-                         "workgroups": wd.B * wd.H * (-(-wd.N // 256))}}
+                         "workgroups": attn_workgroups(wd.B, wd.H, wd.N, wd.causal)}}
         print(f"[bench] {name} {ms:.3f} ms", file=sys.stderr, flush=True)
     del d64
 

@@ -277,7 +277,7 @@ def test_wrapper_allocates_and_rejects_bad_tensors():
 def test_head_shard_shape(orc):
     """One GPU's share of the B8 H32 N8192 d128 causal workload split 8 ways by
     heads (heads 0-3 of every batch row, B8 H4), the shape the benchmark's shard
-    line times: 1024 workgroups, XCD-grouped; heads (0, 0), (3, 3) and (7, 1)
+    line times: 512 workgroups (paired query blocks), XCD-grouped; heads (0, 0), (3, 3) and (7, 1)
     checked on 256 sampled rows each."""
     w = workloads.ATTN["attn_bf16_b8h32n8192_causal"]
     hs = w.H // 8
