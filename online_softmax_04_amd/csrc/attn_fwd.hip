@@ -158,6 +158,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(
     id = (id & 7) * per + (id >> 3);
     bh = id / n_units;
     mt_a = n_units - 1 - (id - bh * n_units);
+    if constexpr (LOCAL) {
+      // document boundaries differ between batch rows, so a run of one row's
+      // heads per XCD left the XCDs unequal work (they finished up to 8% apart
+      // at B8 H32 N8192); give each XCD the same heads of every batch row
+      const int nb = BH / H;
+      bh = (bh % nb) * H + bh / nb;
+    }
   } else {
     bh = id % BH;
     mt_a = n_units - 1 - id / BH;
@@ -534,7 +541,46 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(
     const float l_tot = lacc[0];
     // a block-sparse row can see no key at all: O = 0 and logsumexp -inf there
     const float inv = (SPARSE && l_tot == 0.f) ? 0.f : 1.f / l_tot;
-    {
+    if constexpr (D == 128) {
+      // O leaves through LDS: a lane holds 4 consecutive dims of its query per
+      // accumulator group, so storing from registers writes 16 bytes into each of
+      // 32 rows per instruction; staged row-major, every store writes whole rows.
+      // Each wave stages its 32 rows in its own part of the stage arrays, free
+      // once every wave is past its last product.
+      constexpr int WAVE_BYTES = 32 * ROW_BYTES;
+      constexpr int PER_ARRAY = TILE_BYTES / WAVE_BYTES;  // waves per stage array
+      static_assert(PER_ARRAY >= 2 && kThreads / 64 / PER_ARRAY <= 4, "O staging space");
+      const int arr = wave_s / PER_ARRAY;
+      unsigned char* stg = (arr == 0 ? kb0 : arr == 1 ? kb1 : arr == 2 ? vb0 : vb1) +
+                           (wave_s % PER_ARRAY) * WAVE_BYTES;
+      // lane indices rederived here: left to the compiler, the addresses below
+      // would be shared by both blocks of a pair and held through the second
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+      const int lr = ln & 31, lh = ln >> 5;
+      __syncthreads();  // group 1 has run the last PV
+  #pragma unroll
+      for (int db = 0; db < ND; ++db) {
+  #pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const u32x2 w = u32x2{pack2<T>(o[db][4 * g] * inv, o[db][4 * g + 1] * inv),
+                                pack2<T>(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv)};
+          const int ch = (4 * db + g) ^ (lr & (CPR - 1));
+          *reinterpret_cast<u32x2*>(stg + lr * ROW_BYTES + ch * 16 + 8 * lh) = w;
+        }
+      }
+      __syncthreads();  // the wave's rows are in LDS
+      // rows past N fall outside the buffer and are dropped
+      const auto ro = make_rsrc(O + base + (size_t)qw0_s * D, (int64_t)(N - qw0_s) * ROW_BYTES);
+      constexpr int RPS = 64 / CPR;  // rows per store
+  #pragma unroll
+      for (int j = 0; j < 32 / RPS; ++j) {
+        const int row = j * RPS + ln / CPR, c = ln % CPR;
+        const u32x4 w = *reinterpret_cast<const u32x4*>(stg + row * ROW_BYTES + ((c ^ (row & (CPR - 1))) * 16));
+        __builtin_amdgcn_raw_buffer_store_b128(w, ro, row * ROW_BYTES + c * 16, 0, 0);
+      }
+    } else {
+      // (at d = 64 staging through LDS measured no faster)
       // rows past N fall outside the buffer and are dropped
       const auto ro = make_rsrc(O + base + (size_t)qw0_s * D, (int64_t)(N - qw0_s) * ROW_BYTES);
       const int off = l32 * ROW_BYTES + 8 * hf;
