@@ -174,9 +174,21 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(
     mt_a = n_mtiles - 1 - mt_b;
   }
 
+  // Q^T fragments of query block mt: B operand, lane = query, 8 consecutive head dims
+  auto load_q = [&](const int mt, v8 (&qf)[NK]) __attribute__((always_inline)) {
+    const int qw0 = mt * kBM + 32 * (2 * (wave & 3) + group);
+    const int qw0_s = __builtin_amdgcn_readfirstlane(qw0);
+    const auto rq = make_rsrc(Q + (size_t)bh * (size_t)N * D + (size_t)qw0_s * D,
+                              (int64_t)(N - qw0_s) * ROW_BYTES);
+    const int off = l32 * ROW_BYTES + 16 * hf;
+  #pragma unroll
+    for (int kb = 0; kb < NK; ++kb)
+      qf[kb] = __builtin_bit_cast(v8, __builtin_amdgcn_raw_buffer_load_b128(rq, off + 32 * kb, 0, 0));
+  };
+
   // one query block; called twice when paired (inlined twice: a loop around it
-  // spilled registers)
-  auto block = [&](const int mt) __attribute__((always_inline)) {
+  // spilled registers).  after_loop runs once the block's last Q^T read is done.
+  auto block = [&](const int mt, v8 (&qf)[NK], auto&& after_loop) __attribute__((always_inline)) {
     const int i0 = mt * kBM;
     const size_t base = (size_t)bh * (size_t)N * D;
     const uint16_t* Kh = K + base;
@@ -189,15 +201,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(
     // be scalar, or every access through them becomes a per-lane loop
     const int qw0_s = __builtin_amdgcn_readfirstlane(qw0);
 
-    // ---- Q^T fragments: B operand, lane = query, 8 consecutive head dims -------------
-    v8 qf[NK];
-    {
-      const auto rq = make_rsrc(Q + base + (size_t)qw0_s * D, (int64_t)(N - qw0_s) * ROW_BYTES);
-      const int off = l32 * ROW_BYTES + 16 * hf;
-  #pragma unroll
-      for (int kb = 0; kb < NK; ++kb)
-        qf[kb] = __builtin_bit_cast(v8, __builtin_amdgcn_raw_buffer_load_b128(rq, off + 32 * kb, 0, 0));
-    }
 
     f32x16 o[ND];
   #pragma unroll
@@ -532,6 +535,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(
       tile(i, StageTag<0>{});
       if (i + 1 < n_list) tile(i + 1, StageTag<1>{});
     }
+    after_loop();
     // slot X after the last tile: group 1 finishes the last PV
     if (group == 1 && n_list > 0 && act_at(n_list - 1)) {
       if (((n_list - 1) & 1) == 0) pv(StageTag<0>{}); else pv(StageTag<1>{});
@@ -598,10 +602,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(
       LSE[(size_t)bh * N + qi] = (SPARSE && l_tot == 0.f) ? kNegInf : (m_run + log2f(l_tot)) * kLn2;
   };
 
-  block(mt_a);
-  if (paired && mt_b != mt_a) {
+  // the second block's Q loads go out while the first block finishes
+  const bool two = paired && mt_b != mt_a;
+  v8 qa[NK], qb[NK];
+  load_q(mt_a, qa);
+  block(mt_a, qa, [&]() __attribute__((always_inline)) { if (two) load_q(mt_b, qb); });
+  if (two) {
     __syncthreads();  // the first block's LDS stages are read no more
-    block(mt_b);
+    block(mt_b, qb, []() {});
   }
 }
 
