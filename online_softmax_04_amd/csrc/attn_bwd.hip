@@ -109,20 +109,33 @@ __device__ __forceinline__ void load_tile(__amdgpu_buffer_rsrc_t r, unsigned cha
 }
 
 // Store a transposed accumulator block set acc[ND] (rows = head dims, column =
-// this lane's row of the output) as 16-bit values times `mul`; rows of the
+// this lane's row of the output) as 16-bit values times `mul`, through LDS: a
+// lane holds 4 consecutive head dims of its row per accumulator group, so
+// stores straight from the accumulators write 16 bytes into each of 32 rows per
+// instruction.  The wave writes its 32 rows into `stage` (32 * D * 2 bytes of
+// its own, swizzled like K) and stores whole rows from there, 16 bytes per
+// lane.  Every wave of the workgroup calls it (one barrier inside); rows of the
 // output past the buffer's range are dropped.
 template <typename T, int D>
-__device__ __forceinline__ void store_rows(const f32x16* acc, __amdgpu_buffer_rsrc_t r, int lane, float mul) {
-  constexpr int ROW_BYTES = D * 2, ND = D / 32;
-  const int off = (lane & 31) * ROW_BYTES + 8 * (lane >> 5);
+__device__ __forceinline__ void store_rows(const f32x16* acc, __amdgpu_buffer_rsrc_t r,
+                                           unsigned char* stage, int lane, float mul) {
+  constexpr int ROW_BYTES = D * 2, ND = D / 32, CPR = D / 8, RPS = 64 / CPR;
+  const int l32 = lane & 31, hf = lane >> 5;
 #pragma unroll
   for (int db = 0; db < ND; ++db) {
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const u32x2 w = u32x2{pack2<T>(acc[db][4 * g] * mul, acc[db][4 * g + 1] * mul),
                             pack2<T>(acc[db][4 * g + 2] * mul, acc[db][4 * g + 3] * mul)};
-      __builtin_amdgcn_raw_buffer_store_b64(w, r, off + (db * 32 + 8 * g) * 2, 0, 0);
+      *reinterpret_cast<u32x2*>(stage + l32 * ROW_BYTES + (((4 * db + g) ^ (l32 & (CPR - 1))) * 16) + 8 * hf) = w;
     }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < 32 / RPS; ++j) {
+    const int row = j * RPS + lane / CPR, c = lane % CPR;
+    const u32x4 w = *reinterpret_cast<const u32x4*>(stage + row * ROW_BYTES + ((c ^ (row & (CPR - 1))) * 16));
+    __builtin_amdgcn_raw_buffer_store_b128(w, r, row * ROW_BYTES + c * 16, 0, 0);
   }
 }
 
@@ -280,7 +293,18 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dq(
       tile(t, StageTag<0>{});
       if (t + 1 < n_kt) tile(t + 1, StageTag<1>{});
     }
-    store_rows<T, D>(dq, make_rsrc(dQ + base + (size_t)qw0_s * D, (int64_t)(N - qw0_s) * ROW_BYTES), lane, scale);
+    // the last tile's barrier freed the stage arrays: each wave stages its rows
+    // in its own half of one of them
+    {
+      static_assert(TILE_BYTES == 2 * 32 * ROW_BYTES, "dQ staging space");
+      // lane rederived here: left to the compiler, the staging addresses would be
+      // shared by both blocks of a pair and held through the second
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+      const int arr = wave_s >> 1;
+      unsigned char* stg = (arr == 0 ? kb0 : arr == 1 ? kb1 : arr == 2 ? vb0 : vb1) + (wave_s & 1) * 32 * ROW_BYTES;
+      store_rows<T, D>(dq, make_rsrc(dQ + base + (size_t)qw0_s * D, (int64_t)(N - qw0_s) * ROW_BYTES), stg, ln, scale);
+    }
   };
 
   block(qb_a);
@@ -441,31 +465,61 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dkdv(
     if (t + 1 < n_qt) tile(t + 1, StageTag<1>{});
   }
 
-  // the two waves of a pair (qh = 0, 1) hold partial sums over different
-  // queries: dK through the K/V block first, then dV
-  f32x16* red = reinterpret_cast<f32x16*>(smem);
-  if (qh == 1) {
+  // The two waves of a pair (qh = 0, 1) hold partial sums over different
+  // queries.  The qh = 1 waves leave theirs in LDS (dK in the K/V block, dV in
+  // the stage arrays, key group kg in stage array kg), the qh = 0 waves add
+  // them and write the 16-bit rows of dK and dV into the K/V block, and all
+  // eight waves store whole rows from there (16 bytes per lane, RPS rows per
+  // instruction) rather than 16 bytes into each of 32 rows per instruction.
+  {
+    static_assert(ND * 64 * 64 == TILE_BYTES && 4 * ND * 64 * 64 <= 2 * BLK_BYTES, "staging space");
+    f32x16* red_k = reinterpret_cast<f32x16*>(smem) + kg * ND * 64;
+    f32x16* red_v = reinterpret_cast<f32x16*>(kg == 0 ? qb0 : kg == 1 ? qb1 : kg == 2 ? db0 : db1);
+    if (qh == 1) {
 #pragma unroll
-    for (int db = 0; db < ND; ++db) red[((kg * ND + db) * 64) + lane] = dk[db];
-  }
-  __syncthreads();
-  if (qh == 0) {
+      for (int db = 0; db < ND; ++db) {
+        red_k[db * 64 + lane] = dk[db];
+        red_v[db * 64 + lane] = dv[db];
+      }
+    }
+    __syncthreads();
+    if (qh == 0) {
 #pragma unroll
-    for (int db = 0; db < ND; ++db) dk[db] += red[((kg * ND + db) * 64) + lane];
-  }
-  __syncthreads();
-  if (qh == 1) {
+      for (int db = 0; db < ND; ++db) {
+        dk[db] += red_k[db * 64 + lane];
+        dv[db] += red_v[db * 64 + lane];
+      }
+    }
+    __syncthreads();  // the partial sums are read
+    constexpr int CPR = D / 8;  // 16-byte chunks per row
+    if (qh == 0) {
+      const int kr = 32 * kg + l32;  // this lane's key row in the block
 #pragma unroll
-    for (int db = 0; db < ND; ++db) red[((kg * ND + db) * 64) + lane] = dv[db];
-  }
-  __syncthreads();
-  if (qh == 0) {
+      for (int db = 0; db < ND; ++db) {
 #pragma unroll
-    for (int db = 0; db < ND; ++db) dv[db] += red[((kg * ND + db) * 64) + lane];
-    const int kw0_s = __builtin_amdgcn_readfirstlane(kw0);
-    const int64_t bytes = (int64_t)(N - kw0_s) * ROW_BYTES;
-    store_rows<T, D>(dk, make_rsrc(dK + base + (size_t)kw0_s * D, bytes), lane, scale);
-    store_rows<T, D>(dv, make_rsrc(dV + base + (size_t)kw0_s * D, bytes), lane, 1.f);
+        for (int g = 0; g < 4; ++g) {
+          const int off = kr * ROW_BYTES + (((4 * db + g) ^ (kr & (CPR - 1))) * 16) + 8 * hf;
+          *reinterpret_cast<u32x2*>(smem + off) =
+              u32x2{pack2<T>(dk[db][4 * g] * scale, dk[db][4 * g + 1] * scale),
+                    pack2<T>(dk[db][4 * g + 2] * scale, dk[db][4 * g + 3] * scale)};
+          *reinterpret_cast<u32x2*>(smem + BLK_BYTES + off) =
+              u32x2{pack2<T>(dv[db][4 * g], dv[db][4 * g + 1]), pack2<T>(dv[db][4 * g + 2], dv[db][4 * g + 3])};
+        }
+      }
+    }
+    __syncthreads();  // the rows are in LDS
+    // waves 0-3 store the 128 rows of dK, waves 4-7 those of dV
+    constexpr int RPS = 64 / CPR;  // rows per store instruction
+    const int half = wave_s >> 2, r0 = 32 * (wave_s & 3);
+    const int64_t bytes = (int64_t)(N - k0) * ROW_BYTES;
+    const auto r = make_rsrc((half ? dV : dK) + base + (size_t)k0 * D, bytes);
+    const unsigned char* src = smem + half * BLK_BYTES;
+#pragma unroll
+    for (int j = 0; j < 32 / RPS; ++j) {
+      const int row = r0 + j * RPS + lane / CPR, c = lane % CPR;
+      const u32x4 w = *reinterpret_cast<const u32x4*>(src + row * ROW_BYTES + ((c ^ (row & (CPR - 1))) * 16));
+      __builtin_amdgcn_raw_buffer_store_b128(w, r, row * ROW_BYTES + c * 16, 0, 0);
+    }
   }
 }
 
