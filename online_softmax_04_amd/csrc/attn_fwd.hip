@@ -78,6 +78,31 @@
 namespace osm {
 namespace {
 
+// Wave-wide minimum and maximum of an int: prefix steps through DPP row shifts
+// (1, 2, 4, 8 lanes) leave each 16-lane row's result in its last lane, two row
+// broadcasts carry those on to lane 63, which is read out (wave-uniform).
+// Lanes a shift or broadcast does not reach keep the identity.
+__device__ __forceinline__ int wave_min_i32(int v) {
+  constexpr int kId = 0x7fffffff;
+  v = min(v, __builtin_amdgcn_update_dpp(kId, v, 0x111, 0xf, 0xf, false));  // row_shr:1
+  v = min(v, __builtin_amdgcn_update_dpp(kId, v, 0x112, 0xf, 0xf, false));  // row_shr:2
+  v = min(v, __builtin_amdgcn_update_dpp(kId, v, 0x114, 0xf, 0xf, false));  // row_shr:4
+  v = min(v, __builtin_amdgcn_update_dpp(kId, v, 0x118, 0xf, 0xf, false));  // row_shr:8
+  v = min(v, __builtin_amdgcn_update_dpp(kId, v, 0x142, 0xa, 0xf, false));  // row_bcast:15
+  v = min(v, __builtin_amdgcn_update_dpp(kId, v, 0x143, 0xc, 0xf, false));  // row_bcast:31
+  return __builtin_amdgcn_readlane(v, 63);
+}
+__device__ __forceinline__ int wave_max_i32(int v) {
+  constexpr int kId = (int)0x80000000;
+  v = max(v, __builtin_amdgcn_update_dpp(kId, v, 0x111, 0xf, 0xf, false));
+  v = max(v, __builtin_amdgcn_update_dpp(kId, v, 0x112, 0xf, 0xf, false));
+  v = max(v, __builtin_amdgcn_update_dpp(kId, v, 0x114, 0xf, 0xf, false));
+  v = max(v, __builtin_amdgcn_update_dpp(kId, v, 0x118, 0xf, 0xf, false));
+  v = max(v, __builtin_amdgcn_update_dpp(kId, v, 0x142, 0xa, 0xf, false));
+  v = max(v, __builtin_amdgcn_update_dpp(kId, v, 0x143, 0xc, 0xf, false));
+  return __builtin_amdgcn_readlane(v, 63);
+}
+
 // two 16-bit ones in one word
 template <typename T>
 constexpr unsigned kOnePair = sizeof(T) == 2 && __is_same(T, __bf16) ? 0x3f803f80u : 0x3c003c00u;
@@ -174,6 +199,16 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(
     mt_a = n_mtiles - 1 - mt_b;
   }
 
+  // the window kernel's first K tile depends on the document bounds of the
+  // block's queries: their load goes out ahead of the Q loads
+  int doc_first = 0;
+  if constexpr (LOCAL) {
+    if (doc_start) {
+      const int q = min(mt_a * kBM + 32 * (2 * (wave & 3) + group) + l32, N - 1);
+      doc_first = doc_start[(size_t)(bh / H) * N + q];
+    }
+  }
+
   // Q^T fragments of query block mt: B operand, lane = query, 8 consecutive head dims
   auto load_q = [&](const int mt, v8 (&qf)[NK]) __attribute__((always_inline)) {
     const int qw0 = mt * kBM + 32 * (2 * (wave & 3) + group);
@@ -234,18 +269,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(
     int lo_i = 0, lo_max_w = 0, tw0 = 0, t0 = 0;
     if constexpr (LOCAL) {
       const int qc = min(qi, N - 1);
-      int lo = doc_start ? doc_start[(size_t)(bh / H) * N + qc] : 0;
+      int lo = doc_first;
+      asm volatile("" : "+v"(lo));  // consumed here, after the Q loads went out
       lo = min(max(lo, 0), qc);
       if (window > 0) lo = max(lo, qc - window + 1);
       lo_i = lo;
-      int mn = lo, mx = lo;
-  #pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) {
-        mn = min(mn, __shfl_xor(mn, off));
-        mx = max(mx, __shfl_xor(mx, off));
-      }
-      lo_max_w = mx;
-      tw0 = __builtin_amdgcn_readfirstlane(mn) / BN;
+      lo_max_w = wave_max_i32(lo);
+      tw0 = wave_min_i32(lo) / BN;
       __shared__ int wave_first[kThreads / 64];
       if (lane == 0) wave_first[wave] = tw0;
       __syncthreads();
