@@ -137,8 +137,24 @@ __device__ __forceinline__ void fp8_forward(
     mt_a = n_mtiles - 1 - mt_b;
   }
 
-  // one query block; inlined once per block of the pair
-  auto block = [&](const int mt) __attribute__((always_inline)) {
+  // Q^T fragments of query block mt: lane = query, 32 consecutive head dims per
+  // 64-deep step
+  auto load_q = [&](const int mt, i32x8 (&qf)[NK]) __attribute__((always_inline)) {
+    const int qw0_s = __builtin_amdgcn_readfirstlane(mt * kBM + 32 * (2 * (wave & 3) + group));
+    const auto rq = make_rsrc(Q + (size_t)bh * (size_t)N * kD + (size_t)qw0_s * kD,
+                              (int64_t)(N - qw0_s) * ROW_BYTES);
+    const int off = l32 * ROW_BYTES + 32 * hf;
+  #pragma unroll
+    for (int kb = 0; kb < NK; ++kb) {
+      const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(rq, off + 64 * kb, 0, 0);
+      const u32x4 b = __builtin_amdgcn_raw_buffer_load_b128(rq, off + 64 * kb + 16, 0, 0);
+      qf[kb] = i32x8{(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)b[0], (int)b[1], (int)b[2], (int)b[3]};
+    }
+  };
+
+  // one query block; inlined once per block of the pair.  after_loop runs once
+  // the block's last Q^T read is done.
+  auto block = [&](const int mt, i32x8 (&qf)[NK], auto&& after_loop) __attribute__((always_inline)) {
     const int i0 = mt * kBM;
     const size_t base = (size_t)bh * (size_t)N * kD;  // bytes = elements
     const uint8_t* Kh = K + base;
@@ -147,18 +163,6 @@ __device__ __forceinline__ void fp8_forward(
     const int qi = qw0 + l32;
     const int qw0_s = __builtin_amdgcn_readfirstlane(qw0);
 
-    // ---- Q^T fragments: lane = query, 32 consecutive head dims per 64-deep step
-    i32x8 qf[NK];
-    {
-      const auto rq = make_rsrc(Q + base + (size_t)qw0_s * kD, (int64_t)(N - qw0_s) * ROW_BYTES);
-      const int off = l32 * ROW_BYTES + 32 * hf;
-  #pragma unroll
-      for (int kb = 0; kb < NK; ++kb) {
-        const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(rq, off + 64 * kb, 0, 0);
-        const u32x4 b = __builtin_amdgcn_raw_buffer_load_b128(rq, off + 64 * kb + 16, 0, 0);
-        qf[kb] = i32x8{(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)b[0], (int)b[1], (int)b[2], (int)b[3]};
-      }
-    }
 
     f32x16 o[ND];
   #pragma unroll
@@ -382,6 +386,7 @@ __device__ __forceinline__ void fp8_forward(
       tile(t, StageTag<0>{});
       if (t + 1 < n_kt) tile(t + 1, StageTag<1>{});
     }
+    after_loop();
     if (group == 1 && act(n_kt - 1)) {
       if (((n_kt - 1) & 1) == 0) pv(StageTag<0>{}); else pv(StageTag<1>{});
     }
@@ -406,10 +411,14 @@ __device__ __forceinline__ void fp8_forward(
       LSE[(size_t)bh * N + qi] = (m_run + log2f(l_tot) - kPScale) * kLn2;
   };
 
-  block(mt_a);
-  if (CAUSAL && mt_b != mt_a) {
+  // the second block's Q loads go out while the first block finishes
+  const bool two = CAUSAL && mt_b != mt_a;
+  i32x8 qa[NK], qb[NK];
+  load_q(mt_a, qa);
+  block(mt_a, qa, [&]() __attribute__((always_inline)) { if (two) load_q(mt_b, qb); });
+  if (two) {
     __syncthreads();  // the first block's LDS stages are read no more
-    block(mt_b);
+    block(mt_b, qb, []() {});
   }
 }
 
