@@ -71,6 +71,23 @@ def test_local_shapes(orc, dtype, d, N, window, docs):
           scale, o, lse)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("window", [0, 100])
+def test_local_unordered_document_starts(orc, d, window):
+    """doc_start holds any int per position, not only the starts of packed
+    documents: seeded values from -50 to N + 50, in no order (so a wave's
+    smallest and largest lo_i sit at arbitrary lanes), clamped to 0 .. i as the
+    contract states."""
+    B, H, N = 2, 2, 1000
+    say(f"[attention local] unordered doc starts d={d} window={window}")
+    q, k, v = workloads.random_attn(B, H, N, d, "bf16", seed=911 + d + window)
+    rng = np.random.default_rng([workloads.BASE_SEED + 950, d, window])
+    doc = rng.integers(-50, N + 50, size=(B, N)).astype(np.int32)
+    scale = 1.0 / np.sqrt(d)
+    o, lse = run_local(q, k, v, doc, window, "bf16", scale)
+    check(orc, f"local unordered d{d} w{window}", q, k, v, doc, window, "bf16", scale, o, lse)
+
+
 def test_local_without_masks_is_causal():
     """window 0 and no documents: the same bits as fa_fwd with causal = 1."""
     q, k, v = workloads.random_attn(1, 3, 700, 128, "bf16", seed=41)
