@@ -241,15 +241,23 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(
   #pragma unroll
     for (int db = 0; db < ND; ++db) o[db] = f32x16{};
     f32x16 s[NH];
-    // The row sum of P runs on the matrix unit: with a block of ones as the A
-    // operand, every row of the accumulator receives the sum over the step's keys
-    // of each query's P.  One more MFMA per 16-key step; on the vector ALU the sum
-    // of the 16-bit P takes two-term dot products, which wait for the matrix unit
-    // while the other wave of the SIMD keeps it busy (measured slower at both
-    // head dims).
-    f32x16 lacc = f32x16{};
-    const v8 ones = __builtin_bit_cast(
-        v8, u32x4{kOnePair<T>, kOnePair<T>, kOnePair<T>, kOnePair<T>});
+    // The row sum of P runs on the matrix unit, one 16x16x32 MFMA per 16-key step
+    // (half the cycles of a 32x32x16 one): on the vector ALU the sum of the
+    // 16-bit P takes two-term dot products, which wait for the matrix unit while
+    // the other wave of the SIMD keeps it busy (measured slower at both head
+    // dims).  Read as the 16x16x32 B operand, P^T's register puts column c of
+    // lane group g = l / 16 in lane c + 16 g, i.e. query c + 16 (g % 2), keys of
+    // half g / 2.  An A operand with ones in rows 0 and 8 for the even groups and
+    // rows 4 and 12 for the odd ones (zeros elsewhere) makes accumulator row
+    // 4 (l / 16) of lane l -- its register 0 -- the step's sum for query l % 32,
+    // in both lane halves; the other registers stay zero.
+    f32x4v lacc = f32x4v{};
+    v8 ones;
+    {
+      const int r16 = lane & 15, g16 = lane >> 4;
+      const unsigned w = ((r16 & 3) == 0 && ((r16 >> 2) & 1) == (g16 & 1)) ? kOnePair<T> : 0u;
+      ones = __builtin_bit_cast(v8, u32x4{w, w, w, w});
+    }
     v8 pf[NH][2];  // P^T as 16-bit B operands: [32-key block][16-key step]
     float m_run = kNegInf;
 
@@ -425,7 +433,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(
       if (__any(alpha != 1.f)) {  // wave-uniform; skipped while no row's reference moves
   #pragma unroll
         for (int db = 0; db < ND; ++db) o[db] *= alpha;
-        lacc *= alpha;
+        lacc[0] *= alpha;
       }
     };
     // PV: O^T += V^T P^T, from V stage st.
@@ -443,7 +451,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(
             const v8 vf = __builtin_bit_cast(v8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
             o[db] = Mma<T>::run(vf, pf[kh][kb], o[db]);
           }
-          lacc = Mma<T>::run(ones, pf[kh][kb], lacc);
+          lacc = Mma<T>::run16(ones, pf[kh][kb], lacc);
         }
       }
     };

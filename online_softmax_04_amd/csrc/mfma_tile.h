@@ -1,5 +1,5 @@
 // Tile helpers shared by the attention kernels (gfx950, wave64): buffer
-// descriptors, the 32x32x16 MFMA for 16-bit operands, 16-bit packing, the LDS
+// descriptors, the 32x32x16 and 16x16x32 MFMAs for 16-bit operands, 16-bit packing, the LDS
 // chunk swizzles and the direct global-to-LDS load.
 #pragma once
 
@@ -11,6 +11,7 @@ namespace osm {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4v __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
@@ -31,12 +32,20 @@ struct Mma<__bf16> {
   static __device__ __forceinline__ f32x16 run(v8 a, v8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
   }
+  // 16x16x32: lane l holds row (A) / column (B) l % 16 and 8 k values of group
+  // l / 16; accumulator register r of lane l is element (4 (l / 16) + r, l % 16)
+  static __device__ __forceinline__ f32x4v run16(v8 a, v8 b, f32x4v c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
 };
 template <>
 struct Mma<_Float16> {
   using v8 = f16x8;
   static __device__ __forceinline__ f32x16 run(v8 a, v8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x4v run16(v8 a, v8 b, f32x4v c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
   }
 };
 

@@ -9,6 +9,10 @@
 //    l % 32 of A and column l % 32 of B, 8 consecutive k from 8 (l / 32); writes
 //    each lane's 16 accumulator values.  A [32][16], B [16][32] bf16 bits (row
 //    major), out [64][16] fp32.
+//  * mfma16_bf16_probe: D = A B on v_mfma_f32_16x16x32_bf16 with lane l holding
+//    row l % 16 of A and column l % 16 of B, 8 consecutive k from 8 (l / 16);
+//    writes each lane's 4 accumulator values.  A [16][32], B [32][16] bf16 bits
+//    (row major), out [64][4] fp32.
 //  * permlane32_probe: v_permlane32_swap with both operands x; in [64] u32,
 //    out [2][64] u32 (result halves 0 and 1 per lane).
 //  * ds_read_tr16_probe: LDS filled with in [64][64] u16 (row major); lane l
@@ -23,6 +27,7 @@
 
 typedef __bf16 bf16x8p __attribute__((ext_vector_type(8)));
 typedef float f32x16p __attribute__((ext_vector_type(16)));
+typedef float f32x4p __attribute__((ext_vector_type(4)));
 typedef short s16x4p __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4p lds_s16x4p;
 typedef int i32x8p __attribute__((ext_vector_type(8)));
@@ -37,6 +42,18 @@ __global__ __launch_bounds__(64) void k_mfma_bf16(const uint16_t* A, const uint1
   f32x16p c = {};
   c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
   for (int i = 0; i < 16; ++i) out[l * 16 + i] = c[i];
+}
+
+__global__ __launch_bounds__(64) void k_mfma16_bf16(const uint16_t* A, const uint16_t* B, float* out) {
+  const int l = threadIdx.x, r = l % 16, kb = 8 * (l / 16);
+  bf16x8p a, b;
+  for (int i = 0; i < 8; ++i) {
+    a[i] = __builtin_bit_cast(__bf16, A[r * 32 + kb + i]);
+    b[i] = __builtin_bit_cast(__bf16, B[(kb + i) * 16 + r]);
+  }
+  f32x4p c = {};
+  c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  for (int i = 0; i < 4; ++i) out[l * 4 + i] = c[i];
 }
 
 __global__ __launch_bounds__(64) void k_permlane32(const unsigned* in, unsigned* out) {
@@ -88,6 +105,10 @@ __global__ __launch_bounds__(64) void k_cvt_fp8(const float* in, uint8_t* out) {
 extern "C" {
 int mfma_bf16_probe(const void* A, const void* B, void* out) {
   hipLaunchKernelGGL(k_mfma_bf16, dim3(1), dim3(64), 0, 0, (const uint16_t*)A, (const uint16_t*)B, (float*)out);
+  return (int)hipGetLastError();
+}
+int mfma16_bf16_probe(const void* A, const void* B, void* out) {
+  hipLaunchKernelGGL(k_mfma16_bf16, dim3(1), dim3(64), 0, 0, (const uint16_t*)A, (const uint16_t*)B, (float*)out);
   return (int)hipGetLastError();
 }
 int permlane32_probe(const void* in, void* out) {

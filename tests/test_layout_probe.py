@@ -8,6 +8,12 @@ exactly representable inputs:
   layout that lets the softmax take a query's row maximum inside one lane plus
   one exchange with lane l ^ 32 ("Online softmax, and the register that can't
   move", section "Why the output must live in registers");
+* the 16x16x32 bf16 MFMA: lane l holds row (A) / column (B) l % 16 and the 8
+  consecutive k from 8 (l / 16); accumulator register r of lane l is element
+  (4 (l / 16) + r, l % 16).  The forward kernels' row sum rests on it: fed the
+  32x32x16 P^T register as its B operand and a block of ones in rows 0, 8 (even
+  lane groups) and 4, 12 (odd ones) as A, register 0 of lane l is the sum over
+  the step's 16 keys for query l % 32 (checked below with that very A);
 * v_permlane32_swap with both operands equal: half 0 of the result holds lanes
   0..31 of the input in both halves of the wave, half 1 lanes 32..63, so each lane
   sees its own value and that of lane l ^ 32;
@@ -48,7 +54,7 @@ def probe():
     if not os.path.exists(LIB):
         raise ImportError(f"{LIB} is missing: build it with __graft_entry__.build()")
     L = ctypes.CDLL(LIB)
-    for name, n in (("mfma_bf16_probe", 3), ("permlane32_probe", 2), ("ds_read_tr16_probe", 3),
+    for name, n in (("mfma_bf16_probe", 3), ("mfma16_bf16_probe", 3), ("permlane32_probe", 2), ("ds_read_tr16_probe", 3),
                     ("mfma_fp8_probe", 3), ("cvt_fp8_probe", 2)):
         getattr(L, name).argtypes = [ctypes.c_void_p] * n
         getattr(L, name).restype = ctypes.c_int
@@ -57,6 +63,7 @@ def probe():
 
 # bytes each probe reads or writes per buffer (the fixed sizes of layout_probe.hip)
 SIZES = {"mfma_bf16_probe": (32 * 16 * 2, 16 * 32 * 2, 64 * 16 * 4),
+         "mfma16_bf16_probe": (16 * 32 * 2, 32 * 16 * 2, 64 * 4 * 4),
          "permlane32_probe": (64 * 4, 2 * 64 * 4),
          "ds_read_tr16_probe": (64 * 64 * 2, 64 * 4, 64 * 4 * 2),
          "mfma_fp8_probe": (32 * 64, 64 * 32, 64 * 16 * 4),
@@ -91,6 +98,50 @@ def test_mfma_32x32x16_layout(probe, seed):
         for r in range(16):
             i, j = acc_index(l, r)
             assert got[l, r] == D[i, j], f"lane {l} register {r}: {got[l, r]} != D[{i}, {j}] = {D[i, j]}"
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_mfma_16x16x32_layout(probe, seed):
+    rng = np.random.default_rng([62, seed])
+    A = rng.integers(-8, 9, (16, 32)).astype(np.float32)
+    B = rng.integers(-8, 9, (32, 16)).astype(np.float32)
+    D = A @ B
+    a = torch.from_numpy(workloads.f32_to_bf16_bits(A).view(np.int16)).cuda()
+    b = torch.from_numpy(workloads.f32_to_bf16_bits(B).view(np.int16)).cuda()
+    out = torch.empty((64, 4), dtype=torch.float32, device="cuda")
+    run(probe, "mfma16_bf16_probe", a, b, out)
+    got = out.cpu().numpy()
+    for l in range(64):
+        for r in range(4):
+            i, j = 4 * (l // 16) + r, l % 16
+            assert got[l, r] == D[i, j], f"lane {l} register {r}: {got[l, r]} != D[{i}, {j}] = {D[i, j]}"
+
+
+def test_row_sum_ones_block(probe):
+    """The forward kernels' row sum: each lane's 32x32x16 P^T B register (query
+    l % 32, the 8 keys of half l / 32 of a 16-key step) fed as the 16x16x32 B
+    operand against the kernels' block of ones gives, in register 0 of lane l,
+    the step's sum for query l % 32."""
+    rng = np.random.default_rng(63)
+    P = rng.integers(0, 9, (32, 16)).astype(np.float32)  # [query][key of the step]
+    # lane L's 8 B values, as the 16x16x32 probe reads them: column L % 16,
+    # k 8 (L / 16) + i; fill B so that lane L holds query L % 32, keys 8 (L / 32) + i
+    B = np.zeros((32, 16), np.float32)
+    A = np.zeros((16, 32), np.float32)
+    for L in range(64):
+        for i in range(8):
+            B[8 * (L // 16) + i, L % 16] = P[L % 32, 8 * (L // 32) + i]
+        r, g = L % 16, L // 16
+        if r % 4 == 0 and (r // 4) % 2 == g % 2:
+            A[r, 8 * g:8 * g + 8] = 1.0
+    a = torch.from_numpy(workloads.f32_to_bf16_bits(A).view(np.int16)).cuda()
+    b = torch.from_numpy(workloads.f32_to_bf16_bits(B).view(np.int16)).cuda()
+    out = torch.empty((64, 4), dtype=torch.float32, device="cuda")
+    run(probe, "mfma16_bf16_probe", a, b, out)
+    got = out.cpu().numpy()
+    want = P.sum(axis=1)
+    for l in range(64):
+        assert got[l, 0] == want[l % 32], f"lane {l}: {got[l, 0]} != row sum {want[l % 32]}"
 
 
 def test_permlane32_swap(probe):
