@@ -195,24 +195,23 @@ MFMA_PASS_B = ("SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT SQ
                "SQ_INSTS_VMEM SQ_INSTS_SALU SQ_INSTS_VALU_TRANS_F32")
 
 
-def kernel_mfma_count(w) -> int:
-    """32x32x16 MFMAs one attn_fwd_mfma launch issues on workload w (d = 128): every wave
-    runs QK and PV (D/16 + D/16 MFMAs per 32-key block, two blocks per 64-key tile) and the
-    row sum (one MFMA per 16 keys) on each key tile up to the last one holding a key
-    visible to one of its 32 queries."""
+def kernel_mfma_count(w) -> tuple[int, int]:
+    """MFMAs one attn_fwd_mfma launch issues on workload w (d = 128), as (32x32x16 MFMAs,
+    16x16x32 MFMAs): every wave runs QK and PV (D/16 + D/16 32x32x16 MFMAs per 32-key
+    block, two blocks per 64-key tile) and the row sum (one 16x16x32 MFMA per 16 keys) on
+    each key tile up to the last one holding a key visible to one of its 32 queries."""
     bm, bn = 256, 64
-    per_tile = 2 * (w.d // 16) * 2 + bn // 16
     n_mt = -(-w.N // bm)
     nk_all = -(-w.N // bn)
-    total = 0
+    tiles = 0
     for mt in range(n_mt):
         i0 = mt * bm
         n_kt = min(nk_all, (i0 + bm - 1) // bn + 1) if w.causal else nk_all
         for wave in range(8):
             qw0 = i0 + 32 * (2 * (wave & 3) + (wave >> 2))
             n_w = min(n_kt, (qw0 + 31) // bn + 1) if w.causal else n_kt
-            total += n_w * per_tile
-    return total * w.B * w.H
+            tiles += n_w
+    return tiles * 2 * (w.d // 16) * 2 * w.B * w.H, tiles * (bn // 16) * w.B * w.H
 
 
 def ingest_mfma_fp8(dir_a: str, dir_b: str):
@@ -303,8 +302,9 @@ def ingest_mfma(dir_a: str, dir_b: str):
             if r.get("Agent_Type") == "GPU":
                 cu, simd = int(r["Cu_Count"]), int(r["Simd_Per_Cu"])
                 xcc = int(r.get("Num_Xcc") or xcc)
-    n_mfma = kernel_mfma_count(w)
-    mfma_flop = n_mfma * 32 * 32 * 16 * 2
+    n_big, n_small = kernel_mfma_count(w)
+    mfma_flop = n_big * 32 * 32 * 16 * 2 + n_small * 16 * 16 * 32 * 2
+    n_mfma = mfma_flop / (32 * 32 * 16 * 2)  # in 32x32x16 equivalents (32 busy cycles each)
     counted_flop = mean.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", float("nan")) * 512
     busy = mean.get("SQ_VALU_MFMA_BUSY_CYCLES", float("nan"))
     active = mean.get("GRBM_GUI_ACTIVE", float("nan")) / xcc  # the counter sums the XCDs
@@ -322,10 +322,11 @@ def ingest_mfma(dir_a: str, dir_b: str):
         f"(mean duration under the profiler {dur * 1e3:.3f} ms).\n",
         "| quantity | value |", "|---|---|",
         f"| algorithmic FLOP (4 N^2 d B H / 2) | {w.flops:.4g} |",
-        f"| MFMA FLOP the tile schedule issues ({n_mfma} 32x32x16 MFMAs) | {mfma_flop:.4g} |",
+        f"| MFMA FLOP the tile schedule issues ({n_big} 32x32x16 MFMAs for QK and PV, {n_small} "
+        f"16x16x32 MFMAs for the row sums) | {mfma_flop:.4g} |",
         f"| MFMA FLOP counted (SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512) | {counted_flop:.4g} |",
         f"| SQ_VALU_MFMA_BUSY_CYCLES (summed over SIMDs) | {busy:.4g} |",
-        f"| busy cycles per MFMA | {busy / n_mfma:.2f} |",
+        f"| busy cycles per 32x32x16-equivalent MFMA | {busy / n_mfma:.2f} |",
         f"| GRBM_GUI_ACTIVE per XCD (GPU cycles; the counter sums {xcc} XCDs) | {active:.4g} |",
         f"| mean shader clock = GRBM_GUI_ACTIVE / duration | {clock:.3f} GHz |",
         f"| **MFMA pipe utilisation = busy / (active x {cu} CUs x {simd} SIMDs)** | **{util:.1%}** |",
@@ -335,7 +336,7 @@ def ingest_mfma(dir_a: str, dir_b: str):
         f"| same, as a fraction of the published 2.5 PFLOP/s | {w.flops / dur / 2.5e15:.1%} |",
         "",
         "Instruction mix per dispatch (second pass):\n",
-        "| counter | value | per MFMA |", "|---|---|---|",
+        "| counter | value | per 32x32x16-equivalent MFMA |", "|---|---|---|",
     ]
     for name in MFMA_PASS_B.split():
         v = mean.get(name, float("nan"))
