@@ -55,14 +55,30 @@ constexpr int kKT = 64;        // keys per dQ key tile
 constexpr int kKB = 128;       // keys per dK/dV workgroup
 constexpr int kQT = 64;        // queries per dK/dV query tile
 
+// 16-byte chunk swizzle of the backward's LDS tiles (physical chunk = logical ^
+// bswz(row)).  The tiles are read two ways: as 16-byte row pieces, 16 lanes
+// taking 16 consecutive rows at one logical chunk, and through the transposing
+// reads, 32 lanes taking 4 consecutive rows (aligned to 4) x 4 consecutive
+// chunks.  With the LDS as 64 banks of 4 bytes, the first needs the swizzles of
+// 16 consecutive rows to differ (d = 128; at d = 64, where two 128-byte rows
+// share a bank line, those of the 8 rows of each parity), the second needs the
+// swizzles of 4 aligned consecutive rows to differ in their high two bits
+// (d = 64: rows r and r + 2 in bit 2).  The forward's K-style swizzle (row & 15)
+// meets only the first, and its transposing reads then hit 4 banks 4 times over
+// (2 times at d = 64).
+template <int D>
+__device__ __forceinline__ int bswz(int row) {
+  return D == 128 ? (((row & 3) << 2) | ((row >> 2) & 3)) : ((((row >> 1) & 1) << 2) | ((row >> 2) & 3));
+}
+
 // Offsets of the transposing reads (ds_read_b64_tr_b16) of a row-major tile in
-// the K-style swizzle, for the A operand X^T of X^T Y with X rows = the
+// the bswz swizzle, for the A operand X^T of X^T Y with X rows = the
 // contraction index.  Within each group of 16 lanes the lane at position q
 // supplies the address of row R + q/4, columns C + 4 (q % 4) .. +3, and receives
 // X[R + k][C + q] for k = 0..3; with R = 4 hf (+ 16-row step, + 32-row block) and
 // C = 32 db + 16 ((lane >> 4) & 1) the lane gets its column (32 db + lane % 32)
 // at B-operand positions 8 hf .. 8 hf + 3, and a second read 8 rows further
-// gives 8 hf + 4 .. 8 hf + 7.  The K-style swizzle of row r + 8 is that of row
+// gives 8 hf + 4 .. 8 hf + 7.  The swizzle of row r + 8 is that of row
 // r with one more bit flipped, so the second read has its own offset.
 template <int D>
 struct TrOffsets {
@@ -70,15 +86,15 @@ struct TrOffsets {
   int lo[ND], hi[ND];
   __device__ __forceinline__ explicit TrOffsets(int lane) {
     constexpr int ROW_BYTES = D * 2;
-    constexpr int kFlip8 = D == 128 ? 8 : 4;  // kswz(r + 8) = kswz(r) ^ kFlip8
+    constexpr int kFlip8 = 2;  // bswz(r + 8) = bswz(r) ^ 2 for rows r with r & 8 == 0
     const int hf = lane >> 5, q = lane & 15;
     const int row = 4 * hf + (q >> 2);
     const int col = 16 * ((lane >> 4) & 1) + 4 * (q & 3);
 #pragma unroll
     for (int db = 0; db < ND; ++db) {
       const int ch = (col + 32 * db) >> 3;
-      lo[db] = row * ROW_BYTES + (ch ^ kswz<D>(row)) * 16 + (col & 7) * 2;
-      hi[db] = (row + 8) * ROW_BYTES + (ch ^ kswz<D>(row) ^ kFlip8) * 16 + (col & 7) * 2;
+      lo[db] = row * ROW_BYTES + (ch ^ bswz<D>(row)) * 16 + (col & 7) * 2;
+      hi[db] = (row + 8) * ROW_BYTES + (ch ^ bswz<D>(row) ^ kFlip8) * 16 + (col & 7) * 2;
     }
   }
 };
@@ -94,7 +110,7 @@ __device__ __forceinline__ typename Mma<T>::v8 read_tr(const unsigned char* tile
 }
 
 // Row-major tile of `ROWS` rows loaded straight into LDS by all 8 waves, 16-byte
-// chunks in the K-style swizzle.  Rows past the buffer's range land as zeros.
+// chunks in the bswz swizzle.  Rows past the buffer's range land as zeros.
 template <int D, int ROWS>
 __device__ __forceinline__ void load_tile(__amdgpu_buffer_rsrc_t r, unsigned char* lds, int wave_s, int lane) {
   constexpr int ROW_BYTES = D * 2, CPR = D / 8, RPI = 1024 / ROW_BYTES;
@@ -104,7 +120,7 @@ __device__ __forceinline__ void load_tile(__amdgpu_buffer_rsrc_t r, unsigned cha
   for (int j = 0; j < NI; ++j) {
     const int row = (wave_s * NI + j) * RPI + lane / CPR;
     const int p = lane % CPR;
-    load16_to_lds(r, lds + (wave_s * NI + j) * 1024, row * ROW_BYTES + (p ^ kswz<D>(row)) * 16);
+    load16_to_lds(r, lds + (wave_s * NI + j) * 1024, row * ROW_BYTES + (p ^ bswz<D>(row)) * 16);
   }
 }
 
@@ -234,7 +250,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dq(
     // K and V rows (A operands, rows = keys) through 16-byte reads
     int kroff[NK];
   #pragma unroll
-    for (int kb = 0; kb < NK; ++kb) kroff[kb] = l32 * ROW_BYTES + ((2 * kb + hf) ^ kswz<D>(l32)) * 16;
+    for (int kb = 0; kb < NK; ++kb) kroff[kb] = l32 * ROW_BYTES + ((2 * kb + hf) ^ bswz<D>(l32)) * 16;
     const TrOffsets<D> tro(lane);
     const uint16_t* Kh = K + base;
     const uint16_t* Vh = V + base;
@@ -390,8 +406,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dkdv(
   int qroff[NK], kboff[NK];
 #pragma unroll
   for (int kb = 0; kb < NK; ++kb) {
-    qroff[kb] = (32 * qh + l32) * ROW_BYTES + ((2 * kb + hf) ^ kswz<D>(l32)) * 16;
-    kboff[kb] = (32 * kg + l32) * ROW_BYTES + ((2 * kb + hf) ^ kswz<D>(l32)) * 16;
+    qroff[kb] = (32 * qh + l32) * ROW_BYTES + ((2 * kb + hf) ^ bswz<D>(l32)) * 16;
+    kboff[kb] = (32 * kg + l32) * ROW_BYTES + ((2 * kb + hf) ^ bswz<D>(l32)) * 16;
   }
   const TrOffsets<D> tro(lane);
   auto load_qtile = [&](int t, auto st) __attribute__((always_inline)) {
