@@ -223,7 +223,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(
 
   // one query block; called twice when paired (inlined twice: a loop around it
   // spilled registers).  after_loop runs once the block's last Q^T read is done.
-  auto block = [&](const int mt, v8 (&qf)[NK], auto&& after_loop) __attribute__((always_inline)) {
+  // With rev (the second block of a pair), the key tiles are walked from the
+  // diagonal down to tile 0.  Pair j ends its first block 4 tile times after pair
+  // j + 1, whose second block is 4 tiles longer: walked downwards, all second
+  // blocks of a head read the same key tile at the same time and share it in L2;
+  // walked upwards they would read tiles 4 apart.
+  auto block = [&](const int mt, v8 (&qf)[NK], auto&& after_loop, const bool rev) __attribute__((always_inline)) {
     const int i0 = mt * kBM;
     const size_t base = (size_t)bh * (size_t)N * D;
     const uint16_t* Kh = K + base;
@@ -313,7 +318,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(
         const unsigned b = (unsigned)blk_idx[p0 + i / kTilesPerBlock];
         return (int)min(b, (unsigned)nkb) * kTilesPerBlock + i % kTilesPerBlock;
       } else {
-        return t0 + i;
+        return rev ? n_kt - 1 - i : t0 + i;
       }
     };
     // last key a tile may start at and still hold a key this wave computes with;
@@ -325,7 +330,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(
       if constexpr (SPARSE) {
         return tile_of(i) * BN <= j0_max;
       } else {
-        return act(t0 + i);
+        return act(tile_of(i));
       }
     };
 
@@ -644,10 +649,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(
   const bool two = paired && mt_b != mt_a;
   v8 qa[NK], qb[NK];
   load_q(mt_a, qa);
-  block(mt_a, qa, [&]() __attribute__((always_inline)) { if (two) load_q(mt_b, qb); });
+  block(mt_a, qa, [&]() __attribute__((always_inline)) { if (two) load_q(mt_b, qb); }, false);
   if (two) {
     __syncthreads();  // the first block's LDS stages are read no more
-    block(mt_b, qb, []() {});
+    block(mt_b, qb, []() {}, true);
   }
 }
 

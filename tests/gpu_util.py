@@ -213,3 +213,36 @@ def softmax_rel_gate(what, got, ref, x):
         r_i, c_i = np.argwhere(live)[i]
         raise AssertionError(f"{what}: row {r_i} col {c_i}: relative error {rel[i]:.3e} > "
                              f"{bound[live][i]:.3e}")
+
+
+def reversed_rows(N: int, causal: bool) -> int:
+    """Rows at the start of each head that the dense causal 16-bit forward computes
+    with its key tiles in descending order: a causal workgroup takes query blocks
+    mt and n - 1 - mt (256 rows each, n = ceil(N / 256)) and walks the second, the
+    shorter one (mt < n // 2), from the diagonal down.  Kernels that walk every
+    block upwards give these rows the same keys in another order."""
+    return 256 * (((N + 255) // 256) // 2) if causal else 0
+
+
+def same_but_order(what, o1, l1, o2, l2, N, causal, vmax):
+    """o1/l1 against the dense causal forward's o2/l2 for the same keys: bit-equal on
+    the rows both walk upwards.  On the rows the dense kernel walks downwards
+    (reversed_rows) its reference maximum moves at other tiles, so each 16-bit
+    weight may round differently (by at most half a unit, u = 2^-9 of bf16 or 2^-12
+    of fp16, relative).  O is the weights' convex combination of V rows, so each
+    side is within u * 2 max|V| of the exact combination, and after its own
+    rounding to 16 bits within another u |O|: the two differ by at most
+    4 u max|V| + 2 u max|O|.  l sums the rounded weights, so each logsumexp is
+    within ln(1 + u) of the exact one: they differ by at most 2 u (+ 1e-6 for the
+    fp32 arithmetic)."""
+    r = reversed_rows(N, causal)
+    a1, a2 = o1.view(torch.int16), o2.view(torch.int16)
+    assert torch.equal(a1[..., r:, :], a2[..., r:, :]) and torch.equal(l1[..., r:], l2[..., r:]), \
+        f"{what}: rows walked in the same order differ"
+    if r:
+        u = 2.0 ** -9 if o1.dtype == torch.bfloat16 else 2.0 ** -12
+        x1, x2 = o1[..., :r, :].float(), o2[..., :r, :].float()
+        bad = (x1 - x2).abs() > 4 * u * vmax + 2 * u * torch.maximum(x1.abs(), x2.abs())
+        assert not bool(bad.any()), f"{what}: {int(bad.sum())} elements beyond the rounding bound"
+        dl = float((l1[..., :r] - l2[..., :r]).abs().max())
+        assert dl <= 2 * u + 1e-6, f"{what}: logsumexp differs by {dl:.3g}"

@@ -12,7 +12,7 @@ import torch
 import online_softmax_04_amd as fa
 import oracle
 import workloads
-from gpu_util import gate, gate_lse, lse_tolerance, say, set_vis, to_device, to_f64
+from gpu_util import gate, gate_lse, lse_tolerance, same_but_order, say, set_vis, to_device, to_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -135,8 +135,8 @@ def test_empty_pattern():
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 def test_full_pattern_equals_dense(d, causal):
-    """Every key block listed for every query block: the same tiles in the same
-    order as fa_fwd, so the same bits."""
+    """Every key block listed for every query block: the same tiles as fa_fwd, in
+    its order (the same bits) except on the causal rows fa_fwd walks downwards."""
     B, H, N = 1, 3, 1000
     q, k, v = workloads.random_attn(B, H, N, d, "bf16", seed=17 + d)
     nqb, nkb = (N + QB - 1) // QB, (N + KB - 1) // KB
@@ -147,7 +147,7 @@ def test_full_pattern_equals_dense(d, causal):
     l2 = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
     fa.fa_fwd(qd, kd, vd, o2, l2, B, H, N, d, 0.1, int(causal))
     torch.cuda.synchronize()
-    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
+    same_but_order("full pattern", o1, l1, o2, l2, N, causal, float(np.abs(workloads.bf16_bits_to_f32(v)).max()))
 
 
 def test_out_of_range_blocks_read_nothing(orc):

@@ -11,7 +11,7 @@ import torch
 import online_softmax_04_amd as fa
 import oracle
 import workloads
-from gpu_util import TORCH_DTYPE, gate, gate_lse, lse_tolerance, range_vis, say, to_device, to_f64
+from gpu_util import TORCH_DTYPE, gate, gate_lse, lse_tolerance, range_vis, same_but_order, say, to_device, to_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -89,7 +89,8 @@ def test_local_unordered_document_starts(orc, d, window):
 
 
 def test_local_without_masks_is_causal():
-    """window 0 and no documents: the same bits as fa_fwd with causal = 1."""
+    """window 0 and no documents: the same keys as fa_fwd with causal = 1, in its
+    order (the same bits) except on the rows fa_fwd walks downwards."""
     q, k, v = workloads.random_attn(1, 3, 700, 128, "bf16", seed=41)
     o1, l1 = run_local(q, k, v, None, 0, "bf16", 0.0884)
     qd, kd, vd = (to_device(t, "bf16") for t in (q, k, v))
@@ -97,7 +98,7 @@ def test_local_without_masks_is_causal():
     l2 = torch.empty((1, 3, 700), dtype=torch.float32, device="cuda")
     fa.fa_fwd(qd, kd, vd, o2, l2, 1, 3, 700, 128, 0.0884, 1)
     torch.cuda.synchronize()
-    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
+    same_but_order("window 0", o1, l1, o2, l2, 700, True, float(np.abs(workloads.bf16_bits_to_f32(v)).max()))
 
 
 def test_local_headline_shape(orc):
