@@ -208,7 +208,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dq(
   block_of(BH, CAUSAL ? (n_qblocks + 1) >> 1 : n_qblocks, xcd_groups, true, &bh, &qb_b);
   qb_a = CAUSAL ? n_qblocks - 1 - qb_b : qb_b;
 
-  auto block = [&](const int qb) __attribute__((always_inline)) {
+  // With rev (the second block of a pair) the key tiles are walked from the
+  // diagonal down, so that the second blocks of a head, which start 4 tile times
+  // apart, read the same key tile at the same time (as in the forward kernel).
+  auto block = [&](const int qb, const bool rev) __attribute__((always_inline)) {
     const int i0 = qb * kQB;
     const size_t base = (size_t)bh * (size_t)N * D;
     const int qw0 = i0 + 32 * wave;  // first query of this wave
@@ -260,10 +263,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dq(
       load_tile<D, kKT>(make_rsrc(Vh + (size_t)t * kKT * D, bytes), vbuf(st), wave_s, lane);
     };
 
-    // key tile t from stage st; the next tile loads into the other stage, whose
-    // reads (tile t - 1) ended at the previous barrier
-    auto tile = [&](int t, auto st) __attribute__((always_inline)) {
-      if (t + 1 < n_kt) load_kv(t + 1, StageTag<decltype(st)::value ^ 1>{});
+    auto kt = [&](int i) { return rev ? n_kt - 1 - i : i; };  // key tile at list position i
+    // list position i from stage st; the next position loads into the other
+    // stage, whose reads (position i - 1) ended at the previous barrier
+    auto tile = [&](int i, auto st) __attribute__((always_inline)) {
+      if (i + 1 < n_kt) load_kv(kt(i + 1), StageTag<decltype(st)::value ^ 1>{});
+      const int t = kt(i);
       if (t < n_w) {
         const unsigned char* Kt = kbuf(st);
         const unsigned char* Vt = vbuf(st);
@@ -302,12 +307,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dq(
       __syncthreads();
     };
 
-    load_kv(0, StageTag<0>{});
+    load_kv(kt(0), StageTag<0>{});
     vmem_landed();
     __syncthreads();
-    for (int t = 0; t < n_kt; t += 2) {
-      tile(t, StageTag<0>{});
-      if (t + 1 < n_kt) tile(t + 1, StageTag<1>{});
+    for (int i = 0; i < n_kt; i += 2) {
+      tile(i, StageTag<0>{});
+      if (i + 1 < n_kt) tile(i + 1, StageTag<1>{});
     }
     // the last tile's barrier freed the stage arrays: each wave stages its rows
     // in its own half of one of them
@@ -323,10 +328,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dq(
     }
   };
 
-  block(qb_a);
+  block(qb_a, false);
   if (CAUSAL && qb_b != qb_a) {
     __syncthreads();  // the first block's tiles are read no more
-    block(qb_b);
+    block(qb_b, true);
   }
 }
 
