@@ -198,13 +198,15 @@ def rising_inputs(dtype, d, step):
     """[1, 2, 1024, d] storage arrays whose scores climb by about `step` (log2
     units, c * score) per key tile of the 16-bit kernel (64 keys at d = 128, 128
     at d = 64): row i climbs at rate (1 + u_i / 2), u_i uniform, on top of N(0, 1)
-    noise in the other head dims."""
+    noise in the other head dims.  A negative step gives scores that fall along
+    the keys, which climb along the walk of a causal kernel's second query block
+    of a pair (walked from the diagonal down)."""
     B, H, N = 1, 2, 1024
     scale = 1.0 / np.sqrt(d)
     bn = 128 if d == 64 else 64
     salt = 0 if d == 128 else 1000
-    q, k, v = workloads.random_attn(B, H, N, d, "f32", seed=int(step * 10) + 3 + salt)
-    rng = np.random.default_rng([17, int(step * 10) + salt])
+    q, k, v = workloads.random_attn(B, H, N, d, "f32", seed=int(abs(step) * 10) + 3 + salt + (500 if step < 0 else 0))
+    rng = np.random.default_rng([17, int(abs(step) * 10) + salt + (500 if step < 0 else 0)])
     rate = np.float32(step / (bn * scale * np.log2(np.e)))
     q[..., 0] = np.float32(1.0) + np.float32(0.5) * rng.random((B, H, N), dtype=np.float32)
     k[..., 0] = rate * np.arange(N, dtype=np.float32)[None, None, :]
@@ -232,7 +234,7 @@ def test_large_scores_force_rescales(orc, dtype, d, causal):
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
-@pytest.mark.parametrize("step", [0.5, 3.0, 7.9, 8.1, 30.0])
+@pytest.mark.parametrize("step", [0.5, 3.0, 7.9, 8.1, 30.0, -3.0, -8.1, -30.0])
 def test_rising_scores(orc, dtype, d, causal, step):
     """Scores that climb by about `step` per key tile (rising_inputs), so the
     running maximum keeps moving by a controlled amount: below the kernel's 2^8
