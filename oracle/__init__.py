@@ -25,10 +25,11 @@ _lib = None
 
 def build(src: str = SRC, out: str = LIB) -> str:
     """Compile the oracle with gcc (-O2, no fast-math, IEEE double throughout)."""
+    tmp = f"{out}.{os.getpid()}.tmp"  # one per process: parallel test workers build at once
     cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fno-fast-math",
-           "-ffp-contract=off", src, "-o", out + ".tmp", "-lm", "-lpthread"]
+           "-ffp-contract=off", src, "-o", tmp, "-lm", "-lpthread"]
     subprocess.run(cmd, check=True)
-    os.replace(out + ".tmp", out)
+    os.replace(tmp, out)
     return out
 
 
