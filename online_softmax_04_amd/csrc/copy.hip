@@ -2,7 +2,7 @@
 // practical HBM ceiling of a streaming kernel on this part.  The row softmax
 // moves one read and one write per byte as well ("5.2 CUDA Online Softmax",
 // section 6: one read and one write is the floor of a register-cached row), so
-// this copy, timed in the same run, is what its bandwidth is judged against
+// this copy, timed in the same run, is what its bandwidth is compared with
 // beside the published peak.  It is also the kernel of known size that
 // calibrates the byte counters of a profile.
 //
