@@ -442,7 +442,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(
       }
     };
     // PV: O^T += V^T P^T, from V stage st.
-    auto pv = [&](auto st) __attribute__((always_inline)) {
+    // the row sums of P alone: l += rowsum P over the tile's four 16-key steps
+    auto rowsums = [&]() __attribute__((always_inline)) {
+  #pragma unroll
+      for (int kh = 0; kh < NH; ++kh)
+  #pragma unroll
+        for (int kb = 0; kb < 2; ++kb) lacc = Mma<T>::run16(ones, pf[kh][kb], lacc);
+    };
+    auto pv = [&](auto st, bool with_rowsums = true) __attribute__((always_inline)) {
       const unsigned char* Vt = vbuf(st);
   #pragma unroll
       for (int kh = 0; kh < NH; ++kh) {
@@ -456,40 +463,43 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(
             const v8 vf = __builtin_bit_cast(v8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
             o[db] = Mma<T>::run(vf, pf[kh][kb], o[db]);
           }
-          lacc = Mma<T>::run16(ones, pf[kh][kb], lacc);
+          if (with_rowsums) lacc = Mma<T>::run16(ones, pf[kh][kb], lacc);
         }
       }
     };
 
-    // PV(tp) then QK(tq) in one block, with the LDS operand reads running a fixed
-    // distance ahead of the MFMAs that consume them: enough reads in flight to
-    // cover LDS latency, few enough registers to avoid spilling.  nld (a
-    // compile-time count) direct loads issued by loads() are spread evenly
-    // between the MFMAs.
+    // Row sums, PV(tp), then QK(tq) in one block, with the LDS operand reads running
+    // a fixed distance ahead of the MFMAs that consume them: enough reads in flight
+    // to cover LDS latency, few enough registers to avoid spilling.  The row sums
+    // read only registers, so they go first and run while the first PV operands
+    // are read (in slot Y the stages were published by the barrier just before).
+    // Their order, and so l, is that of the PV loop.  nld (a compile-time count)
+    // direct loads issued by loads() are spread evenly between the MFMAs.
     auto pv_qk = [&](auto stp, auto stq, auto nld, auto&& loads) __attribute__((always_inline)) {
       constexpr int NL = decltype(nld)::value;
       loads();
-      pv(stp);
+      rowsums();
+      pv(stp, false);
       qk(stq);
-      // PV MFMAs take two transposed reads each, QK MFMAs one read
-      constexpr int kAhead = 4;               // MFMAs whose operands are read ahead
-      // (the row-sum MFMA that ends each 16-key step reads nothing)
-      constexpr int kStep = ND + 1;  // PV MFMAs per 16-key step
-      constexpr int kPv = 2 * NH * kStep, kQk = NH * NK;
+      constexpr int kAhead = 4;  // operand-reading MFMAs whose reads are issued ahead
+      constexpr int kRs = 2 * NH, kPv = 2 * NH * ND, kQk = NH * NK;
+      constexpr int kTot = kRs + kPv + kQk;
+      // operand-reading MFMA k: PV (two transposed reads) for k < kPv, then QK (one read)
   #pragma unroll
-      for (int j = 0; j < kAhead; ++j)
-        if (j % kStep != ND) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS reads
-      constexpr int kEvery = NL ? (kPv + kQk) / (NL + 1) : 1;
+      for (int k = 0; k < kAhead; ++k) {
+        if (k < kPv) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS reads
+        else __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      constexpr int kEvery = NL ? kTot / (NL + 1) : 1;
   #pragma unroll
-      for (int i = 0; i < kPv + kQk; ++i) {
+      for (int i = 0; i < kTot; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
         if (NL && i % kEvery == kEvery - 1 && i / kEvery < NL)
           __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one direct load
-        const int j = i + kAhead;                           // operand reads for MFMA j
-        if (j < kPv) {
-          if (j % kStep != ND) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-        } else if (j < kPv + kQk) {
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        if (i >= kRs) {
+          const int k = i - kRs + kAhead;
+          if (k < kPv) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+          else if (k < kPv + kQk) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
       }
     };
